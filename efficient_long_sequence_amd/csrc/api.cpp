@@ -1,0 +1,275 @@
+// C ABI of libmita: argument validation, the launch plan and workspace
+// carve-up, and the enqueue order of the forward pass.  No device memory is
+// allocated and no state is kept between calls.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/mita.h"
+#include "mita_plan.h"
+
+using namespace mita;
+
+namespace {
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+mita_status validate(const void* Q, const void* K, const void* V, void* O, mita_dtype dtype, int B, int H,
+                     int N, int d, mita_pool pool, int m, int k, int s, bool check_ptrs) {
+  if (check_ptrs && (!Q || !K || !V || !O)) return MITA_ERR_NULL;
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return MITA_ERR_SHAPE;
+  if (pool.grid_h <= 0 || pool.grid_w <= 0 || pool.land_h <= 0 || pool.land_w <= 0) return MITA_ERR_SHAPE;
+  if ((long long)pool.grid_h * pool.grid_w != N) return MITA_ERR_SHAPE;
+  if ((long long)pool.land_h * pool.land_w != m) return MITA_ERR_SHAPE;
+  if (pool.land_h > pool.grid_h || pool.land_w > pool.grid_w) return MITA_ERR_SHAPE;
+  if (k < 1 || k > N) return MITA_ERR_PARAM;
+  if (s < 1 || s > m) return MITA_ERR_PARAM;
+  if (check_ptrs) {
+    const uintptr_t mis = ((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15u;
+    if (mis) return MITA_ERR_PARAM;
+  }
+  if (dtype != MITA_F32 && dtype != MITA_BF16) return MITA_ERR_UNSUPPORTED;
+  if (d != 32 && d != 64) return MITA_ERR_UNSUPPORTED;
+  if (s > MAX_S || m > MAX_M || (long long)N > MAX_N) return MITA_ERR_UNSUPPORTED;
+  if (N > NSMALL && k > MAX_K_SPARSE) return MITA_ERR_UNSUPPORTED;
+  if ((long long)B * H > 65535) return MITA_ERR_UNSUPPORTED;
+  return MITA_OK;
+}
+
+// Sizes, launch shapes and workspace regions.  With base == nullptr only the
+// sizes are meaningful (used by mita_workspace_bytes).
+Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int m, int k, int s, char* base) {
+  Plan p;
+  std::memset(&p, 0, sizeof(p));
+  p.dtype = dtype == MITA_BF16 ? 1 : 0;
+  p.esize = p.dtype ? 2 : 4;
+  p.B = B; p.H = H; p.BH = B * H; p.N = N; p.d = d;
+  p.gh = pool.grid_h; p.gw = pool.grid_w; p.lh = pool.land_h; p.lw = pool.land_w;
+  p.m = m; p.k = k; p.s = s;
+  p.cscale = (float)(1.4426950408889634 / std::sqrt((double)d));
+
+  // landmark scoring: rows per workgroup tile
+  if (p.dtype == 0 || m <= 64) { p.sc_nw = 4; p.sc_ib = 1; }
+  else if (m <= 128) { p.sc_nw = 8; p.sc_ib = 1; }
+  else if (m <= 256) { p.sc_nw = 8; p.sc_ib = 2; }
+  else { p.sc_nw = 8; p.sc_ib = 4; }
+  p.sc_R = p.sc_nw * 16 * p.sc_ib;
+  p.sc_rt = ceil_div(m, p.sc_R);
+  // key chunks: aim for about two workgroups per compute unit
+  const long long target = 512;
+  int C = ceil_div(target, (long long)p.BH * p.sc_rt);
+  C = C < 1 ? 1 : C;
+  const int max_c = ceil_div(N, 32);
+  C = C > max_c ? max_c : C;
+  int L = ceil_div(N, C);
+  L = (L + 31) / 32 * 32;
+  if (L > (1 << 23)) L = 1 << 23;
+  p.L = L;
+  p.C = ceil_div(N, L);
+
+  p.dense = N <= NSMALL ? 1 : 0;
+  p.capg = p.dense ? N : CAPG;
+  if (!p.dense) {
+    p.sigma = k / 16 > 1 ? k / 16 : 1;
+    p.NS = N / p.sigma;
+    p.G = p.NS < 512 ? p.NS : 512;
+    const double lam = (double)k / p.sigma;
+    int J = (int)std::ceil(lam + 6.0 * std::sqrt(lam) + 3.0);
+    p.J = J > p.G ? p.G : J;
+    const long long est_target = 512;
+    int gpb = ceil_div((long long)p.G * p.BH * p.sc_rt, est_target);
+    p.est_gpb = gpb < 1 ? 1 : gpb;
+    // staged candidates per workgroup: about three times k survivors per row
+    const double expect = (double)p.sc_R * p.L * (3.0 * k / N);
+    int cb = 256;
+    while (cb < 2.0 * expect && cb < 8192) cb <<= 1;
+    p.cb = cb;
+    // Test hook (host-forced): MITA_TEST_FORCE_FALLBACK=1 sets every candidate
+    // threshold to +inf, so no row collects candidates and every row is
+    // selected by the exact fallback kernel instead.
+    const char* ff = std::getenv("MITA_TEST_FORCE_FALLBACK");
+    p.force_fallback = (ff != nullptr && ff[0] == '1') ? 1 : 0;
+  }
+
+  // routing and attention tiles
+  p.smax = s <= 1 ? 1 : s <= 2 ? 2 : s <= 4 ? 4 : 8;
+  const double avg = (double)N / m;
+  if (p.dtype == 0 || avg <= 16) { p.at_nw = 1; p.at_ib = 1; }
+  else if (avg <= 64) { p.at_nw = 4; p.at_ib = 1; }
+  else if (avg <= 512) { p.at_nw = 4; p.at_ib = 4; }
+  else { p.at_nw = 8; p.at_ib = 4; }
+  p.T = p.at_nw * 16 * p.at_ib;
+  p.UB = p.BH * (ceil_div(N, p.T) + m);
+
+  // workspace
+  const size_t BH = p.BH, Mr = (size_t)p.BH * m;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    char* ptr = base ? base + off : nullptr;
+    off = align_up(off + bytes, 256);
+    return ptr;
+  };
+  p.qt = take(Mr * d * p.esize);
+  p.gmax = (float*)take(p.dense ? 0 : Mr * p.G * 4);
+  p.tau = (float*)take(Mr * 4);
+  p.mhat = (float*)take(Mr * 4);
+  p.vpart = (float*)take(Mr * p.C * (d + 4) * 4);
+  p.cand = (uint64_t*)take(Mr * p.capg * 8);
+  const size_t zoff = off;
+  p.cand_cnt = (int*)take(Mr * 4);
+  p.counts = (int*)take((size_t)s * Mr * 4);
+  p.cursor = (int*)take((size_t)s * Mr * 4);
+  p.zero_begin = base ? base + zoff : nullptr;
+  p.zero_bytes = off - zoff;
+  p.fail = (int*)take(Mr * 4);
+  p.topk = (int32_t*)take(Mr * k * 4);
+  p.vt32 = (float*)take(Mr * d * 4);
+  p.vtT = take(Mr * d * p.esize);
+  p.route = (int32_t*)take(BH * N * s * 4);
+  p.gpre = (int*)take((size_t)s * Mr * 4);
+  p.perm = (int32_t*)take((size_t)s * BH * N * 4);
+  p.wl = (WorkItem*)take((size_t)s * p.UB * sizeof(WorkItem));
+  p.wl_count = (int*)take(MAX_S * 4);
+  p.part = (float*)take(s > 1 ? (size_t)(s - 1) * BH * N * (d + 4) * 4 : 0);
+  p.total_bytes = off;
+  return p;
+}
+
+struct Timer {
+  void* const* ev;
+  hipStream_t st;
+  void begin(int stage) const {
+    if (ev) (void)hipEventRecord((hipEvent_t)ev[2 * stage], st);
+  }
+  void end(int stage) const {
+    if (ev) (void)hipEventRecord((hipEvent_t)ev[2 * stage + 1], st);
+  }
+};
+
+mita_status run(const void* Q, const void* K, const void* V, void* O, mita_dtype dtype, int B, int H, int N,
+                int d, mita_pool pool, int m, int k, int s, const mita_debug* dbg, void* workspace,
+                size_t workspace_bytes, void* stream, void* const* events) {
+  mita_status st = validate(Q, K, V, O, dtype, B, H, N, d, pool, m, k, s, true);
+  if (st != MITA_OK) return st;
+  if (!workspace) return MITA_ERR_NULL;
+  if ((uintptr_t)workspace & 15u) return MITA_ERR_PARAM;
+  Plan p = make_plan(dtype, B, H, N, d, pool, m, k, s, (char*)workspace);
+  if (workspace_bytes < p.total_bytes) return MITA_ERR_WORKSPACE;
+  p.Q = Q; p.K = K; p.V = V; p.O = O;
+  p.stream = (hipStream_t)stream;
+  const Timer tm{events, p.stream};
+
+  (void)hipGetLastError();  // clear any earlier sticky launch error
+  tm.begin(ST_POOL);
+  launch_zero(p);
+  launch_pool(p);
+  tm.end(ST_POOL);
+  tm.begin(ST_EST);
+  if (!p.dense) launch_estimate(p);
+  tm.end(ST_EST);
+  tm.begin(ST_SCORE);
+  launch_score(p);
+  tm.end(ST_SCORE);
+  tm.begin(ST_FINAL);
+  launch_final(p);
+  tm.end(ST_FINAL);
+  tm.begin(ST_ROUTE);
+  launch_route(p);
+  tm.end(ST_ROUTE);
+  tm.begin(ST_BUCKET);
+  launch_bucket(p);
+  tm.end(ST_BUCKET);
+  tm.begin(ST_ATTEND);
+  launch_attend(p);
+  tm.end(ST_ATTEND);
+
+  if (dbg) {
+    const size_t Mr = (size_t)p.BH * m;
+    if (dbg->topk) (void)hipMemcpyAsync(dbg->topk, p.topk, Mr * k * 4, hipMemcpyDeviceToDevice, p.stream);
+    if (dbg->route)
+      (void)hipMemcpyAsync(dbg->route, p.route, (size_t)p.BH * N * s * 4, hipMemcpyDeviceToDevice, p.stream);
+    if (dbg->vtilde) (void)hipMemcpyAsync(dbg->vtilde, p.vt32, Mr * d * 4, hipMemcpyDeviceToDevice, p.stream);
+    if (dbg->qtilde)
+      (void)hipMemcpyAsync(dbg->qtilde, p.qt, Mr * d * p.esize, hipMemcpyDeviceToDevice, p.stream);
+  }
+  return hipGetLastError() == hipSuccess ? MITA_OK : MITA_ERR_HIP;
+}
+
+const char* const kStageNames[ST_COUNT] = {"pool", "estimate", "score", "select", "route", "bucket", "attend"};
+
+}  // namespace
+
+extern "C" {
+
+size_t mita_workspace_bytes(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int m, int k, int s) {
+  if (validate(nullptr, nullptr, nullptr, nullptr, dtype, B, H, N, d, pool, m, k, s, false) != MITA_OK) return 0;
+  return make_plan(dtype, B, H, N, d, pool, m, k, s, nullptr).total_bytes;
+}
+
+mita_status mita_forward(const void* Q, const void* K, const void* V, void* O, mita_dtype dtype, int B, int H,
+                         int N, int d, mita_pool pool, int m, int k, int s, const mita_debug* dbg, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return run(Q, K, V, O, dtype, B, H, N, d, pool, m, k, s, dbg, workspace, workspace_bytes, stream, nullptr);
+}
+
+mita_status mita_forward_timed(const void* Q, const void* K, const void* V, void* O, mita_dtype dtype, int B,
+                               int H, int N, int d, mita_pool pool, int m, int k, int s, const mita_debug* dbg,
+                               void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+  if (!events) return MITA_ERR_NULL;
+  return run(Q, K, V, O, dtype, B, H, N, d, pool, m, k, s, dbg, workspace, workspace_bytes, stream, events);
+}
+
+int mita_num_stages(void) { return ST_COUNT; }
+
+const char* mita_stage_name(int stage) { return (stage >= 0 && stage < ST_COUNT) ? kStageNames[stage] : "?"; }
+
+mita_status mita_events_create(void** events, int count) {
+  if (!events || count <= 0) return MITA_ERR_NULL;
+  for (int i = 0; i < count; ++i) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return MITA_ERR_HIP;
+    events[i] = (void*)e;
+  }
+  return MITA_OK;
+}
+
+mita_status mita_events_destroy(void** events, int count) {
+  if (!events || count <= 0) return MITA_ERR_NULL;
+  for (int i = 0; i < count; ++i)
+    if (events[i]) (void)hipEventDestroy((hipEvent_t)events[i]);
+  return MITA_OK;
+}
+
+mita_status mita_events_elapsed(void* const* events, int n_pairs, float* ms) {
+  if (!events || !ms || n_pairs <= 0) return MITA_ERR_NULL;
+  for (int i = 0; i < n_pairs; ++i) {
+    if (hipEventSynchronize((hipEvent_t)events[2 * i + 1]) != hipSuccess) return MITA_ERR_HIP;
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, (hipEvent_t)events[2 * i], (hipEvent_t)events[2 * i + 1]) != hipSuccess)
+      return MITA_ERR_HIP;
+    ms[i] = t;
+  }
+  return MITA_OK;
+}
+
+const char* mita_status_str(mita_status status) {
+  switch (status) {
+    case MITA_OK: return "ok";
+    case MITA_ERR_NULL: return "a required pointer is NULL";
+    case MITA_ERR_SHAPE: return "inconsistent shape (B, H, N, d, pooling grid or m)";
+    case MITA_ERR_PARAM: return "k or s out of range, or a pointer is not 16-byte aligned";
+    case MITA_ERR_UNSUPPORTED: return "unsupported configuration (d, dtype, s, m, N or k limit)";
+    case MITA_ERR_WORKSPACE: return "workspace smaller than mita_workspace_bytes()";
+    case MITA_ERR_HIP: return "HIP runtime error while enqueueing";
+  }
+  return "unknown status";
+}
+
+const char* mita_version(void) { return "mita-gfx950 0.1"; }
+
+}  // extern "C"

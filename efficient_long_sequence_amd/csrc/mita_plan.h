@@ -1,0 +1,97 @@
+// Host-side launch plan: every size, launch shape and workspace region of one
+// mita_forward call, derived from the arguments alone (so sizing and running
+// agree by construction).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mita {
+
+// Rows of N up to this size keep every landmark score as a candidate ("dense"
+// selection); above it a sampled threshold filters candidates first.
+constexpr int NSMALL = 8192;
+// Candidate capacity per landmark row in sparse mode; also the largest block
+// sort in the selection kernel (8192 x 8 bytes of LDS).
+constexpr int CAPG = 8192;
+constexpr int MAX_S = 8;
+constexpr int MAX_M = 4096;
+constexpr int MAX_K_SPARSE = 2048;
+constexpr long long MAX_N = 1LL << 26;
+// Stages reported by the profiling entry point.
+enum Stage { ST_POOL = 0, ST_EST, ST_SCORE, ST_FINAL, ST_ROUTE, ST_BUCKET, ST_ATTEND, ST_COUNT };
+
+struct WorkItem {
+  int start;  // first position in the slot's permutation array
+  int count;  // queries in this tile
+  int be;     // bh * m + expert
+  int pad;
+};
+
+struct Plan {
+  // arguments
+  int dtype;  // 0 f32, 1 bf16
+  int esize;  // bytes per element
+  int B, H, BH, N, d, gh, gw, lh, lw, m, k, s;
+  // landmark scoring
+  int dense;      // 1: every score is a candidate
+  int capg;       // candidate slots per landmark row
+  int sc_nw, sc_ib, sc_R, sc_rt;  // waves, 16-row blocks per wave, rows per tile, row tiles
+  int L, C;       // keys per chunk, chunks per head
+  int cb;         // LDS candidate staging entries per workgroup
+  // threshold estimate (sparse mode)
+  int sigma;      // sample stride
+  int NS;         // samples per head
+  int G;          // sample groups per landmark row
+  int J;          // rank of the threshold among the group maxima
+  int est_gpb;    // groups per estimator workgroup
+  int force_fallback;  // test hook: every row takes the exact fallback path
+  // routing / attention
+  int smax;       // compiled top-s list length (>= s)
+  int at_nw, at_ib, T;  // attention waves, 16-query blocks per wave, queries per tile
+  int UB;         // upper bound on work items per slot
+  float cscale;   // log2(e) / sqrt(d)
+
+  // workspace regions
+  void* qt;         // [BH, m, d] dtype
+  float* gmax;      // [BH, m, G]
+  float* tau;       // [BH, m] raw-score threshold
+  float* mhat;      // [BH, m] sample maximum (raw)
+  float* vpart;     // [BH, m, C, d + 4]: max, normaliser, 2 pad, d sums
+  uint64_t* cand;   // [BH, m, capg]
+  int* cand_cnt;    // [BH, m]           (zeroed each call)
+  int* counts;      // [s, BH, m]        (zeroed each call)
+  int* cursor;      // [s, BH, m]        (zeroed each call)
+  int* fail;        // [BH, m]
+  int32_t* topk;    // [BH, m, k]
+  float* vt32;      // [BH, m, d]
+  void* vtT;        // [BH, m, d] dtype
+  int32_t* route;   // [BH, N, s]
+  int* gpre;        // [s, BH, m] exclusive prefix of counts
+  int32_t* perm;    // [s, BH * N]
+  WorkItem* wl;     // [s, UB]
+  int* wl_count;    // [s]
+  float* part;      // [s - 1, BH, N, d + 4]
+  void* zero_begin;
+  size_t zero_bytes;
+  size_t total_bytes;
+
+  // call
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  hipStream_t stream;
+};
+
+// Launchers (one per translation unit); each enqueues on plan.stream.
+void launch_zero(const Plan& p);
+void launch_pool(const Plan& p);
+void launch_estimate(const Plan& p);
+void launch_score(const Plan& p);
+void launch_final(const Plan& p);
+void launch_route(const Plan& p);
+void launch_bucket(const Plan& p);
+void launch_attend(const Plan& p);
+
+}  // namespace mita

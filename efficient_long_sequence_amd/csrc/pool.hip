@@ -1,0 +1,91 @@
+// Step 1: landmark queries by average pooling of Q (MiTA tutorial (iwxt.cn),
+// ch.4 step 1, paper section 3.2; gist.science summary, section 2.2).
+//
+// One workgroup per (head, landmark).  Its window is a rectangle of the token
+// grid (adaptive bounds [floor(iG/P), ceil((i+1)G/P)) per axis, tokens
+// row-major); every window row is a contiguous run of tokens, and every
+// thread loads whole 16-byte chunks of token rows, so the reads coalesce.
+// Sums are kept in fp64 (exact for the value ranges met in practice: every
+// input value is a bf16 or fp32 number and a window holds at most a few
+// thousand of them), divided once by the window size, and rounded once to the
+// input dtype, nearest with ties to even.
+#include "mita_dev.h"
+#include "mita_plan.h"
+
+namespace mita {
+
+// float64 -> bf16, round to nearest even, from the 64-bit pattern (a detour
+// through float32 would round twice).  Values below the bf16 normal range
+// (|x| < 2^-126, never a mean of realistic data) go through float32.
+__device__ __forceinline__ __bf16 f64_to_bf16(double x) {
+  if (fabs(x) < 1.1754943508222875e-38) return (__bf16)(float)x;
+  uint64_t u = (uint64_t)__double_as_longlong(x);
+  u += 0x00000FFFFFFFFFFFull + ((u >> 45) & 1ull);  // half ulp - 1, plus lsb
+  u &= ~0x00001FFFFFFFFFFFull;                      // keep 1 + 7 significand bits
+  return (__bf16)(float)__longlong_as_double((long long)u);  // both casts exact
+}
+__device__ __forceinline__ void store_rounded(__bf16* p, double x) { *p = f64_to_bf16(x); }
+__device__ __forceinline__ void store_rounded(float* p, double x) { *p = (float)x; }
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_pool(const T* __restrict__ Q, T* __restrict__ Qt, int N,
+                                              int gh, int gw, int lh, int lw) {
+  constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  constexpr int CPT = D / EPC;              // chunks per token row
+  constexpr int TPP = 256 / CPT;            // tokens per pass of the block
+  const int m = lh * lw;
+  const int bh = blockIdx.x / m, i = blockIdx.x % m;
+  const long long lr = i / lw, lc = i % lw;
+  const int r0 = (int)((lr * gh) / lh), r1 = (int)(((lr + 1) * gh + lh - 1) / lh);
+  const int c0 = (int)((lc * gw) / lw), c1 = (int)(((lc + 1) * gw + lw - 1) / lw);
+  const int wc = c1 - c0, W = (r1 - r0) * wc;
+  const int chunk = threadIdx.x % CPT, tslot = threadIdx.x / CPT;
+
+  double acc[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
+  const T* base = Q + (size_t)bh * N * D + chunk * EPC;
+  for (int w = tslot; w < W; w += TPP) {
+    const long long n = (long long)(r0 + w / wc) * gw + c0 + w % wc;
+    const uint4 raw = *(const uint4*)(base + (size_t)n * D);
+    const T* v = (const T*)&raw;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] += (double)(float)v[e];
+  }
+  __shared__ double red[256][EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) red[threadIdx.x][e] = acc[e];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const int c = threadIdx.x, ch = c / EPC, e = c % EPC;
+    double s = 0.0;
+    for (int ts = 0; ts < TPP; ++ts) s += red[ts * CPT + ch][e];
+    store_rounded(Qt + ((size_t)bh * m + i) * D + c, s / (double)W);
+  }
+}
+
+__global__ void k_zero(uint4* __restrict__ p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+void launch_zero(const Plan& p) {
+  const size_t n16 = p.zero_bytes / 16;
+  if (n16 == 0) return;
+  const int blocks = (int)((n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024);
+  hipLaunchKernelGGL(k_zero, dim3(blocks), dim3(256), 0, p.stream, (uint4*)p.zero_begin, n16);
+}
+
+void launch_pool(const Plan& p) {
+  dim3 grid((unsigned)(p.BH * p.m));
+  if (p.dtype == 1 && p.d == 64)
+    hipLaunchKernelGGL((k_pool<__bf16, 64>), grid, dim3(256), 0, p.stream, (const __bf16*)p.Q, (__bf16*)p.qt, p.N, p.gh, p.gw, p.lh, p.lw);
+  else if (p.dtype == 1 && p.d == 32)
+    hipLaunchKernelGGL((k_pool<__bf16, 32>), grid, dim3(256), 0, p.stream, (const __bf16*)p.Q, (__bf16*)p.qt, p.N, p.gh, p.gw, p.lh, p.lw);
+  else if (p.dtype == 0 && p.d == 64)
+    hipLaunchKernelGGL((k_pool<float, 64>), grid, dim3(256), 0, p.stream, (const float*)p.Q, (float*)p.qt, p.N, p.gh, p.gw, p.lh, p.lw);
+  else
+    hipLaunchKernelGGL((k_pool<float, 32>), grid, dim3(256), 0, p.stream, (const float*)p.Q, (float*)p.qt, p.N, p.gh, p.gw, p.lh, p.lw);
+}
+
+}  // namespace mita

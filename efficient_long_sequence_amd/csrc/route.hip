@@ -1,0 +1,243 @@
+// Step 5 of MiTA: route every query to its top-s landmarks by q . q~_i
+// (MiTA tutorial (iwxt.cn), ch.4 step 4, paper section 3.2: the score only
+// selects experts, no gate mixes them), then group the queries by chosen
+// expert so the attention kernel can stage each expert's keys once for all of
+// its queries (the grouping the bit.fan article describes for the authors'
+// Algorithm 1; here a counting sort on the device with no host round trip).
+//
+//   k_route   one workgroup per (head, 64*NW queries): Q Q~^T on the matrix
+//             cores, landmarks streamed through LDS 32 at a time; each lane
+//             keeps a sorted top-s list for its query (ties to the lower
+//             landmark, which arrives first), the four lane groups of a query
+//             are merged at the end; a per-workgroup histogram of the chosen
+//             experts is added to the global per-(slot, head, expert) counts.
+//   k_scan    one workgroup: exclusive prefix of the counts (the start of each
+//             expert's bucket) and the work list of (expert, query tile)
+//             items, per slot.
+//   k_scatter writes each query into its expert's bucket (order inside a
+//             bucket is immaterial: every query's output depends only on its
+//             own row).
+#include "mita_dev.h"
+#include "mita_plan.h"
+#include "tile.h"
+
+namespace mita {
+
+struct Cand {
+  float v;
+  int i;
+};
+__device__ __forceinline__ bool better(float v, int i, float w, int j) { return v > w || (v == w && i < j); }
+
+// Insert (v, i) into a list sorted by `better`, keeping its first S entries.
+template <int S>
+__device__ __forceinline__ void insert_full(float* lv, int* li, float v, int i) {
+#pragma unroll
+  for (int t = S - 1; t >= 0; --t) {
+    const bool above = (t > 0) && better(v, i, lv[t - 1], li[t - 1]);
+    const bool here = better(v, i, lv[t], li[t]);
+    if (above) { lv[t] = lv[t - 1]; li[t] = li[t - 1]; }
+    else if (here) { lv[t] = v; li[t] = i; }
+  }
+}
+
+template <typename T, int D, int NW, int SMAX>
+__global__ __launch_bounds__(NW * 64) void k_route(const T* __restrict__ Q, const T* __restrict__ Qt,
+                                                   int32_t* __restrict__ route, int* __restrict__ counts,
+                                                   int N, int m, int s, int BH, int hist_lds) {
+  constexpr int NT = NW * 64;
+  using TL = TileLayout<T, D>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* buf0 = (T*)smem;
+  T* buf1 = buf0 + TL::K_ELEMS;
+  int* hist = (int*)(buf1 + TL::K_ELEMS);
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, li = lane % 16, lg = lane / 16;
+  const int bh = blockIdx.y;
+  const int qbase = blockIdx.x * (NW * 64) + wave * 64;
+  const T* Qh = Q + (size_t)bh * N * D;
+  const T* Qth = Qt + (size_t)bh * m * D;
+
+  if (hist_lds)
+    for (int x = tid; x < s * m; x += NT) hist[x] = 0;
+
+  Frag<T> qf[4][D / 32];
+  float lv[4][SMAX];
+  int lx[4][SMAX];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int n = qbase + b * 16 + li;
+#pragma unroll
+    for (int dc = 0; dc < D / 32; ++dc) {
+      if (n < N) load8(qf[b][dc], Qh + (size_t)n * D + dc * 32 + 8 * lg);
+      else zero(qf[b][dc]);
+    }
+#pragma unroll
+    for (int t = 0; t < SMAX; ++t) { lv[b][t] = -INFINITY; lx[b][t] = 0x7FFFFFFF; }
+  }
+
+  TileLoader<T, D, NT, false> ld;
+  auto rowL = [&](int i0) {
+    return [=](int r) -> const T* { const int i = i0 + r; return i < m ? Qth + (size_t)i * D : nullptr; };
+  };
+  auto none = [](int) -> const T* { return nullptr; };
+  const int nsteps = (m + 31) / 32;
+  ld.load(rowL(0), none);
+  ld.store(buf0, nullptr);
+  __syncthreads();
+  for (int st = 0; st < nsteps; ++st) {
+    const int i0 = st * 32;
+    T* cur = (st & 1) ? buf1 : buf0;
+    T* nxt = (st & 1) ? buf0 : buf1;
+    const bool more = st + 1 < nsteps;
+    if (more) ld.load(rowL(i0 + 32), none);
+    StepFrags<T, D> f;
+    f.load_keys(cur, li, lg);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      float sc[8];
+      step_scores(f, qf[b], sc);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int i = i0 + slot_key(t, lg);
+        // within a lane landmarks arrive in increasing order: strict '>'
+        // keeps the lower index on ties
+        if (i < m && sc[t] > lv[b][SMAX - 1]) insert_full<SMAX>(lv[b], lx[b], sc[t], i);
+      }
+    }
+    if (more) ld.store(nxt, nullptr);
+    __syncthreads();
+  }
+
+  // merge the four lane groups of each query
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+#pragma unroll
+    for (int sh = 16; sh <= 32; sh <<= 1) {
+      float ov[SMAX];
+      int ox[SMAX];
+#pragma unroll
+      for (int t = 0; t < SMAX; ++t) { ov[t] = __shfl_xor(lv[b][t], sh); ox[t] = __shfl_xor(lx[b][t], sh); }
+#pragma unroll
+      for (int t = 0; t < SMAX; ++t) insert_full<SMAX>(lv[b], lx[b], ov[t], ox[t]);
+    }
+    const int n = qbase + b * 16 + li;
+    if (lg == 0 && n < N) {
+      int32_t* dst = route + ((size_t)bh * N + n) * s;
+#pragma unroll
+      for (int t = 0; t < SMAX; ++t) {
+        if (t < s) {
+          // a valid list always holds s landmarks; the clamp only keeps
+          // non-finite inputs (unspecified results) inside the buffers
+          const int e = min(max(lx[b][t], 0), m - 1);
+          dst[t] = e;
+          if (hist_lds) atomicAdd(hist + t * m + e, 1);
+          else atomicAdd(counts + ((size_t)t * BH + bh) * m + e, 1);
+        }
+      }
+    }
+  }
+  if (hist_lds) {
+    __syncthreads();
+    for (int x = tid; x < s * m; x += NT) {
+      const int c = hist[x];
+      if (c) atomicAdd(counts + ((size_t)(x / m) * BH + bh) * m + (x % m), c);
+    }
+  }
+}
+
+// Exclusive prefix of the expert counts and the work list, for every slot.
+// One workgroup of 1024 threads; each thread owns a contiguous segment.
+__global__ __launch_bounds__(1024) void k_scan(const int* __restrict__ counts, int* __restrict__ gpre,
+                                               WorkItem* __restrict__ wl, int* __restrict__ wl_count,
+                                               int E, int m, int s, int T, int UB) {
+  __shared__ int sn[1024], stl[1024];
+  const int tid = threadIdx.x;
+  const int seg = (E + 1023) / 1024;
+  const int lo = min(E, tid * seg), hi = min(E, lo + seg);
+  for (int t = 0; t < s; ++t) {
+    const int* c = counts + (size_t)t * E;
+    int n_sum = 0, t_sum = 0;
+    for (int x = lo; x < hi; ++x) { n_sum += c[x]; t_sum += (c[x] + T - 1) / T; }
+    sn[tid] = n_sum;
+    stl[tid] = t_sum;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
+      const int a = tid >= off ? sn[tid - off] : 0, b = tid >= off ? stl[tid - off] : 0;
+      __syncthreads();
+      sn[tid] += a;
+      stl[tid] += b;
+      __syncthreads();
+    }
+    int nb = sn[tid] - n_sum, tb = stl[tid] - t_sum;
+    if (tid == 1023) wl_count[t] = stl[1023];
+    WorkItem* w = wl + (size_t)t * UB;
+    for (int x = lo; x < hi; ++x) {
+      const int n = c[x];
+      gpre[(size_t)t * E + x] = nb;
+      for (int q = 0; q * T < n; ++q) {
+        WorkItem it;
+        it.start = nb + q * T;
+        it.count = min(T, n - q * T);
+        it.be = x;
+        it.pad = 0;
+        w[tb++] = it;
+      }
+      nb += n;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ route, const int* __restrict__ gpre,
+                                                 int* __restrict__ cursor, int32_t* __restrict__ perm, int N,
+                                                 int m, int s, int BH) {
+  const int bh = blockIdx.y;
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  for (int t = 0; t < s; ++t) {
+    const int e = route[((size_t)bh * N + n) * s + t];
+    const size_t x = ((size_t)t * BH + bh) * m + e;
+    const int pos = gpre[x] + atomicAdd(cursor + x, 1);
+    perm[(size_t)t * BH * N + pos] = n;
+  }
+}
+
+template <typename T, int D, int SMAX>
+static void launch_route_t(const Plan& p) {
+  using TL = TileLayout<T, D>;
+  constexpr int NW = 4;
+  const int hist_lds = (p.s * p.m <= 16384) ? 1 : 0;
+  const size_t lds = 2 * TL::K_ELEMS * sizeof(T) + (hist_lds ? (size_t)p.s * p.m * 4 : 0);
+  dim3 grid((unsigned)((p.N + NW * 64 - 1) / (NW * 64)), (unsigned)p.BH);
+  hipLaunchKernelGGL((k_route<T, D, NW, SMAX>), grid, dim3(NW * 64), lds, p.stream, (const T*)p.Q,
+                     (const T*)p.qt, p.route, p.counts, p.N, p.m, p.s, p.BH, hist_lds);
+}
+
+template <typename T, int D>
+static void launch_route_s(const Plan& p) {
+  switch (p.smax) {
+    case 1: launch_route_t<T, D, 1>(p); break;
+    case 2: launch_route_t<T, D, 2>(p); break;
+    case 4: launch_route_t<T, D, 4>(p); break;
+    default: launch_route_t<T, D, 8>(p); break;
+  }
+}
+
+void launch_route(const Plan& p) {
+  if (p.dtype == 0) {
+    if (p.d == 32) launch_route_s<float, 32>(p); else launch_route_s<float, 64>(p);
+  } else {
+    if (p.d == 32) launch_route_s<__bf16, 32>(p); else launch_route_s<__bf16, 64>(p);
+  }
+}
+
+void launch_bucket(const Plan& p) {
+  const int E = p.BH * p.m;
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, p.stream, p.counts, p.gpre, p.wl, p.wl_count, E, p.m, p.s,
+                     p.T, p.UB);
+  dim3 grid((unsigned)((p.N + 255) / 256), (unsigned)p.BH);
+  hipLaunchKernelGGL(k_scatter, grid, dim3(256), 0, p.stream, p.route, p.gpre, p.cursor, p.perm, p.N, p.m, p.s,
+                     p.BH);
+}
+
+}  // namespace mita

@@ -1,0 +1,451 @@
+// Steps 2-4 of MiTA: landmark scores, per-landmark top-k and shared values.
+// (MiTA tutorial (iwxt.cn), ch.4 steps 2-3, paper section 3.2: every
+// landmark q~_i scores all N keys with q~_i . k_j / sqrt(d); its top-k keys
+// form routed expert i; the softmax of the same scores over all N keys
+// weights V into the shared value v~_i.)
+//
+// Kernels, in launch order:
+//   k_est     (large N only) scores every landmark against a strided sample of
+//             the keys on the matrix cores and keeps the maximum of each of G
+//             sample groups;
+//   k_tau     per landmark row: the J-th largest group maximum becomes the
+//             candidate threshold tau, the largest one the first softmax
+//             offset;
+//   k_score   one workgroup per (head, landmark-row tile, key chunk): the
+//             score tile Q~ K^T on the matrix cores, an online softmax with
+//             P.V on the matrix cores (partial v~ per chunk), and every score
+//             >= tau kept as a candidate (all scores when N is small).  The
+//             m x N score matrix never reaches HBM;
+//   k_final   per landmark row: merges the v~ partials (the rescaled-sum
+//             identity (Z1 o1 + Z2 o2)/(Z1 + Z2) of tutorial ch.4) and selects
+//             the exact top-k from the candidates with a block bitonic sort;
+//   k_fallback exact streaming top-k for any row whose candidate count was
+//             below k or above capacity (a threshold estimate that missed).
+//
+// Exactness of the selection: the candidates of a row are exactly the keys
+// whose fp32 score is >= tau, an upper set of the score order.  If there are
+// at least k of them, the k largest candidates (ties to the lower index) are
+// the k largest keys of the whole row; otherwise the row is redone by
+// k_fallback.  tau only decides how much work this takes, never the result.
+#include "mita_dev.h"
+#include "mita_plan.h"
+#include "tile.h"
+
+namespace mita {
+
+__device__ __forceinline__ int sample_pos(int t, int sigma) {
+  uint32_t h = (uint32_t)t * 2654435761u;
+  h ^= h >> 15;
+  return t * sigma + (int)(h % (uint32_t)sigma);
+}
+
+// ---------------------------------------------------------------------------
+// sampled group maxima
+// ---------------------------------------------------------------------------
+template <typename T, int D, int NW, int IB>
+__global__ __launch_bounds__(NW * 64) void k_est(const T* __restrict__ K, const T* __restrict__ Qt,
+                                                 float* __restrict__ gmax, int N, int m, int sigma,
+                                                 int NS, int G, int gpb) {
+  constexpr int NT = NW * 64;
+  using TL = TileLayout<T, D>;
+  __shared__ __align__(16) T ks[TL::K_ELEMS];
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, li = lane % 16, lg = lane / 16;
+  const int bh = blockIdx.z, rt = blockIdx.y;
+  const int rbase = rt * (NW * 16 * IB) + wave * 16 * IB;
+  const T* Kh = K + (size_t)bh * N * D;
+
+  Frag<T> qf[IB][D / 32];
+#pragma unroll
+  for (int b = 0; b < IB; ++b) {
+    const int row = rbase + b * 16 + li;
+#pragma unroll
+    for (int dc = 0; dc < D / 32; ++dc) {
+      if (row < m) load8(qf[b][dc], Qt + ((size_t)bh * m + row) * D + dc * 32 + 8 * lg);
+      else zero(qf[b][dc]);
+    }
+  }
+  TileLoader<T, D, NT, false> ld;
+  const int Sg = NS / G;
+  for (int gl = 0; gl < gpb; ++gl) {
+    const int grp = blockIdx.x * gpb + gl;
+    if (grp >= G) break;
+    const int t_begin = grp * Sg, t_end = (grp == G - 1) ? NS : t_begin + Sg;
+    float run[IB];
+#pragma unroll
+    for (int b = 0; b < IB; ++b) run[b] = -INFINITY;
+    for (int t0 = t_begin; t0 < t_end; t0 += 32) {
+      ld.load([&](int r) -> const T* {
+                const int t = t0 + r;
+                return t < t_end ? Kh + (size_t)sample_pos(t, sigma) * D : nullptr;
+              },
+              [](int) -> const T* { return nullptr; });
+      __syncthreads();
+      ld.store(ks, nullptr);
+      __syncthreads();
+      StepFrags<T, D> f;
+      f.load_keys(ks, li, lg);
+      const int nv = min(32, t_end - t0);
+#pragma unroll
+      for (int b = 0; b < IB; ++b) {
+        float sc[8];
+        step_scores(f, qf[b], sc);
+        if (nv < 32) {
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            if (slot_key(t, lg) >= nv) sc[t] = -INFINITY;
+        }
+        run[b] = fmaxf(run[b], max8(sc));
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < IB; ++b) {
+      const float gm = wave_max_groups(run[b]);
+      const int row = rbase + b * 16 + li;
+      if (row < m && lg == 0) gmax[((size_t)bh * m + row) * G + grp] = gm;
+    }
+  }
+}
+
+__global__ void k_fill(float* __restrict__ p, int n, float v) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = v;
+}
+
+__global__ __launch_bounds__(256) void k_tau(const float* __restrict__ gmax, float* __restrict__ tau,
+                                             float* __restrict__ mhat, int G, int J) {
+  __shared__ float a[512];
+  const size_t r = blockIdx.x;
+  const int P = next_pow2(G);
+  for (int i = threadIdx.x; i < P; i += blockDim.x) a[i] = i < G ? gmax[r * G + i] : -INFINITY;
+  __syncthreads();
+  block_bitonic_sort(a, P, true);
+  if (threadIdx.x == 0) {
+    tau[r] = a[J - 1];
+    mhat[r] = a[0];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fused scores, partial shared values and candidates
+// ---------------------------------------------------------------------------
+template <typename T, int D, int NW, int IB>
+__global__ __launch_bounds__(NW * 64) void k_score(
+    const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ Qt,
+    const float* __restrict__ tau_in, const float* __restrict__ mhat_in, float* __restrict__ vpart,
+    uint64_t* __restrict__ cand, int* __restrict__ cand_cnt, int N, int m, int L, int C, int capg,
+    int cb_cap, float cscale) {
+  constexpr int NT = NW * 64;
+  constexpr int R = NW * 16 * IB;
+  using TL = TileLayout<T, D>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* buf0 = (T*)smem;
+  T* buf1 = buf0 + TL::ELEMS;
+  uint2* s_cand = (uint2*)(smem + 2 * TL::ELEMS * sizeof(T));
+  int* s_rowcnt = (int*)(s_cand + cb_cap);
+  int* s_rowbase = s_rowcnt + R;
+  int* s_ncand = s_rowbase + R;
+
+  const bool dense = tau_in == nullptr;
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, li = lane % 16, lg = lane / 16;
+  const int ch = blockIdx.x, rt = blockIdx.y, bh = blockIdx.z;
+  const int rbase = rt * R + wave * 16 * IB;
+  const T* Kh = K + (size_t)bh * N * D;
+  const T* Vh = V + (size_t)bh * N * D;
+  const int j_begin = ch * L, j_end = min(N, j_begin + L);
+
+  if (!dense) {
+    for (int r = tid; r < R; r += NT) s_rowcnt[r] = 0;
+    if (tid == 0) *s_ncand = 0;
+  }
+
+  Frag<T> qf[IB][D / 32];
+  float M[IB], Z[IB], tau[IB];
+  f32x4 acc[IB][D / 16];
+#pragma unroll
+  for (int b = 0; b < IB; ++b) {
+    const int row = rbase + b * 16 + li;
+    const bool valid = row < m;
+#pragma unroll
+    for (int dc = 0; dc < D / 32; ++dc) {
+      if (valid) load8(qf[b][dc], Qt + ((size_t)bh * m + row) * D + dc * 32 + 8 * lg);
+      else zero(qf[b][dc]);
+    }
+    M[b] = (mhat_in != nullptr && valid) ? mhat_in[(size_t)bh * m + row] * cscale : M0;
+    tau[b] = dense ? -INFINITY : (valid ? tau_in[(size_t)bh * m + row] : INFINITY);
+    Z[b] = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb) acc[b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  auto rowK = [&](int j0) {
+    return [=](int r) -> const T* { const int j = j0 + r; return j < j_end ? Kh + (size_t)j * D : nullptr; };
+  };
+  auto rowV = [&](int j0) {
+    return [=](int r) -> const T* { const int j = j0 + r; return j < j_end ? Vh + (size_t)j * D : nullptr; };
+  };
+
+  TileLoader<T, D, NT, true> ld;
+  const int nsteps = (j_end - j_begin + 31) / 32;
+  ld.load(rowK(j_begin), rowV(j_begin));
+  ld.store(buf0, buf0 + TL::K_ELEMS);
+  __syncthreads();
+  for (int st = 0; st < nsteps; ++st) {
+    const int j0 = j_begin + st * 32;
+    T* cur = (st & 1) ? buf1 : buf0;
+    T* nxt = (st & 1) ? buf0 : buf1;
+    const bool more = st + 1 < nsteps;
+    if (more) ld.load(rowK(j0 + 32), rowV(j0 + 32));
+    StepFrags<T, D> f;
+    f.load_keys(cur, li, lg);
+    f.load_vals(cur + TL::K_ELEMS, li, lg);
+    const int nv = min(32, j_end - j0);
+#pragma unroll
+    for (int b = 0; b < IB; ++b) {
+      float sc[8];
+      step_scores(f, qf[b], sc);
+      if (nv < 32) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          if (slot_key(t, lg) >= nv) sc[t] = -INFINITY;
+      }
+      const float mx = max8(sc);
+      const int row = rbase + b * 16 + li;
+      if (dense) {
+        if (row < m) {
+          uint64_t* dst = cand + ((size_t)bh * m + row) * capg + j0;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const int kl = slot_key(t, lg);
+            if (kl < nv) dst[kl] = ckey(sc[t], (uint32_t)(j0 + kl));
+          }
+        }
+      } else if (wave_any(mx >= tau[b])) {
+        if (mx >= tau[b]) {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            if (sc[t] >= tau[b]) {
+              const int jl = j0 + slot_key(t, lg) - j_begin;
+              const int e = atomicAdd(s_ncand, 1);
+              if (e < cb_cap) {
+                s_cand[e] = make_uint2(__float_as_uint(sc[t]), ((uint32_t)(row - rt * R) << 23) | (uint32_t)jl);
+              } else {
+                const int pos = atomicAdd(cand_cnt + (size_t)bh * m + row, 1);
+                if (pos < capg) cand[((size_t)bh * m + row) * capg + pos] = ckey(sc[t], (uint32_t)(j_begin + jl));
+              }
+            }
+          }
+        }
+      }
+      softmax_step(f, sc, mx, cscale, M[b], Z[b], acc[b]);
+    }
+    if (more) ld.store(nxt, nxt + TL::K_ELEMS);
+    __syncthreads();
+  }
+
+  // partial shared values of this chunk: (max, normaliser, 2 pad, unnormalised sums)
+#pragma unroll
+  for (int b = 0; b < IB; ++b) {
+    const float Zt = wave_sum_groups(Z[b]);
+    const int row = rbase + b * 16 + li;
+    if (row < m) {
+      float* dst = vpart + (((size_t)bh * m + row) * C + ch) * (D + 4);
+      if (lg == 0) { dst[0] = M[b]; dst[1] = Zt; }
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb)
+        *(float4*)(dst + 4 + cb * 16 + 4 * lg) = make_float4(acc[b][cb][0], acc[b][cb][1], acc[b][cb][2], acc[b][cb][3]);
+    }
+  }
+
+  if (!dense) {
+    const int ns = min(*s_ncand, cb_cap);
+    for (int e = tid; e < ns; e += NT) atomicAdd(s_rowcnt + (s_cand[e].y >> 23), 1);
+    __syncthreads();
+    for (int r = tid; r < R; r += NT) {
+      const int row = rt * R + r, c = s_rowcnt[r];
+      s_rowbase[r] = (c > 0 && row < m) ? atomicAdd(cand_cnt + (size_t)bh * m + row, c) : 0;
+      s_rowcnt[r] = 0;
+    }
+    __syncthreads();
+    for (int e = tid; e < ns; e += NT) {
+      const uint2 v = s_cand[e];
+      const int r = (int)(v.y >> 23), row = rt * R + r;
+      const int pos = s_rowbase[r] + atomicAdd(s_rowcnt + r, 1);
+      if (pos < capg)
+        cand[((size_t)bh * m + row) * capg + pos] = ckey(__uint_as_float(v.x), (uint32_t)(j_begin + (int)(v.y & 0x7FFFFFu)));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// selection and shared-value merge, one workgroup per landmark row
+// ---------------------------------------------------------------------------
+// Writes the k indices of the block-sorted keys a[0..k) (descending order)
+// in ascending index order to out[0..k).  Reuses a[] as scratch.
+__device__ void emit_topk(uint64_t* a, int k, int32_t* out) {
+  const int Pk = next_pow2(k < 2 ? 2 : k);
+  for (int j = threadIdx.x; j < Pk; j += blockDim.x)
+    a[j] = j < k ? (uint64_t)ckey_idx(a[j]) : ~0ull;
+  __syncthreads();
+  block_bitonic_sort(a, Pk, false);
+  for (int j = threadIdx.x; j < k; j += blockDim.x) out[j] = (int32_t)a[j];
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_final(const float* __restrict__ vpart, const uint64_t* __restrict__ cand,
+                                               const int* __restrict__ cand_cnt, int32_t* __restrict__ topk,
+                                               float* __restrict__ vt32, T* __restrict__ vtT, int* __restrict__ fail,
+                                               int N, int k, int C, int capg, int dense) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint64_t* a = (uint64_t*)smem;
+  const size_t r = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid < D) {
+    const float* pr = vpart + r * C * (D + 4);
+    float Mx = M0;
+    for (int c = 0; c < C; ++c) Mx = fmaxf(Mx, pr[(size_t)c * (D + 4)]);
+    float Zs = 0.f, s = 0.f;
+    for (int c = 0; c < C; ++c) {
+      const float* q = pr + (size_t)c * (D + 4);
+      const float w = __builtin_amdgcn_exp2f(q[0] - Mx);
+      Zs += q[1] * w;
+      s += q[4 + tid] * w;
+    }
+    const float v = s / Zs;
+    vt32[r * D + tid] = v;
+    vtT[r * D + tid] = from_f32<T>(v);
+  }
+  const int cnt = dense ? N : cand_cnt[r];
+  if (cnt < k || cnt > capg) {
+    if (tid == 0) fail[r] = 1;
+    return;
+  }
+  if (tid == 0) fail[r] = 0;
+  const int P = next_pow2(cnt < 2 ? 2 : cnt);
+  const uint64_t* src = cand + r * capg;
+  for (int j = tid; j < P; j += blockDim.x) a[j] = j < cnt ? src[j] : 0ull;
+  __syncthreads();
+  block_bitonic_sort(a, P, true);
+  emit_topk(a, k, topk + r * k);
+}
+
+// Exact streaming top-k of one landmark row over all N keys (fp32 dot
+// products on the vector units), for rows k_final flagged.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_fallback(const T* __restrict__ K, const T* __restrict__ Qt,
+                                                  const int* __restrict__ fail, int32_t* __restrict__ topk,
+                                                  int N, int m, int k) {
+  const size_t r = blockIdx.x;
+  if (fail[r] == 0) return;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint64_t* a = (uint64_t*)smem;
+  __shared__ float q[D];
+  __shared__ int nb;
+  __shared__ uint64_t theta;
+  const int tid = threadIdx.x;
+  const size_t bh = r / m;
+  const T* Kh = K + bh * (size_t)N * D;
+  if (tid < D) q[tid] = to_f32<T>(Qt[r * D + tid]);
+  if (tid == 0) { nb = 0; theta = 0ull; }
+  __syncthreads();
+  const int keep = 2 * k;
+  for (int j0 = 0; j0 < N; j0 += 256) {
+    const int j = j0 + tid;
+    if (j < N) {
+      const T* kr = Kh + (size_t)j * D;
+      float s = 0.f;
+      for (int c = 0; c < D; ++c) s = __builtin_fmaf(q[c], to_f32<T>(kr[c]), s);
+      const uint64_t key = ckey(s, (uint32_t)j);
+      if (key > theta) a[atomicAdd(&nb, 1)] = key;
+    }
+    __syncthreads();
+    const int n = nb;
+    if (n > keep) {
+      const int P = next_pow2(n);
+      for (int i = n + tid; i < P; i += blockDim.x) a[i] = 0ull;
+      __syncthreads();
+      block_bitonic_sort(a, P, true);
+      if (tid == 0) { nb = k; theta = a[k - 1]; }
+    }
+    __syncthreads();
+  }
+  const int n = nb;
+  const int P = next_pow2(n < 2 ? 2 : n);
+  for (int i = n + tid; i < P; i += blockDim.x) a[i] = 0ull;
+  __syncthreads();
+  block_bitonic_sort(a, P, true);
+  emit_topk(a, k, topk + r * k);
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <typename T, int D, int NW, int IB>
+static void launch_score_t(const Plan& p) {
+  using TL = TileLayout<T, D>;
+  constexpr int R = NW * 16 * IB;
+  const bool dense = p.dense != 0;
+  if (!dense && p.force_fallback) {
+    const int n = p.BH * p.m;
+    hipLaunchKernelGGL(k_fill, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, p.stream, p.tau, n, INFINITY);
+  } else if (!dense) {
+    dim3 grid((unsigned)((p.G + p.est_gpb - 1) / p.est_gpb), (unsigned)p.sc_rt, (unsigned)p.BH);
+    hipLaunchKernelGGL((k_est<T, D, NW, IB>), grid, dim3(NW * 64), 0, p.stream, (const T*)p.K, (const T*)p.qt,
+                       p.gmax, p.N, p.m, p.sigma, p.NS, p.G, p.est_gpb);
+    hipLaunchKernelGGL(k_tau, dim3((unsigned)(p.BH * p.m)), dim3(256), 0, p.stream, p.gmax, p.tau, p.mhat, p.G, p.J);
+  }
+}
+
+template <typename T, int D, int NW, int IB>
+static void launch_score_main(const Plan& p) {
+  using TL = TileLayout<T, D>;
+  constexpr int R = NW * 16 * IB;
+  const bool dense = p.dense != 0;
+  const size_t lds = 2 * TL::ELEMS * sizeof(T) + (dense ? 0 : (size_t)p.cb * 8 + 2 * R * 4 + 16);
+  dim3 grid((unsigned)p.C, (unsigned)p.sc_rt, (unsigned)p.BH);
+  if (lds > 65536)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_score<T, D, NW, IB>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL((k_score<T, D, NW, IB>), grid, dim3(NW * 64), lds, p.stream, (const T*)p.K, (const T*)p.V,
+                     (const T*)p.qt, dense ? nullptr : p.tau, (dense || p.force_fallback) ? nullptr : p.mhat, p.vpart, p.cand,
+                     p.cand_cnt, p.N, p.m, p.L, p.C, p.capg, dense ? 0 : p.cb, p.cscale);
+}
+
+template <typename T, int D>
+static void launch_final_t(const Plan& p) {
+  const size_t lds = (size_t)next_pow2(p.capg < 2 ? 2 : p.capg) * 8;
+  hipLaunchKernelGGL((k_final<T, D>), dim3((unsigned)(p.BH * p.m)), dim3(256), lds, p.stream, p.vpart, p.cand,
+                     p.cand_cnt, p.topk, p.vt32, (T*)p.vtT, p.fail, p.N, p.k, p.C, p.capg, p.dense);
+  if (!p.dense) {
+    const size_t lds2 = (size_t)next_pow2(2 * p.k + 256) * 8;
+    hipLaunchKernelGGL((k_fallback<T, D>), dim3((unsigned)(p.BH * p.m)), dim3(256), lds2, p.stream,
+                       (const T*)p.K, (const T*)p.qt, p.fail, p.topk, p.N, p.m, p.k);
+  }
+}
+
+#define MITA_SCORE_DISPATCH(FN)                                                     \
+  do {                                                                              \
+    if (p.dtype == 0) {                                                             \
+      if (p.d == 32) FN<float, 32, 4, 1>(p); else FN<float, 64, 4, 1>(p);           \
+    } else if (p.d == 32) {                                                         \
+      if (p.sc_nw == 4) FN<__bf16, 32, 4, 1>(p);                                    \
+      else if (p.sc_ib == 1) FN<__bf16, 32, 8, 1>(p);                               \
+      else if (p.sc_ib == 2) FN<__bf16, 32, 8, 2>(p);                               \
+      else FN<__bf16, 32, 8, 4>(p);                                                 \
+    } else {                                                                        \
+      if (p.sc_nw == 4) FN<__bf16, 64, 4, 1>(p);                                    \
+      else if (p.sc_ib == 1) FN<__bf16, 64, 8, 1>(p);                               \
+      else if (p.sc_ib == 2) FN<__bf16, 64, 8, 2>(p);                               \
+      else FN<__bf16, 64, 8, 4>(p);                                                 \
+    }                                                                               \
+  } while (0)
+
+void launch_estimate(const Plan& p) { MITA_SCORE_DISPATCH(launch_score_t); }
+void launch_score(const Plan& p) { MITA_SCORE_DISPATCH(launch_score_main); }
+void launch_final(const Plan& p) {
+  if (p.dtype == 0) {
+    if (p.d == 32) launch_final_t<float, 32>(p); else launch_final_t<float, 64>(p);
+  } else {
+    if (p.d == 32) launch_final_t<__bf16, 32>(p); else launch_final_t<__bf16, 64>(p);
+  }
+}
+
+}  // namespace mita

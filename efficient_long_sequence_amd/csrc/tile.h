@@ -1,0 +1,180 @@
+// A 32-row step of keys (and values) staged in LDS for the matrix cores.
+//
+// Keys are stored row-major, Ks[j][c] with a padded row stride KS, which is
+// the A-operand order of the score product (key rows, d along K).  Values are
+// stored transposed, Vs[c][j] with row stride VS, which is the A-operand
+// order of O^T = V^T P^T (d rows, keys along K).  Each thread first pulls its
+// 16-byte chunks of the step into registers (so the global loads of step
+// i+1 overlap the matrix work of step i) and then writes them to LDS; the
+// transposing write packs two key rows per 32-bit word for bf16.
+#pragma once
+#include "mita_dev.h"
+
+namespace mita {
+
+template <typename T, int D>
+struct TileLayout {
+  static constexpr int EPC = 16 / (int)sizeof(T);     // elements per 16 bytes
+  static constexpr int KS = D + EPC;   // padded key row (elements); 16-byte aligned rows
+  static constexpr int VS = 36;        // padded V^T row (elements); 8-byte (bf16) / 16-byte (f32) aligned
+  static constexpr int K_ELEMS = 32 * KS;
+  static constexpr int V_ELEMS = D * VS;
+  static constexpr int ELEMS = K_ELEMS + V_ELEMS;
+};
+
+template <typename T, int D, int NT, bool WITH_V>
+struct TileLoader {
+  using L = TileLayout<T, D>;
+  static constexpr int EPC = L::EPC;
+  static constexpr int CPR = D / EPC;                  // 16-byte chunks per row
+  static constexpr int KCH = 32 * CPR;
+  static constexpr int KPT = (KCH + NT - 1) / NT;
+  static constexpr int VROWS = sizeof(T) == 2 ? 2 : 1;  // rows per transposing task
+  static constexpr int VCH = WITH_V ? (32 / VROWS) * CPR : 0;
+  static constexpr int VPT = WITH_V ? (VCH + NT - 1) / NT : 0;
+  static constexpr int VS = L::VS;
+
+  uint4 kreg[KPT];
+  uint4 vreg[VPT > 0 ? VPT : 1][VROWS];
+
+  // rk(j) / rv(j): pointer to key / value row j of the step, or nullptr for a
+  // row past the end (it is staged as zeros).
+  template <class RK, class RV>
+  __device__ __forceinline__ void load(RK rk, RV rv) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int c = 0; c < KPT; ++c) {
+      const int i = tid + c * NT;
+      kreg[c] = make_uint4(0, 0, 0, 0);
+      if (i < KCH) {
+        const T* p = rk(i / CPR);
+        if (p) kreg[c] = *(const uint4*)(p + (i % CPR) * EPC);
+      }
+    }
+    if constexpr (WITH_V) {
+#pragma unroll
+      for (int c = 0; c < VPT; ++c) {
+        const int i = tid + c * NT;
+#pragma unroll
+        for (int r = 0; r < VROWS; ++r) {
+          vreg[c][r] = make_uint4(0, 0, 0, 0);
+          if (i < VCH) {
+            const T* p = rv((i / CPR) * VROWS + r);
+            if (p) vreg[c][r] = *(const uint4*)(p + (i % CPR) * EPC);
+          }
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(T* Ks, T* Vs) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int c = 0; c < KPT; ++c) {
+      const int i = tid + c * NT;
+      if (i < KCH) *(uint4*)(Ks + (i / CPR) * L::KS + (i % CPR) * EPC) = kreg[c];
+    }
+    if constexpr (WITH_V) {
+#pragma unroll
+      for (int c = 0; c < VPT; ++c) {
+        const int i = tid + c * NT;
+        if (i < VCH) {
+          const int jp = i / CPR, c0 = (i % CPR) * EPC;
+          if constexpr (sizeof(T) == 2) {
+            const uint32_t* a = (const uint32_t*)&vreg[c][0];
+            const uint32_t* b = (const uint32_t*)&vreg[c][1];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              // elements 2u, 2u+1 of rows 2jp (a) and 2jp+1 (b)
+              const uint32_t lo = (a[u] & 0xFFFFu) | (b[u] << 16);
+              const uint32_t hi = (a[u] >> 16) | (b[u] & 0xFFFF0000u);
+              *(uint32_t*)(Vs + (c0 + 2 * u) * VS + 2 * jp) = lo;
+              *(uint32_t*)(Vs + (c0 + 2 * u + 1) * VS + 2 * jp) = hi;
+            }
+          } else {
+            const float* a = (const float*)&vreg[c][0];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) Vs[(c0 + u) * VS + jp] = a[u];
+          }
+        }
+      }
+    }
+  }
+};
+
+// Per-lane key slot -> key offset inside a 32-key step.
+__device__ __forceinline__ int slot_key(int t, int g) { return t < 4 ? 4 * g + t : 16 + 4 * g + (t - 4); }
+
+// A operands of one step for a wave: keys (2 tiles of 16 x D) and V^T.
+template <typename T, int D>
+struct StepFrags {
+  Frag<T> ka[2][D / 32];
+  Frag<T> va[D / 16];
+  __device__ __forceinline__ void load_keys(const T* Ks, int li, int g) {
+    using L = TileLayout<T, D>;
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int dc = 0; dc < D / 32; ++dc) load8(ka[jt][dc], Ks + (jt * 16 + li) * L::KS + dc * 32 + 8 * g);
+  }
+  __device__ __forceinline__ void load_vals(const T* Vs, int li, int g) {
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb) {
+      const T* row = Vs + (cb * 16 + li) * TileLayout<T, D>::VS;
+      load4x2(va[cb], row + 4 * g, row + 16 + 4 * g);
+    }
+  }
+};
+
+// Scores of one 16-query block against the 32 keys of the step: 8 per lane.
+template <typename T, int D>
+__device__ __forceinline__ void step_scores(const StepFrags<T, D>& f, const Frag<T>* qf, float* sc) {
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int dc = 0; dc < D / 32; ++dc) {
+    mma16(s0, f.ka[0][dc], qf[dc]);
+    mma16(s1, f.ka[1][dc], qf[dc]);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) { sc[r] = s0[r]; sc[4 + r] = s1[r]; }
+}
+
+// Online-softmax update of one 16-query block with the 8 raw scores of this
+// lane (already -inf where masked).  M is the running maximum in the scaled
+// log2 domain (identical in the four lane groups of a query), Z this lane's
+// share of the normaliser, acc the O^T accumulator.
+template <typename T, int D>
+__device__ __forceinline__ void softmax_step(const StepFrags<T, D>& f, const float* sc, float mx_raw,
+                                             float cscale, float& M, float& Z, f32x4* acc) {
+  const float xm = mx_raw * cscale;
+  if (wave_any(xm > M + THRESH)) {
+    // The decision uses the query's own maximum over its four lane groups,
+    // so each query's running maximum (and every rounding that follows from
+    // it) is independent of which other queries share the wave.
+    const float gm = wave_max_groups(xm);
+    if (gm > M + THRESH) {
+      const float alpha = __builtin_amdgcn_exp2f(M - gm);
+      Z *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[cb][r] *= alpha;
+      M = gm;
+    }
+  }
+  const float nm = -M;
+  float p[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t], cscale, nm));
+  Z += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  Frag<T> pf;
+  set8(pf, p);
+#pragma unroll
+  for (int cb = 0; cb < D / 16; ++cb) mma16(acc[cb], f.va[cb], pf);
+}
+
+__device__ __forceinline__ float max8(const float* s) {
+  return fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+}
+
+}  // namespace mita

@@ -1,0 +1,176 @@
+"""Python binding of libmita (ctypes): argument marshalling only.
+
+Every step of the forward pass runs in the library's HIP kernels; this module
+turns torch tensors into device pointers and the current HIP stream, sizes
+the workspace, and raises on a non-OK status.  There is no CPU fallback: if
+``libmita.so`` is missing, every entry point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmita.so")
+
+F32, BF16 = 0, 1
+
+STATUS = {
+    0: "MITA_OK", 1: "MITA_ERR_NULL", 2: "MITA_ERR_SHAPE", 3: "MITA_ERR_PARAM",
+    4: "MITA_ERR_UNSUPPORTED", 5: "MITA_ERR_WORKSPACE", 6: "MITA_ERR_HIP",
+}
+
+EXPORTS = [
+    "mita_workspace_bytes", "mita_forward", "mita_forward_timed", "mita_num_stages",
+    "mita_stage_name", "mita_events_create", "mita_events_destroy", "mita_events_elapsed",
+    "mita_status_str", "mita_version",
+]
+
+
+class Pool(ctypes.Structure):
+    _fields_ = [("grid_h", ctypes.c_int), ("grid_w", ctypes.c_int),
+                ("land_h", ctypes.c_int), ("land_w", ctypes.c_int)]
+
+
+class Debug(ctypes.Structure):
+    _fields_ = [("topk", ctypes.c_void_p), ("route", ctypes.c_void_p),
+                ("vtilde", ctypes.c_void_p), ("qtilde", ctypes.c_void_p)]
+
+
+class MitaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmita.so from the package directory (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m efficient_long_sequence_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    c_int, c_size, vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+    L.mita_workspace_bytes.restype = c_size
+    L.mita_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int, Pool, c_int, c_int, c_int]
+    fwd = [vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, Pool, c_int, c_int, c_int,
+           ctypes.POINTER(Debug), vp, c_size, vp]
+    L.mita_forward.restype = c_int
+    L.mita_forward.argtypes = fwd
+    L.mita_forward_timed.restype = c_int
+    L.mita_forward_timed.argtypes = fwd + [ctypes.POINTER(vp)]
+    L.mita_num_stages.restype = c_int
+    L.mita_stage_name.restype = ctypes.c_char_p
+    L.mita_stage_name.argtypes = [c_int]
+    L.mita_events_create.restype = c_int
+    L.mita_events_create.argtypes = [ctypes.POINTER(vp), c_int]
+    L.mita_events_destroy.restype = c_int
+    L.mita_events_destroy.argtypes = [ctypes.POINTER(vp), c_int]
+    L.mita_events_elapsed.restype = c_int
+    L.mita_events_elapsed.argtypes = [ctypes.POINTER(vp), c_int, ctypes.POINTER(ctypes.c_float)]
+    L.mita_status_str.restype = ctypes.c_char_p
+    L.mita_status_str.argtypes = [c_int]
+    L.mita_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(code: int):
+    if code != 0:
+        raise MitaError(code, lib().mita_status_str(code).decode())
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return BF16
+    if t == torch.float32:
+        return F32
+    raise MitaError(4, f"unsupported dtype {t}")
+
+
+def workspace_bytes(dtype: torch.dtype, B: int, H: int, N: int, d: int, pool, k: int, s: int) -> int:
+    gh, gw, lh, lw = pool
+    return int(lib().mita_workspace_bytes(_dtype_code(dtype), B, H, N, d, Pool(gh, gw, lh, lw),
+                                          lh * lw, k, s))
+
+
+@dataclass
+class DebugOut:
+    topk: torch.Tensor    # int32 [B, H, m, k]
+    route: torch.Tensor   # int32 [B, H, N, s]
+    vtilde: torch.Tensor  # float32 [B, H, m, d]
+    qtilde: torch.Tensor  # dtype [B, H, m, d]
+
+
+class Events:
+    """Per-stage HIP event pairs for mita_forward_timed."""
+
+    def __init__(self):
+        self.n = lib().mita_num_stages()
+        self.arr = (ctypes.c_void_p * (2 * self.n))()
+        _check(lib().mita_events_create(self.arr, 2 * self.n))
+        self.names = [lib().mita_stage_name(i).decode() for i in range(self.n)]
+
+    def elapsed_ms(self) -> dict:
+        ms = (ctypes.c_float * self.n)()
+        _check(lib().mita_events_elapsed(self.arr, self.n, ms))
+        return {self.names[i]: float(ms[i]) for i in range(self.n)}
+
+    def close(self):
+        if self.arr is not None:
+            lib().mita_events_destroy(self.arr, 2 * self.n)
+            self.arr = None
+
+
+def forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, pool, k: int, s: int,
+            debug: bool = False, workspace: torch.Tensor | None = None,
+            out: torch.Tensor | None = None, events: Events | None = None, m: int | None = None):
+    """MiTA forward pass on the GPU.
+
+    Q, K, V: contiguous device tensors [B, H, N, d] (bf16 or fp32).
+    pool: (grid_h, grid_w, land_h, land_w); m = land_h * land_w unless given
+    (a mismatching m is passed through so the library can reject it).
+    Returns O, or (O, DebugOut) when ``debug``.
+    """
+    L = lib()
+    B, H, N, d = Q.shape
+    gh, gw, lh, lw = pool
+    m = lh * lw if m is None else m
+    dt = _dtype_code(Q.dtype)
+    for t in (Q, K, V):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != Q.dtype or t.shape != Q.shape:
+            raise MitaError(2, "Q, K, V must be contiguous device tensors of one shape and dtype")
+    P = Pool(gh, gw, lh, lw)
+    need = int(L.mita_workspace_bytes(dt, B, H, N, d, P, m, k, s))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=Q.device)
+    O = torch.empty_like(Q) if out is None else out
+    dbg_struct, dbg = None, None
+    if debug:
+        dev = Q.device
+        dbg = DebugOut(
+            topk=torch.empty((B, H, m, k), dtype=torch.int32, device=dev),
+            route=torch.empty((B, H, N, s), dtype=torch.int32, device=dev),
+            vtilde=torch.empty((B, H, m, d), dtype=torch.float32, device=dev),
+            qtilde=torch.empty((B, H, m, d), dtype=Q.dtype, device=dev),
+        )
+        dbg_struct = Debug(dbg.topk.data_ptr(), dbg.route.data_ptr(), dbg.vtilde.data_ptr(),
+                           dbg.qtilde.data_ptr())
+    stream = torch.cuda.current_stream(Q.device).cuda_stream
+    args = (Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), dt, B, H, N, d, P, m, k, s,
+            ctypes.byref(dbg_struct) if dbg_struct is not None else None,
+            workspace.data_ptr(), workspace.numel(), stream)
+    if events is None:
+        code = L.mita_forward(*args)
+    else:
+        code = L.mita_forward_timed(*args, events.arr)
+    _check(code)
+    return (O, dbg) if debug else O

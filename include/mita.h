@@ -1,0 +1,133 @@
+/*
+ * mita.h - C ABI of the MI355X (gfx950) MiTA forward-pass library (libmita.so).
+ *
+ * MiTA (Mixture-of-Top-k Attention; Wen et al., arXiv 2602.01219 v6) replaces
+ * each query's scan over N keys by m + s*k entries.  Per (b, h) head the
+ * forward pass computes, as the MiTA tutorial (iwxt.cn/tutorials/mita-attention)
+ * restates paper section 3.2, eqs. 5-12, in its chapter 4:
+ *
+ *   1. Q~ [m, d]: average pooling of Q over m windows of the token grid;
+ *   2. landmark scores s~_ij = q~_i . k_j / sqrt(d) over all N keys;
+ *   3. routed expert i = the top-k keys of row i (indices I [m, k]);
+ *   4. shared values v~_i = sum_j softmax_j(s~_ij) v_j over all N keys;
+ *   5. route every query to the s landmarks with the largest q . q~_i;
+ *   6. one softmax over [q~_1..q~_m, the s*k routed keys] with values
+ *      [v~_1..v~_m, the routed values]; o = V* softmax(K* q / sqrt(d)).
+ *
+ * Conventions fixed where the pages leave them open:
+ *   - Q~ is the exact window mean rounded once (nearest, ties to even) to the
+ *     input dtype; windows are adaptive, half-open
+ *     [floor(i*G/P), ceil((i+1)*G/P)) per grid axis.
+ *   - tokens n = row*grid_w + col and landmarks i = row*land_w + col
+ *     (row-major, as the tutorial's 2x4 grid example in chapter 5);
+ *   - top-k and top-s ties go to the lowest index; I rows are returned in
+ *     ascending key index, routes by score descending then landmark index;
+ *   - every logit is scaled by 1/sqrt(d); the routing score is the unscaled
+ *     q . q~ (same order);
+ *   - non-causal: every query sees all m shared entries.
+ *
+ * Threading and ownership: the caller owns every buffer (inputs, outputs,
+ * debug outputs and the workspace).  The library allocates no device memory
+ * and keeps no state between calls; mita_forward only validates arguments and
+ * enqueues kernels on the caller's HIP stream, then returns without
+ * synchronising.  Buffers must stay valid until the stream reaches that point.
+ * Calls on different streams must use different workspaces.
+ *
+ * Errors: every argument is validated before anything is enqueued; on an
+ * error nothing is launched and no output is written.  Nothing is thrown
+ * across the ABI.
+ */
+#ifndef MITA_H
+#define MITA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MITA_OK = 0,
+  MITA_ERR_NULL = 1,        /* a required pointer is NULL */
+  MITA_ERR_SHAPE = 2,       /* B,H,N,d <= 0; N != grid_h*grid_w; m != land_h*land_w;
+                               landmark grid larger than the token grid */
+  MITA_ERR_PARAM = 3,       /* k not in [1, N]; s not in [1, m]; pointer not 16-byte aligned */
+  MITA_ERR_UNSUPPORTED = 4, /* d not in {32, 64}; unknown dtype; s > 8; m > 4096;
+                               N > 2^26; k > 2048 when N > 8192 */
+  MITA_ERR_WORKSPACE = 5,   /* workspace smaller than mita_workspace_bytes() */
+  MITA_ERR_HIP = 6          /* the HIP runtime reported an error while enqueueing */
+} mita_status;
+
+typedef enum { MITA_F32 = 0, MITA_BF16 = 1 } mita_dtype;
+
+/* Pooling grid: N = grid_h * grid_w tokens, m = land_h * land_w landmarks.
+ * A 1-D sequence uses grid_h = land_h = 1. */
+typedef struct {
+  int grid_h, grid_w, land_h, land_w;
+} mita_pool;
+
+/* Optional debug outputs (each may be NULL; the struct pointer may be NULL).
+ *   topk   int32 [B, H, m, k]  routed-expert key indices, ascending per row
+ *   route  int32 [B, H, N, s]  chosen landmarks, score descending then index
+ *   vtilde float [B, H, m, d]  shared values v~ in float32
+ *   qtilde dtype [B, H, m, d]  landmark queries q~ in the input dtype
+ * They are filled by device-to-device copies enqueued on the same stream. */
+typedef struct {
+  int32_t* topk;
+  int32_t* route;
+  float* vtilde;
+  void* qtilde;
+} mita_debug;
+
+/* Bytes of device workspace mita_forward needs for these arguments (0 if the
+ * arguments are invalid).  Host-only; no HIP call. */
+size_t mita_workspace_bytes(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool,
+                            int m, int k, int s);
+
+/* The MiTA forward pass (steps 1-6 above) for B*H independent heads.
+ *   Q, K, V   device, dtype, contiguous [B, H, N, d] (d innermost), read only
+ *   O         device, dtype, contiguous [B, H, N, d], written
+ *   dbg       optional debug outputs (see mita_debug), or NULL
+ *   workspace device buffer of at least mita_workspace_bytes(...) bytes,
+ *             16-byte aligned, owned by the caller; contents need not be
+ *             initialised and are overwritten
+ *   stream    a hipStream_t (NULL = the default stream)
+ * Returns MITA_OK once all work is enqueued. */
+mita_status mita_forward(const void* Q, const void* K, const void* V, void* O, mita_dtype dtype,
+                         int B, int H, int N, int d, mita_pool pool, int m, int k, int s,
+                         const mita_debug* dbg, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Profiling variant: identical work, and additionally records a pair of HIP
+ * events around each stage on `stream`.  `events` holds 2 * mita_num_stages()
+ * hipEvent_t handles made by mita_events_create (start, stop per stage).
+ * Read the stage times with mita_events_elapsed after the stream finished. */
+mita_status mita_forward_timed(const void* Q, const void* K, const void* V, void* O,
+                               mita_dtype dtype, int B, int H, int N, int d, mita_pool pool,
+                               int m, int k, int s, const mita_debug* dbg, void* workspace,
+                               size_t workspace_bytes, void* stream, void* const* events);
+
+/* Number of timed stages and their names ("pool", "estimate", "score", ...). */
+int mita_num_stages(void);
+const char* mita_stage_name(int stage);
+
+/* Create / destroy `count` HIP events with timing enabled (the handles are
+ * written to events[0..count)).  mita_events_elapsed fills ms[i] with the time
+ * between events[2i] and events[2i+1] for i < n_pairs, blocking until they
+ * complete; a stage that launched nothing reports 0. */
+mita_status mita_events_create(void** events, int count);
+mita_status mita_events_destroy(void** events, int count);
+mita_status mita_events_elapsed(void* const* events, int n_pairs, float* ms);
+
+/* Human-readable text for a status code (static storage). */
+const char* mita_status_str(mita_status status);
+
+/* Library version string. */
+const char* mita_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MITA_H */

@@ -1,0 +1,90 @@
+"""The C-ABI library loads, exports every symbol include/mita.h declares, and
+rejects invalid arguments before touching the GPU.
+
+These run on the CPU: every mita_forward call below is invalid in some way,
+and validation happens before any HIP call, so no kernel is launched and no
+pointer is dereferenced (the device pointers are placeholders).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from efficient_long_sequence_amd import mita
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+A = 0x10000  # 16-byte aligned placeholder address, never dereferenced
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "mita.h")).read()
+    return sorted(set(re.findall(r"\b(mita_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = mita.lib()
+    names = _declared()
+    assert set(names) == set(mita.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.mita_version().startswith(b"mita-gfx950")
+
+
+def _fwd(**kw):
+    a = dict(Q=A, K=A, V=A, O=A, dt=mita.BF16, B=1, H=2, N=4096, d=64, pool=(1, 4096, 1, 64), m=64,
+             k=64, s=1, ws=A, wsb=1 << 40)
+    a.update(kw)
+    P = mita.Pool(*a["pool"])
+    return mita.lib().mita_forward(a["Q"], a["K"], a["V"], a["O"], a["dt"], a["B"], a["H"], a["N"], a["d"], P,
+                                   a["m"], a["k"], a["s"], None, a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=0), 1), (dict(O=0), 1), (dict(ws=0), 1),
+    (dict(B=0), 2), (dict(N=4095), 2), (dict(m=63), 2), (dict(pool=(1, 4096, 2, 32)), 2),
+    (dict(pool=(2, 2048, 1, 64), N=4096), 0),  # valid shape: checked separately below
+    (dict(d=0), 2),
+    (dict(k=0), 3), (dict(k=4097), 3), (dict(s=0), 3), (dict(s=65), 3), (dict(K=A + 8), 3),
+    (dict(ws=A + 4), 3),
+    (dict(d=48), 4), (dict(dt=7), 4), (dict(s=9, m=64), 4),
+    (dict(N=1 << 20, pool=(1, 1 << 20, 1, 64), k=4096), 4),
+    (dict(m=4097 * 1, pool=(1, 8192, 1, 4097), N=8192), 4),
+    (dict(wsb=100), 5),
+])
+def test_invalid_arguments_are_rejected(kw, code):
+    if code == 0:
+        # a valid pooling grid with an undersized workspace is reported as such
+        kw = dict(kw, wsb=16)
+        code = 5
+    assert _fwd(**kw) == code
+
+
+def test_workspace_bytes():
+    L = mita.lib()
+    P = mita.Pool(1, 1 << 20, 1, 512)
+    big = L.mita_workspace_bytes(mita.BF16, 1, 2, 1 << 20, 64, P, 512, 512, 1)
+    assert 50 << 20 < big < 1 << 30
+    assert L.mita_workspace_bytes(mita.BF16, 1, 2, 1 << 20, 64, P, 511, 512, 1) == 0
+    assert L.mita_workspace_bytes(mita.F32, 1, 1, 256, 32, mita.Pool(16, 16, 4, 4), 16, 16, 1) > 0
+    s2 = L.mita_workspace_bytes(mita.BF16, 4, 2, 65536, 64, mita.Pool(1, 65536, 1, 128), 128, 128, 2)
+    s1 = L.mita_workspace_bytes(mita.BF16, 4, 2, 65536, 64, mita.Pool(1, 65536, 1, 128), 128, 128, 1)
+    assert s2 > s1
+
+
+def test_status_strings_and_stages():
+    L = mita.lib()
+    for c in range(7):
+        assert L.mita_status_str(c)
+    n = L.mita_num_stages()
+    names = [L.mita_stage_name(i).decode() for i in range(n)]
+    assert names[0] == "pool" and "attend" in names and "score" in names
+    assert L.mita_stage_name(99) == b"?"
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(mita, "_lib", None)
+    monkeypatch.setattr(mita, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        mita.lib()

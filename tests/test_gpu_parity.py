@@ -1,0 +1,145 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every workload of the workload table runs in the launch configuration the
+benchmark uses; heads, landmark rows and queries are sampled where the oracle
+would take too long, always including full rows of v~ for the joint softmax.
+Edge cases cover ragged tiles, both dtypes and head dims, s > 1, k = N,
+one-token windows, exact ties, the sampled-threshold (large N) selection and
+both of its fallback triggers.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from efficient_long_sequence_amd import synth
+from efficient_long_sequence_amd.configs import WORKLOADS
+from tests import gpu_harness as gh_
+from oracle import mita_oracle as mo
+
+pytestmark = pytest.mark.gpu
+
+
+def _pool(w):
+    return (w.grid_h, w.grid_w, w.land_h, w.land_w)
+
+
+def _inputs(B, H, N, d, kind, n_clusters, dtype, seed):
+    return synth.make(B, H, N, d, kind, n_clusters, dtype, seed)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+# ---------------------------------------------------------------------------
+# the workload table
+# ---------------------------------------------------------------------------
+HEAD_SAMPLE = {"tiny_n256_f32": None, "deit_s_n196": [(0, 0), (17, 3), (63, 5)],
+               "ade_n1024": [(0, 0), (7, 5)], "ade_n1600": [(3, 2), (7, 5)],
+               "long_n64k_s1": [(1, 1)], "long_n64k_s2": [(2, 0)], "long_n256k": [(0, 1)],
+               "long_n1m": [(0, 0)]}
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_parity(name):
+    w = WORKLOADS[name]
+    Q, K, V = synth.make_from_workload(w)
+    queries = rows = None
+    if w.N >= 200000:
+        queries = np.sort(np.random.default_rng(0).choice(w.N, size=4096, replace=False))
+    if w.N >= 1000000:
+        rows = np.sort(np.random.default_rng(1).choice(w.m, size=48, replace=False))
+    gh_.run_and_check(Q, K, V, _pool(w), w.k, w.s, w.dtype, heads=HEAD_SAMPLE[name], queries=queries,
+                      rows=rows, label=name)
+
+
+# ---------------------------------------------------------------------------
+# edge cases at sizes the oracle checks in full
+# ---------------------------------------------------------------------------
+EDGE = {
+    # label: (B, H, grid_h, grid_w, d, land_h, land_w, k, s, kind, clusters, dtype)
+    "ragged_2d": (2, 3, 25, 40, 64, 3, 7, 37, 1, "clustered", 16, "bf16"),
+    "d32_s3": (1, 2, 1, 777, 32, 1, 13, 50, 3, "clustered", 8, "bf16"),
+    "f32_d64_s2": (2, 1, 12, 20, 64, 4, 5, 20, 2, "iid", 0, "f32"),
+    "f32_d32_ragged": (1, 3, 7, 9, 32, 2, 3, 11, 1, "clustered", 4, "f32"),
+    "k_equals_n": (1, 2, 1, 96, 64, 1, 1, 96, 1, "iid", 0, "bf16"),
+    "k_equals_n_m4": (1, 1, 8, 12, 64, 2, 2, 96, 2, "clustered", 4, "bf16"),
+    "one_token_windows": (1, 2, 8, 8, 64, 8, 8, 8, 1, "clustered", 8, "bf16"),
+    "s_equals_m": (1, 1, 4, 16, 64, 2, 2, 5, 4, "iid", 0, "bf16"),
+    "k1_s1": (3, 1, 10, 10, 64, 5, 5, 1, 1, "clustered", 16, "bf16"),
+    "few_clusters_uneven": (1, 2, 1, 3000, 64, 1, 30, 40, 1, "clustered", 2, "bf16"),
+    "large_m": (1, 1, 1, 12000, 64, 1, 600, 24, 2, "runs", 32, "bf16"),
+    "dense_limit_8192": (1, 1, 64, 128, 64, 8, 8, 100, 1, "clustered", 16, "bf16"),
+}
+
+
+@pytest.mark.parametrize("label", list(EDGE))
+def test_edge_parity(label):
+    B, H, gh, gw, d, lh, lw, k, s, kind, nc, dtype = EDGE[label]
+    Q, K, V = _inputs(B, H, gh * gw, d, kind, nc, dtype, seed=zlib.crc32(label.encode()) % 1000)
+    gh_.run_and_check(Q, K, V, (gh, gw, lh, lw), k, s, dtype, label=label)
+
+
+def test_closed_form_matches_dense_attention():
+    """m = 1, k = N: O equals dense softmax attention over keys [q~; K] and values [v~; V]."""
+    N, d = 200, 64
+    Q, K, V = _inputs(1, 1, N, d, "iid", 0, "bf16", seed=21)
+    gpu = gh_.run_gpu(Q, K, V, (1, N, 1, 1), N, 1, "bf16")
+    qt = gpu["qtilde"][0, 0]
+    t = lambda a: torch.tensor(np.asarray(a, dtype=np.float64))[None, None]
+    Kh, Vh = K[0, 0].astype(np.float64), V[0, 0].astype(np.float64)
+    vt = torch.nn.functional.scaled_dot_product_attention(t(qt), t(Kh), t(Vh))[0, 0].numpy()
+    np.testing.assert_allclose(gpu["vtilde"][0, 0], vt, atol=2e-2)
+    dense = torch.nn.functional.scaled_dot_product_attention(
+        t(Q[0, 0]), t(np.concatenate([qt, Kh])), t(np.concatenate([vt, Vh])))[0, 0].numpy()
+    err = np.abs(gpu["O"][0, 0] - dense)
+    assert err.max() < 2e-2 and err.mean() < 2e-3
+
+
+def test_exact_ties_go_to_lowest_index_dense():
+    N, d, k = 300, 64, 17
+    Q, _, V = _inputs(1, 2, N, d, "iid", 0, "bf16", seed=5)
+    K = np.broadcast_to(Q[:, :, :1], Q.shape).copy()  # every key equal: all scores tie
+    gpu = gh_.run_gpu(Q, K, V, (1, N, 1, 6), k, 2, "bf16")
+    np.testing.assert_array_equal(gpu["topk"], np.broadcast_to(np.arange(k), gpu["topk"].shape))
+    np.testing.assert_allclose(gpu["vtilde"], np.broadcast_to(V.astype(np.float64).mean(axis=2, keepdims=True),
+                                                              gpu["vtilde"].shape), atol=2e-2)
+
+
+# ---------------------------------------------------------------------------
+# large-N selection: sampled threshold, and both fallback triggers
+# ---------------------------------------------------------------------------
+def test_sparse_threshold_path():
+    Q, K, V = _inputs(1, 2, 20000, 64, "runs", 64, "bf16", seed=31)
+    gh_.run_and_check(Q, K, V, (1, 20000, 1, 40), 64, 2, "bf16", label="sparse_threshold")
+
+
+def test_sparse_forced_fallback(monkeypatch):
+    """Host-forced: every candidate threshold +inf, every row selected by the exact fallback kernel."""
+    monkeypatch.setenv("MITA_TEST_FORCE_FALLBACK", "1")
+    Q, K, V = _inputs(1, 2, 12000, 64, "runs", 16, "bf16", seed=32)
+    gh_.run_and_check(Q, K, V, (1, 12000, 1, 24), 100, 1, "bf16", label="forced_fallback")
+
+
+def test_sparse_overflow_fallback_with_ties():
+    """All 16384 keys tie: every row has more candidates than capacity and falls back;
+    the exact result is the k lowest indices."""
+    N, d, k = 16384, 64, 33
+    Q, _, V = _inputs(1, 1, N, d, "iid", 0, "bf16", seed=33)
+    K = np.broadcast_to(Q[:, :, 5:6], Q.shape).copy()
+    gpu = gh_.run_gpu(Q, K, V, (1, N, 1, 16), k, 1, "bf16")
+    np.testing.assert_array_equal(gpu["topk"], np.broadcast_to(np.arange(k), gpu["topk"].shape))
+    gh_.run_and_check(Q, K, V, (1, N, 1, 16), k, 1, "bf16", queries=np.arange(0, N, 7), label="overflow")
+
+
+def test_deterministic():
+    w = WORKLOADS["ade_n1024"]
+    Q, K, V = synth.make_from_workload(w)
+    a = gh_.run_gpu(Q, K, V, _pool(w), w.k, w.s, w.dtype)
+    b = gh_.run_gpu(Q, K, V, _pool(w), w.k, w.s, w.dtype)
+    for key in ("O", "topk", "route", "vtilde", "qtilde"):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
