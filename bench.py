@@ -1,0 +1,244 @@
+"""Benchmark of the MiTA forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one full mita_forward call (pool, landmark scoring with shared
+values and top-k, routing, bucketing, joint-softmax attention) over one batch
+of synthetic inputs already resident in HBM.  The headline workload is the
+N = 1M long sequence (B=1, H=2, d=64, m=k=512, s=1); the N = 64K and 256K
+shapes are timed the same way and reported beside it.  Prints one JSON line.
+
+The roofline of the dominant kernel uses the per-stage durations measured
+with HIP events on the launch stream during the timed steps; its HBM traffic
+comes from committed rocprofv3 counter summaries (profiles/) when they were
+taken on the current kernel sources, else null.  The CPU baseline times the
+fp64 oracle on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from efficient_long_sequence_amd.configs import HEADLINE, LONG, WORKLOADS  # noqa: E402
+
+METRIC = "MiTA fwd tokens/s (B·H·N) at N=64K/256K/1M; % of HBM and MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = {
+    "attend": ["attend.hip", "tile.h", "mita_dev.h"],
+    "score": ["score.hip", "tile.h", "mita_dev.h"],
+}
+
+
+def sources_sha(stage: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(stage, []):
+        with open(os.path.join(ROOT, "efficient_long_sequence_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(w, stage: str):
+    """Algorithmic flops and HBM bytes of one launch of a stage's kernel(s).
+
+    attend: per query, m + s*k logits and value sums of length d
+            (4 d (m + s k) flops); reads Q, the m*k gathered K and V rows,
+            Q~ and V~ (bf16), the expert index lists and the permutation,
+            writes O.
+    score:  per landmark row and key, one logit and one value sum
+            (4 d N m flops); reads K and V once, writes the v~ partials.
+    """
+    es = 2 if w.dtype == "bf16" else 4
+    BH, N, d, m, k, s = w.B * w.H, w.N, w.d, w.m, w.k, w.s
+    if stage == "attend":
+        flops = 4.0 * d * N * (m + s * k) * BH
+        byts = BH * (2 * N * d * es + 2 * m * k * d * es + 2 * m * d * es + m * k * 4 + s * N * 4)
+    elif stage == "score":
+        flops = 4.0 * d * N * m * BH
+        chunks = 1  # partial records are small next to K and V
+        byts = BH * (2 * N * d * es + m * d * es + m * chunks * (d + 4) * 4)
+    else:
+        return None, None
+    return flops, float(byts)
+
+
+def make_device_inputs(w):
+    import torch
+    from efficient_long_sequence_amd import synth
+    Q, K, V = synth.make_from_workload(w)
+    out = []
+    for x in (Q, K, V):
+        if w.dtype == "bf16":
+            bits = synth.f32_to_bf16_bits(x)
+            out.append(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda())
+        else:
+            out.append(torch.from_numpy(x).cuda())
+    return (Q, K, V), out
+
+
+def time_workload(w, steps: int, warmup: int):
+    import torch
+    from efficient_long_sequence_amd import mita
+    host, (q, k, v) = make_device_inputs(w)
+    pool = (w.grid_h, w.grid_w, w.land_h, w.land_w)
+    ws = torch.empty(mita.workspace_bytes(q.dtype, w.B, w.H, w.N, w.d, pool, w.k, w.s), dtype=torch.uint8,
+                     device=q.device)
+    out = torch.empty_like(q)
+    for _ in range(warmup):
+        mita.forward(q, k, v, pool, w.k, w.s, workspace=ws, out=out)
+    events = [mita.Events() for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        mita.forward(q, k, v, pool, w.k, w.s, workspace=ws, out=out, events=events[i])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    stages = {}
+    for ev in events:
+        for name, ms in ev.elapsed_ms().items():
+            stages[name] = stages.get(name, 0.0) + ms / steps
+        ev.close()
+    return dict(seconds=dt, ms_per_step=1e3 * dt / steps, tokens_per_s=w.tokens * steps / dt, stages=stages,
+                host=host, q=q, k=k, v=v, pool=pool, ws=ws)
+
+
+def roofline(w, stages: dict):
+    dom = max(("attend", "score"), key=lambda s: stages.get(s, 0.0))
+    flops, byts = algorithmic(w, dom)
+    sec = stages[dom] * 1e-3
+    intensity = flops / byts
+    peak_f = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
+    traffic = measured_traffic(w, dom)
+    if intensity > ridge:
+        r = dict(bound="mfma", achieved=flops / sec / 1e12, peak=peak_f, unit="TFLOP/s")
+    else:
+        r = dict(bound="hbm", achieved=byts / sec / 1e9, peak=PEAK_HBM_GBS, unit="GB/s")
+    r["frac"] = r["achieved"] / r["peak"]
+    r["traffic"] = traffic
+    r.update(kernel=dom, kernel_ms=stages[dom], alg_flops=flops, alg_bytes=byts,
+             hbm_gbs_alg=byts / sec / 1e9, mfma_tflops_alg=flops / sec / 1e12)
+    return r
+
+
+def measured_traffic(w, stage: str):
+    """HBM bytes per launch from the committed counter summary, if it matches
+    this workload and the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ent = rec.get(f"{stage}:{w.name}")
+    if not ent or ent.get("sources_sha") != sources_sha(stage):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, run):
+    """Time the fp64 oracle on a bounded sample of the same workload.
+
+    Sample: head 0.  Pooling runs in full; landmark scoring, top-k and shared
+    values run on 1/16 of the landmark rows; routing and the joint softmax on
+    1/16 of the queries (with the GPU's expert lists and shared values as
+    inputs, which the oracle's cost does not depend on).  Each part's time is
+    scaled by its sampling factor and summed over the B*H heads.
+    """
+    import torch
+    from oracle import mita_oracle as mo
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    from efficient_long_sequence_amd import mita
+    Q, K, V = (x[0, 0].astype(np.float64) for x in run["host"])
+    _, dbg = mita.forward(run["q"], run["k"], run["v"], run["pool"], w.k, w.s, debug=True)
+    torch.cuda.synchronize()
+    I_gpu = dbg.topk[0, 0].cpu().numpy().astype(np.int64)
+    Vt_gpu = dbg.vtilde[0, 0].cpu().numpy().astype(np.float64)
+    fr, fq = 16, 16
+    t0 = time.perf_counter()
+    Qt = mo.landmarks(Q, w.grid_h, w.grid_w, w.land_h, w.land_w, w.dtype)
+    t_pool = time.perf_counter() - t0
+    rows = np.arange(0, w.m, fr)
+    t0 = time.perf_counter()
+    for r0 in range(0, rows.size, 32):
+        rr = rows[r0:r0 + 32]
+        S = mo.landmark_scores(Qt, K, rows=rr)
+        mo.topk(S, w.k)
+        mo.shared_values(S, V)
+        del S
+    t_rows = time.perf_counter() - t0
+    qs = np.arange(0, w.N, fq)
+    t0 = time.perf_counter()
+    e, R, _ = mo.route(Q[qs], Qt, w.s)
+    mo.attend(Q[qs], K, V, Qt, Vt_gpu, I_gpu, e, R=R)
+    t_query = time.perf_counter() - t0
+    est_head = t_pool + t_rows * (w.m / rows.size) + t_query * (w.N / qs.size)
+    measured = t_pool + t_rows + t_query
+    est_total = est_head * w.B * w.H
+    return dict(value=w.tokens / est_total, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=(f"{w.name} head 0: pooling in full, scoring/top-k/shared values on "
+                        f"{rows.size}/{w.m} landmark rows, routing and joint softmax on "
+                        f"{qs.size}/{w.N} queries; {measured:.1f}s measured, scaled to "
+                        f"{est_total:.1f}s for all {w.B * w.H} heads"))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=HEADLINE, choices=list(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", action="store_true", help="time only --workload")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(every head is independent: a multi-GPU run would shard heads with no communication)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    w = WORKLOADS[args.workload]
+    run = time_workload(w, args.steps, args.warmup)
+    others = []
+    if not args.only:
+        for name in LONG:
+            if name == w.name:
+                continue
+            wo = WORKLOADS[name]
+            r = time_workload(wo, args.steps, args.warmup)
+            others.append(dict(workload=name, tokens_per_s=r["tokens_per_s"], ms_per_step=r["ms_per_step"],
+                               stages_ms=r["stages"], roofline=roofline(wo, r["stages"])))
+            del r
+            torch.cuda.empty_cache()
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, run)
+    line = dict(
+        metric=METRIC, value=run["tokens_per_s"], unit="tokens/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=run["ms_per_step"], higher_is_better=True, scaling="weak",
+        vs_baseline=None, dtype=w.dtype, data="synthetic",
+        config=dict(workload=w.name, B=w.B, H=w.H, N=w.N, d=w.d, m=w.m, k=w.k, s=w.s,
+                    pool=f"{w.grid_h}x{w.grid_w} tokens -> {w.land_h}x{w.land_w} landmarks",
+                    values=f"{w.kind}, {w.n_clusters} clusters, seed {w.seed}"),
+        roofline=roofline(w, run["stages"]), cpu_baseline=cpu, stages_ms=run["stages"],
+        other_workloads=others,
+    )
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -61,7 +61,8 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
   p.sc_R = p.sc_nw * 16 * p.sc_ib;
   p.sc_rt = ceil_div(m, p.sc_R);
   // key chunks: aim for about two workgroups per compute unit
-  const long long target = 512;
+  // (512-row tiles run one workgroup per compute unit, smaller ones two)
+  const long long target = p.sc_R >= 512 ? 256 : 512;
   int C = ceil_div(target, (long long)p.BH * p.sc_rt);
   C = C < 1 ? 1 : C;
   const int max_c = ceil_div(N, 32);
@@ -75,7 +76,7 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
   p.dense = N <= NSMALL ? 1 : 0;
   p.capg = p.dense ? N : CAPG;
   if (!p.dense) {
-    p.sigma = k / 16 > 1 ? k / 16 : 1;
+    p.sigma = k / 32 > 1 ? k / 32 : 1;
     p.NS = N / p.sigma;
     p.G = p.NS < 512 ? p.NS : 512;
     const double lam = (double)k / p.sigma;
@@ -84,10 +85,10 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
     const long long est_target = 512;
     int gpb = ceil_div((long long)p.G * p.BH * p.sc_rt, est_target);
     p.est_gpb = gpb < 1 ? 1 : gpb;
-    // staged candidates per workgroup: about three times k survivors per row
-    const double expect = (double)p.sc_R * p.L * (3.0 * k / N);
+    // staged candidates per workgroup: the threshold admits about 2.5 k keys per row
+    const double expect = (double)p.sc_R * p.L * (2.5 * k / N);
     int cb = 256;
-    while (cb < 2.0 * expect && cb < 8192) cb <<= 1;
+    while (cb < 1.5 * expect && cb < 8192) cb <<= 1;
     p.cb = cb;
     // Test hook (host-forced): MITA_TEST_FORCE_FALLBACK=1 sets every candidate
     // threshold to +inf, so no row collects candidates and every row is

@@ -96,17 +96,18 @@ __global__ __launch_bounds__(NW * 64) void k_attend(
     f.load_keys(cur, li, lg);
     f.load_vals(cur + TL::K_ELEMS, li, lg);
     const int nv = min(32, ne - x0);
+    float sc[IB][8];
 #pragma unroll
-    for (int b = 0; b < IB; ++b) {
-      float sc[8];
-      step_scores(f, qf[b], sc);
-      if (nv < 32) {
+    for (int b = 0; b < IB; ++b) step_scores(f, qf[b], sc[b]);
+    if (nv < 32) {
+#pragma unroll
+      for (int b = 0; b < IB; ++b)
 #pragma unroll
         for (int t = 0; t < 8; ++t)
-          if (slot_key(t, lg) >= nv) sc[t] = -INFINITY;
-      }
-      softmax_step(f, sc, max8(sc), cscale, M[b], Z[b], acc[b]);
+          if (slot_key(t, lg) >= nv) sc[b][t] = -INFINITY;
     }
+#pragma unroll
+    for (int b = 0; b < IB; ++b) softmax_step(f, sc[b], max8(sc[b]), cscale, M[b], Z[b], acc[b]);
     if (more) ld.store(nxt, nxt + TL::K_ELEMS);
     __syncthreads();
   }

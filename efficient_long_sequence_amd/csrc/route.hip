@@ -16,7 +16,8 @@
 //             items, per slot.
 //   k_scatter writes each query into its expert's bucket (order inside a
 //             bucket is immaterial: every query's output depends only on its
-//             own row).
+//             own row); per-workgroup LDS counts, one global reservation per
+//             expert present in the workgroup.
 #include "mita_dev.h"
 #include "mita_plan.h"
 #include "tile.h"
@@ -188,17 +189,30 @@ __global__ __launch_bounds__(1024) void k_scan(const int* __restrict__ counts, i
   }
 }
 
+// Each workgroup counts its 256 queries per expert in LDS, reserves one
+// contiguous range per expert with a single global atomic, and writes the
+// queries there (queries that share an expert in a block cost one atomic).
 __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ route, const int* __restrict__ gpre,
                                                  int* __restrict__ cursor, int32_t* __restrict__ perm, int N,
                                                  int m, int s, int BH) {
+  extern __shared__ int s_cnt[];  // [m] counts, then [m] bases
+  int* s_base = s_cnt + m;
   const int bh = blockIdx.y;
   const int n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= N) return;
   for (int t = 0; t < s; ++t) {
-    const int e = route[((size_t)bh * N + n) * s + t];
-    const size_t x = ((size_t)t * BH + bh) * m + e;
-    const int pos = gpre[x] + atomicAdd(cursor + x, 1);
-    perm[(size_t)t * BH * N + pos] = n;
+    for (int x = threadIdx.x; x < m; x += 256) s_cnt[x] = 0;
+    __syncthreads();
+    const int e = n < N ? route[((size_t)bh * N + n) * s + t] : -1;
+    const int r = e >= 0 ? atomicAdd(s_cnt + e, 1) : 0;
+    __syncthreads();
+    const size_t xb = ((size_t)t * BH + bh) * m;
+    for (int x = threadIdx.x; x < m; x += 256) {
+      const int c = s_cnt[x];
+      if (c) s_base[x] = gpre[xb + x] + atomicAdd(cursor + xb + x, c);
+    }
+    __syncthreads();
+    if (e >= 0) perm[(size_t)t * BH * N + s_base[e] + r] = n;
+    __syncthreads();
   }
 }
 
@@ -236,8 +250,8 @@ void launch_bucket(const Plan& p) {
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, p.stream, p.counts, p.gpre, p.wl, p.wl_count, E, p.m, p.s,
                      p.T, p.UB);
   dim3 grid((unsigned)((p.N + 255) / 256), (unsigned)p.BH);
-  hipLaunchKernelGGL(k_scatter, grid, dim3(256), 0, p.stream, p.route, p.gpre, p.cursor, p.perm, p.N, p.m, p.s,
-                     p.BH);
+  hipLaunchKernelGGL(k_scatter, grid, dim3(256), (size_t)2 * p.m * sizeof(int), p.stream, p.route, p.gpre, p.cursor,
+                     p.perm, p.N, p.m, p.s, p.BH);
 }
 
 }  // namespace mita

@@ -65,18 +65,19 @@ __global__ __launch_bounds__(NW * 64) void k_est(const T* __restrict__ K, const 
     }
   }
   TileLoader<T, D, NT, false> ld;
+  // Group g holds the samples t = u * G + g, u < Sg: its keys are spread over
+  // the whole sequence, so runs of similar keys do not pile into one group.
   const int Sg = NS / G;
   for (int gl = 0; gl < gpb; ++gl) {
     const int grp = blockIdx.x * gpb + gl;
     if (grp >= G) break;
-    const int t_begin = grp * Sg, t_end = (grp == G - 1) ? NS : t_begin + Sg;
     float run[IB];
 #pragma unroll
     for (int b = 0; b < IB; ++b) run[b] = -INFINITY;
-    for (int t0 = t_begin; t0 < t_end; t0 += 32) {
+    for (int u0 = 0; u0 < Sg; u0 += 32) {
       ld.load([&](int r) -> const T* {
-                const int t = t0 + r;
-                return t < t_end ? Kh + (size_t)sample_pos(t, sigma) * D : nullptr;
+                const int u = u0 + r;
+                return u < Sg ? Kh + (size_t)sample_pos(u * G + grp, sigma) * D : nullptr;
               },
               [](int) -> const T* { return nullptr; });
       __syncthreads();
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(NW * 64) void k_est(const T* __restrict__ K, const 
       __syncthreads();
       StepFrags<T, D> f;
       f.load_keys(ks, li, lg);
-      const int nv = min(32, t_end - t0);
+      const int nv = min(32, Sg - u0);
 #pragma unroll
       for (int b = 0; b < IB; ++b) {
         float sc[8];
@@ -127,7 +128,7 @@ __global__ __launch_bounds__(256) void k_tau(const float* __restrict__ gmax, flo
 // ---------------------------------------------------------------------------
 // fused scores, partial shared values and candidates
 // ---------------------------------------------------------------------------
-template <typename T, int D, int NW, int IB>
+template <typename T, int D, int NW, int IB, bool DENSE>
 __global__ __launch_bounds__(NW * 64) void k_score(
     const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ Qt,
     const float* __restrict__ tau_in, const float* __restrict__ mhat_in, float* __restrict__ vpart,
@@ -144,7 +145,6 @@ __global__ __launch_bounds__(NW * 64) void k_score(
   int* s_rowbase = s_rowcnt + R;
   int* s_ncand = s_rowbase + R;
 
-  const bool dense = tau_in == nullptr;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, li = lane % 16, lg = lane / 16;
   const int ch = blockIdx.x, rt = blockIdx.y, bh = blockIdx.z;
   const int rbase = rt * R + wave * 16 * IB;
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(NW * 64) void k_score(
   const T* Vh = V + (size_t)bh * N * D;
   const int j_begin = ch * L, j_end = min(N, j_begin + L);
 
-  if (!dense) {
+  if constexpr (!DENSE) {
     for (int r = tid; r < R; r += NT) s_rowcnt[r] = 0;
     if (tid == 0) *s_ncand = 0;
   }
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(NW * 64) void k_score(
       else zero(qf[b][dc]);
     }
     M[b] = (mhat_in != nullptr && valid) ? mhat_in[(size_t)bh * m + row] * cscale : M0;
-    tau[b] = dense ? -INFINITY : (valid ? tau_in[(size_t)bh * m + row] : INFINITY);
+    tau[b] = DENSE ? -INFINITY : (valid ? tau_in[(size_t)bh * m + row] : INFINITY);
     Z[b] = 0.f;
 #pragma unroll
     for (int cb = 0; cb < D / 16; ++cb) acc[b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -198,44 +198,57 @@ __global__ __launch_bounds__(NW * 64) void k_score(
     f.load_keys(cur, li, lg);
     f.load_vals(cur + TL::K_ELEMS, li, lg);
     const int nv = min(32, j_end - j0);
+    // all score tiles of the step first, so the softmax of one row block
+    // overlaps the matrix work of the others
+    float sc[IB][8];
 #pragma unroll
-    for (int b = 0; b < IB; ++b) {
-      float sc[8];
-      step_scores(f, qf[b], sc);
-      if (nv < 32) {
+    for (int b = 0; b < IB; ++b) step_scores(f, qf[b], sc[b]);
+    if (nv < 32) {
+#pragma unroll
+      for (int b = 0; b < IB; ++b)
 #pragma unroll
         for (int t = 0; t < 8; ++t)
-          if (slot_key(t, lg) >= nv) sc[t] = -INFINITY;
-      }
-      const float mx = max8(sc);
+          if (slot_key(t, lg) >= nv) sc[b][t] = -INFINITY;
+    }
+#pragma unroll
+    for (int b = 0; b < IB; ++b) {
+      const float mx = max8(sc[b]);
       const int row = rbase + b * 16 + li;
-      if (dense) {
+      if constexpr (DENSE) {
         if (row < m) {
           uint64_t* dst = cand + ((size_t)bh * m + row) * capg + j0;
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
             const int kl = slot_key(t, lg);
-            if (kl < nv) dst[kl] = ckey(sc[t], (uint32_t)(j0 + kl));
+            if (kl < nv) dst[kl] = ckey(sc[b][t], (uint32_t)(j0 + kl));
           }
         }
       } else if (wave_any(mx >= tau[b])) {
-        if (mx >= tau[b]) {
+        uint32_t msk = 0;
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            if (sc[t] >= tau[b]) {
-              const int jl = j0 + slot_key(t, lg) - j_begin;
-              const int e = atomicAdd(s_ncand, 1);
-              if (e < cb_cap) {
-                s_cand[e] = make_uint2(__float_as_uint(sc[t]), ((uint32_t)(row - rt * R) << 23) | (uint32_t)jl);
-              } else {
-                const int pos = atomicAdd(cand_cnt + (size_t)bh * m + row, 1);
-                if (pos < capg) cand[((size_t)bh * m + row) * capg + pos] = ckey(sc[t], (uint32_t)(j_begin + jl));
-              }
+        for (int t = 0; t < 8; ++t) msk |= (sc[b][t] >= tau[b] ? 1u : 0u) << t;
+        if (msk) {
+          // one LDS reservation per lane for all of its candidates
+          int e = atomicAdd(s_ncand, __builtin_popcount(msk));
+          const uint32_t rl = (uint32_t)(row - rt * R) << 23;
+          while (msk) {
+            const int t = __builtin_ctz(msk);
+            msk &= msk - 1;
+            float v = sc[b][0];
+#pragma unroll
+            for (int u = 1; u < 8; ++u) v = (t == u) ? sc[b][u] : v;
+            const int jl = j0 + slot_key(t, lg) - j_begin;
+            if (e < cb_cap) {
+              s_cand[e] = make_uint2(__float_as_uint(v), rl | (uint32_t)jl);
+            } else {
+              const int pos = atomicAdd(cand_cnt + (size_t)bh * m + row, 1);
+              if (pos < capg) cand[((size_t)bh * m + row) * capg + pos] = ckey(v, (uint32_t)(j_begin + jl));
             }
+            ++e;
           }
         }
       }
-      softmax_step(f, sc, mx, cscale, M[b], Z[b], acc[b]);
+      softmax_step(f, sc[b], mx, cscale, M[b], Z[b], acc[b]);
     }
     if (more) ld.store(nxt, nxt + TL::K_ELEMS);
     __syncthreads();
@@ -255,7 +268,7 @@ __global__ __launch_bounds__(NW * 64) void k_score(
     }
   }
 
-  if (!dense) {
+  if constexpr (!DENSE) {
     const int ns = min(*s_ncand, cb_cap);
     for (int e = tid; e < ns; e += NT) atomicAdd(s_rowcnt + (s_cand[e].y >> 23), 1);
     __syncthreads();
@@ -296,20 +309,41 @@ __global__ __launch_bounds__(256) void k_final(const float* __restrict__ vpart, 
                                                int N, int k, int C, int capg, int dense) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint64_t* a = (uint64_t*)smem;
+  __shared__ float red[256];
+  __shared__ float zred[256 / D];
   const size_t r = blockIdx.x;
   const int tid = threadIdx.x;
-  if (tid < D) {
-    const float* pr = vpart + r * C * (D + 4);
-    float Mx = M0;
-    for (int c = 0; c < C; ++c) Mx = fmaxf(Mx, pr[(size_t)c * (D + 4)]);
-    float Zs = 0.f, s = 0.f;
-    for (int c = 0; c < C; ++c) {
+  constexpr int NG = 256 / D;  // chunk groups
+  const float* pr = vpart + r * C * (D + 4);
+  // largest chunk maximum
+  float mx = M0;
+  for (int c = tid; c < C; c += 256) mx = fmaxf(mx, pr[(size_t)c * (D + 4)]);
+  red[tid] = mx;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
+    __syncthreads();
+  }
+  const float Mx = red[0];
+  __syncthreads();
+  // rescaled sums, chunk groups in parallel (rescaled-sum identity)
+  {
+    const int e = tid % D, cg = tid / D;
+    float zs = 0.f, sv = 0.f;
+    for (int c = cg; c < C; c += NG) {
       const float* q = pr + (size_t)c * (D + 4);
       const float w = __builtin_amdgcn_exp2f(q[0] - Mx);
-      Zs += q[1] * w;
-      s += q[4 + tid] * w;
+      zs += q[1] * w;
+      sv += q[4 + e] * w;
     }
-    const float v = s / Zs;
+    red[tid] = sv;
+    if (e == 0) zred[cg] = zs;
+  }
+  __syncthreads();
+  if (tid < D) {
+    float sv = 0.f, zs = 0.f;
+    for (int g = 0; g < NG; ++g) { sv += red[g * D + tid]; zs += zred[g]; }
+    const float v = sv / zs;
     vt32[r * D + tid] = v;
     vtT[r * D + tid] = from_f32<T>(v);
   }
@@ -401,12 +435,18 @@ static void launch_score_main(const Plan& p) {
   const bool dense = p.dense != 0;
   const size_t lds = 2 * TL::ELEMS * sizeof(T) + (dense ? 0 : (size_t)p.cb * 8 + 2 * R * 4 + 16);
   dim3 grid((unsigned)p.C, (unsigned)p.sc_rt, (unsigned)p.BH);
+  if (dense) {
+    hipLaunchKernelGGL((k_score<T, D, NW, IB, true>), grid, dim3(NW * 64), lds, p.stream, (const T*)p.K,
+                       (const T*)p.V, (const T*)p.qt, nullptr, nullptr, p.vpart, p.cand, p.cand_cnt, p.N, p.m, p.L,
+                       p.C, p.capg, 0, p.cscale);
+    return;
+  }
   if (lds > 65536)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_score<T, D, NW, IB>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_score<T, D, NW, IB, false>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL((k_score<T, D, NW, IB>), grid, dim3(NW * 64), lds, p.stream, (const T*)p.K, (const T*)p.V,
-                     (const T*)p.qt, dense ? nullptr : p.tau, (dense || p.force_fallback) ? nullptr : p.mhat, p.vpart, p.cand,
-                     p.cand_cnt, p.N, p.m, p.L, p.C, p.capg, dense ? 0 : p.cb, p.cscale);
+  hipLaunchKernelGGL((k_score<T, D, NW, IB, false>), grid, dim3(NW * 64), lds, p.stream, (const T*)p.K,
+                     (const T*)p.V, (const T*)p.qt, p.tau, p.force_fallback ? nullptr : p.mhat, p.vpart, p.cand,
+                     p.cand_cnt, p.N, p.m, p.L, p.C, p.capg, p.cb, p.cscale);
 }
 
 template <typename T, int D>
