@@ -20,10 +20,13 @@ OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmita.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "pool.hip", "score.hip", "route.hip", "attend.hip"]
+SOURCES = ["api.cpp", "pool.hip", "score.hip", "route.hip", "attend.hip", "resident.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # finite inputs only (non-finite ones give unspecified results): lets
+    # max/min skip NaN canonicalisation in the softmax inner loops
+    "-fno-honor-nans", "-mno-amdgpu-ieee",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
     "-Wno-unused-variable", "-Wno-unused-local-typedef",
 ]

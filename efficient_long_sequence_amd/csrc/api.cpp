@@ -8,7 +8,7 @@
 #include <cstdlib>
 #include <cstring>
 
-#include "../../include/mita.h"
+#include "mita.h"
 #include "mita_plan.h"
 
 using namespace mita;
@@ -99,12 +99,29 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
 
   // routing and attention tiles
   p.smax = s <= 1 ? 1 : s <= 2 ? 2 : s <= 4 ? 4 : 8;
-  const double avg = (double)N / m;
-  if (p.dtype == 0 || avg <= 16) { p.at_nw = 1; p.at_ib = 1; }
-  else if (avg <= 64) { p.at_nw = 4; p.at_ib = 1; }
-  else if (avg <= 512) { p.at_nw = 4; p.at_ib = 4; }
-  else { p.at_nw = 8; p.at_ib = 4; }
-  p.T = p.at_nw * 16 * p.at_ib;
+  const double avg = (double)N / m;  // queries per expert and slot, on average
+  const size_t hist_bytes = (size_t)s * m <= 4096 ? (size_t)s * m * 4 : 0;
+  p.fast = (resident_bytes(p.dtype, d, m) + hist_bytes <= RES_MAX && resident_bytes(p.dtype, d, k) <= RES_MAX) ? 1 : 0;
+  if (p.fast) {
+    // routing workgroups: about 1024 in all, 512 queries at least
+    long long qpw = ((long long)p.BH * N + 1023) / 1024;
+    qpw = (qpw + 511) / 512 * 512;
+    p.rs_qpw = (int)(qpw < 512 ? 512 : qpw);
+    if (p.dtype == 0 || avg <= 16) { p.ex_nw = 1; p.ex_ib = 1; }
+    else if (avg <= 64) { p.ex_nw = 1; p.ex_ib = 2; }
+    else if (avg <= 256) { p.ex_nw = 4; p.ex_ib = 4; }
+    else { p.ex_nw = 8; p.ex_ib = 4; }
+    const int per = p.ex_nw * 16 * p.ex_ib;
+    int gpw = (int)(avg / per + 0.5);
+    gpw = gpw < 1 ? 1 : gpw > 4 ? 4 : gpw;
+    p.T = per * gpw;
+  } else {
+    if (p.dtype == 0 || avg <= 16) { p.at_nw = 1; p.at_ib = 1; }
+    else if (avg <= 64) { p.at_nw = 4; p.at_ib = 1; }
+    else if (avg <= 512) { p.at_nw = 4; p.at_ib = 4; }
+    else { p.at_nw = 8; p.at_ib = 4; }
+    p.T = p.at_nw * 16 * p.at_ib;
+  }
   p.UB = p.BH * (ceil_div(N, p.T) + m);
 
   // workspace
@@ -136,7 +153,9 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
   p.perm = (int32_t*)take((size_t)s * BH * N * 4);
   p.wl = (WorkItem*)take((size_t)s * p.UB * sizeof(WorkItem));
   p.wl_count = (int*)take(MAX_S * 4);
-  p.part = (float*)take(s > 1 ? (size_t)(s - 1) * BH * N * (d + 4) * 4 : 0);
+  p.part = (float*)take(!p.fast && s > 1 ? (size_t)(s - 1) * BH * N * (d + 4) * 4 : 0);
+  p.plse = (float*)take(p.fast ? BH * N * 4 : 0);
+  p.po = take(p.fast ? BH * N * d * (p.dtype ? 2 : 4) : 0);  // fp16 / fp32
   p.total_bytes = off;
   return p;
 }
@@ -180,13 +199,15 @@ mita_status run(const void* Q, const void* K, const void* V, void* O, mita_dtype
   launch_final(p);
   tm.end(ST_FINAL);
   tm.begin(ST_ROUTE);
-  launch_route(p);
+  if (p.fast) launch_route_shared(p);
+  else launch_route(p);
   tm.end(ST_ROUTE);
   tm.begin(ST_BUCKET);
   launch_bucket(p);
   tm.end(ST_BUCKET);
   tm.begin(ST_ATTEND);
-  launch_attend(p);
+  if (p.fast) launch_expert(p);
+  else launch_attend(p);
   tm.end(ST_ATTEND);
 
   if (dbg) {

@@ -96,18 +96,8 @@ __global__ __launch_bounds__(NW * 64) void k_attend(
     f.load_keys(cur, li, lg);
     f.load_vals(cur + TL::K_ELEMS, li, lg);
     const int nv = min(32, ne - x0);
-    float sc[IB][8];
-#pragma unroll
-    for (int b = 0; b < IB; ++b) step_scores(f, qf[b], sc[b]);
-    if (nv < 32) {
-#pragma unroll
-      for (int b = 0; b < IB; ++b)
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-          if (slot_key(t, lg) >= nv) sc[b][t] = -INFINITY;
-    }
-#pragma unroll
-    for (int b = 0; b < IB; ++b) softmax_step(f, sc[b], max8(sc[b]), cscale, M[b], Z[b], acc[b]);
+    if (nv == 32) attn_step<IB, false>(f, qf, nv, lg, cscale, M, Z, acc, NoHook{});
+    else attn_step<IB, true>(f, qf, nv, lg, cscale, M, Z, acc, NoHook{});
     if (more) ld.store(nxt, nxt + TL::K_ELEMS);
     __syncthreads();
   }

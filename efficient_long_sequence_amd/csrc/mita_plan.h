@@ -50,6 +50,9 @@ struct Plan {
   int smax;       // compiled top-s list length (>= s)
   int at_nw, at_ib, T;  // attention waves, 16-query blocks per wave, queries per tile
   int UB;         // upper bound on work items per slot
+  int fast;       // LDS-resident routing + shared part and per-expert attention
+  int rs_qpw;     // queries per routing workgroup (resident path)
+  int ex_nw, ex_ib;  // expert kernel waves and 16-query blocks per query group
   float cscale;   // log2(e) / sqrt(d)
 
   // workspace regions
@@ -71,7 +74,9 @@ struct Plan {
   int32_t* perm;    // [s, BH * N]
   WorkItem* wl;     // [s, UB]
   int* wl_count;    // [s]
-  float* part;      // [s - 1, BH, N, d + 4]
+  float* part;      // [s - 1, BH, N, d + 4]  (streaming path)
+  float* plse;      // [BH, N] log2-sum-exp of the finished part (resident path)
+  void* po;         // [BH, N, d] normalised output of the finished part (fp16; fp32 for fp32 inputs)
   void* zero_begin;
   size_t zero_bytes;
   size_t total_bytes;
@@ -93,5 +98,10 @@ void launch_final(const Plan& p);
 void launch_route(const Plan& p);
 void launch_bucket(const Plan& p);
 void launch_attend(const Plan& p);
+void launch_route_shared(const Plan& p);
+void launch_expert(const Plan& p);
+size_t resident_bytes(int dtype, int d, int E);
+// LDS a resident entry set may take (of 160 KB per compute unit).
+constexpr size_t RES_MAX = 150 * 1024;
 
 }  // namespace mita

@@ -1,0 +1,395 @@
+// LDS-resident routing and attention (used when the m landmark entries and
+// the k entries of one expert each fit in LDS).
+//
+// MiTA's joint softmax (MiTA tutorial (iwxt.cn), ch.4 steps 5-6) runs over
+// the m shared entries (q~_i, v~_i), the same for every query of a head, and
+// the k entries of the query's expert.  Both kernels below keep their entry
+// set in LDS for the lifetime of the workgroup (keys row-major, values
+// transposed for the P.V matrix product) and let every wave stream its own
+// queries through it with no barrier in the inner loop:
+//
+//   k_route_shared  per (head, range of queries): q . q~_i for all m
+//                   landmarks on the matrix cores.  The raw scores pick the
+//                   top-s experts (routing, tutorial ch.4 step 4) and, scaled
+//                   by 1/sqrt(d), are the shared logits of the joint softmax
+//                   (the reuse the tutorial's cost count of ch.6 assumes), so
+//                   the shared part of the output is finished here and stored
+//                   as a partial: log2-sum-exp and the normalised output
+//                   (fp16).
+//   k_expert        per (expert, range of its queries): the expert's k
+//                   gathered key/value rows staged once, the routed logits
+//                   and values on the matrix cores, then the merge with the
+//                   stored partial by the rescaled-sum identity
+//                   (Z1 o1 + Z2 o2) / (Z1 + Z2) of tutorial ch.4.  One launch
+//                   per routing slot; the last one writes O.
+#include "mita_dev.h"
+#include "mita_plan.h"
+#include "tile.h"
+
+namespace mita {
+
+typedef _Float16 f16;
+
+// Storage type of the finished-part output between kernels: fp16 for bf16
+// inputs (a smaller rounding than the bf16 output itself), fp32 for fp32.
+template <typename T> struct PartT { typedef f16 type; };
+template <> struct PartT<float> { typedef float type; };
+
+template <typename P> struct Vec4;
+template <> struct Vec4<f16> { typedef __attribute__((__vector_size__(4 * sizeof(f16)))) f16 type; };
+template <> struct Vec4<float> { typedef __attribute__((__vector_size__(4 * sizeof(float)))) float type; };
+
+template <typename T, int D>
+struct Resident {
+  static constexpr int EPC = 16 / (int)sizeof(T);
+  static constexpr int KS = D + EPC;  // key row stride (as TileLayout)
+  static constexpr int CPR = D / EPC;
+  __host__ __device__ static int pad(int E) { return (E + 31) / 32 * 32; }
+  __host__ __device__ static size_t bytes(int Ep) { return ((size_t)Ep * KS + (size_t)D * (Ep + 4)) * sizeof(T); }
+
+  // Stage E entries: key row x from rk(x), value row from rv(x); rows E..Ep-1
+  // are zero.  Keys row-major [Ep][KS]; values transposed [D][Ep + 4].
+  template <class RK, class RV>
+  __device__ static void load(T* Ks, T* Vs, int E, int Ep, RK rk, RV rv) {
+    const int vs = Ep + 4;
+    for (int i = threadIdx.x; i < Ep * CPR; i += blockDim.x) {
+      const int x = i / CPR, c = i % CPR;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (x < E) v = *(const uint4*)(rk(x) + c * EPC);
+      *(uint4*)(Ks + x * KS + c * EPC) = v;
+    }
+    if constexpr (sizeof(T) == 2) {
+      for (int i = threadIdx.x; i < (Ep / 2) * CPR; i += blockDim.x) {
+        const int xp = i / CPR, c0 = (i % CPR) * EPC;
+        uint4 ra = make_uint4(0, 0, 0, 0), rb = make_uint4(0, 0, 0, 0);
+        if (2 * xp < E) ra = *(const uint4*)(rv(2 * xp) + c0);
+        if (2 * xp + 1 < E) rb = *(const uint4*)(rv(2 * xp + 1) + c0);
+        const uint32_t* a = (const uint32_t*)&ra;
+        const uint32_t* b = (const uint32_t*)&rb;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          *(uint32_t*)(Vs + (c0 + 2 * u) * vs + 2 * xp) = (a[u] & 0xFFFFu) | (b[u] << 16);
+          *(uint32_t*)(Vs + (c0 + 2 * u + 1) * vs + 2 * xp) = (a[u] >> 16) | (b[u] & 0xFFFF0000u);
+        }
+      }
+    } else {
+      for (int i = threadIdx.x; i < Ep * CPR; i += blockDim.x) {
+        const int x = i / CPR, c0 = (i % CPR) * EPC;
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (x < E) a = *(const float4*)(rv(x) + c0);
+        Vs[(c0 + 0) * vs + x] = a.x;
+        Vs[(c0 + 1) * vs + x] = a.y;
+        Vs[(c0 + 2) * vs + x] = a.z;
+        Vs[(c0 + 3) * vs + x] = a.w;
+      }
+    }
+  }
+
+  // Matrix-core operands of the 32 entries starting at x0.
+  __device__ static void frags(StepFrags<T, D>& f, const T* Ks, const T* Vs, int Ep, int x0, int li, int g) {
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int dc = 0; dc < D / 32; ++dc) load8(f.ka[jt][dc], Ks + (x0 + jt * 16 + li) * KS + dc * 32 + 8 * g);
+    const int vs = Ep + 4;
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb) {
+      const T* row = Vs + (cb * 16 + li) * vs + x0;
+      load4x2(f.va[cb], row + 4 * g, row + 16 + 4 * g);
+    }
+  }
+};
+
+template <int S>
+__device__ __forceinline__ void list_insert(float* lv, int* lx, float v, int i) {
+#pragma unroll
+  for (int t = S - 1; t >= 0; --t) {
+    const bool above = (t > 0) && (v > lv[t - 1] || (v == lv[t - 1] && i < lx[t - 1]));
+    const bool here = v > lv[t] || (v == lv[t] && i < lx[t]);
+    if (above) { lv[t] = lv[t - 1]; lx[t] = lx[t - 1]; }
+    else if (here) { lv[t] = v; lx[t] = i; }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <typename T, int D, int NW, int SMAX>
+__global__ __launch_bounds__(NW * 64) void k_route_shared(
+    const T* __restrict__ Q, const T* __restrict__ Qt, const T* __restrict__ VtT, int32_t* __restrict__ route,
+    int* __restrict__ counts, float* __restrict__ plse, typename PartT<T>::type* __restrict__ po, int N, int m, int s,
+    int BH, int qpw, int hist_lds, float cscale) {
+  using RL = Resident<T, D>;
+  using P = typename PartT<T>::type;
+  using PV = typename Vec4<P>::type;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int Mp = RL::pad(m);
+  T* Ks = (T*)smem;
+  T* Vs = Ks + (size_t)Mp * RL::KS;
+  int* hist = (int*)(smem + RL::bytes(Mp));
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, li = lane % 16, lg = lane / 16;
+  const int bh = blockIdx.y;
+  const int q0 = blockIdx.x * qpw, q1 = min(N, q0 + qpw);
+  const T* Qh = Q + (size_t)bh * N * D;
+  if (hist_lds)
+    for (int x = tid; x < s * m; x += NW * 64) hist[x] = 0;
+  RL::load(Ks, Vs, m, Mp, [&](int x) { return Qt + ((size_t)bh * m + x) * D; },
+           [&](int x) { return VtT + ((size_t)bh * m + x) * D; });
+  __syncthreads();
+
+  const int ngroups = (q1 - q0 + 63) / 64;
+  for (int gi = wave; gi < ngroups; gi += NW) {
+    const int qb = q0 + gi * 64;
+    Frag<T> qf[4][D / 32];
+    float lv[4][SMAX], M[4], Z[4];
+    int lx[4][SMAX];
+    f32x4 acc[4][D / 16];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int n = qb + b * 16 + li;
+#pragma unroll
+      for (int dc = 0; dc < D / 32; ++dc) {
+        if (n < q1) load8(qf[b][dc], Qh + (size_t)n * D + dc * 32 + 8 * lg);
+        else zero(qf[b][dc]);
+      }
+#pragma unroll
+      for (int t = 0; t < SMAX; ++t) { lv[b][t] = -INFINITY; lx[b][t] = 0x7FFFFFFF; }
+      M[b] = M0;
+      Z[b] = 0.f;
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb) acc[b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    int x0 = 0;
+    // landmarks reach a lane in increasing order: strict '>' keeps the lower
+    // index on ties
+    auto topsel = [&](int b, const float* sc, float) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (sc[t] > lv[b][SMAX - 1]) list_insert<SMAX>(lv[b], lx[b], sc[t], x0 + slot_key(t, lg));
+    };
+    for (; x0 + 32 <= m; x0 += 32) {
+      StepFrags<T, D> f;
+      RL::frags(f, Ks, Vs, Mp, x0, li, lg);
+      attn_step<4, false>(f, qf, 32, lg, cscale, M, Z, acc, topsel);
+    }
+    if (x0 < m) {
+      StepFrags<T, D> f;
+      RL::frags(f, Ks, Vs, Mp, x0, li, lg);
+      attn_step<4, true>(f, qf, m - x0, lg, cscale, M, Z, acc, topsel);
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+#pragma unroll
+      for (int sh = 16; sh <= 32; sh <<= 1) {
+        float ov[SMAX];
+        int ox[SMAX];
+#pragma unroll
+        for (int t = 0; t < SMAX; ++t) { ov[t] = __shfl_xor(lv[b][t], sh); ox[t] = __shfl_xor(lx[b][t], sh); }
+#pragma unroll
+        for (int t = 0; t < SMAX; ++t) list_insert<SMAX>(lv[b], lx[b], ov[t], ox[t]);
+      }
+      const float Zt = wave_sum_groups(Z[b]);
+      const int n = qb + b * 16 + li;
+      if (n >= q1) continue;
+      const size_t qrow = (size_t)bh * N + n;
+      if (lg == 0) {
+        int32_t* dst = route + qrow * s;
+#pragma unroll
+        for (int t = 0; t < SMAX; ++t) {
+          if (t < s) {
+            // a valid list holds s landmarks; the clamp only keeps non-finite
+            // inputs (unspecified results) inside the buffers
+            const int e = min(max(lx[b][t], 0), m - 1);
+            dst[t] = e;
+            if (hist_lds) atomicAdd(hist + t * m + e, 1);
+            else atomicAdd(counts + ((size_t)t * BH + bh) * m + e, 1);
+          }
+        }
+        plse[qrow] = M[b] + __builtin_amdgcn_logf(Zt);
+      }
+      const float inv = 1.0f / Zt;
+      P* o = po + qrow * D;
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb) {
+        PV h;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) h[r] = (P)(acc[b][cb][r] * inv);
+        *(PV*)(o + cb * 16 + 4 * lg) = h;
+      }
+    }
+  }
+  if (hist_lds) {
+    __syncthreads();
+    for (int x = tid; x < s * m; x += NW * 64) {
+      const int c = hist[x];
+      if (c) atomicAdd(counts + ((size_t)(x / m) * BH + bh) * m + (x % m), c);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <typename T, int D, int NW, int IB>
+__global__ __launch_bounds__(NW * 64) void k_expert(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const int32_t* __restrict__ topk,
+    const int32_t* __restrict__ perm, const WorkItem* __restrict__ wl, const int* __restrict__ wl_count,
+    float* __restrict__ plse, typename PartT<T>::type* __restrict__ po, T* __restrict__ O, int N, int m, int k,
+    int last, float cscale) {
+  using RL = Resident<T, D>;
+  using P = typename PartT<T>::type;
+  using PV = typename Vec4<P>::type;
+  extern __shared__ __align__(16) unsigned char smem[];
+  // Work items of one expert are consecutive in the list; hand each XCD (the
+  // hardware places workgroup i on XCD i mod 8) one contiguous eighth of the
+  // list so an expert's tiles share that XCD's L2.
+  const int nwl = *wl_count;
+  const int seg = (nwl + 7) / 8;
+  const int item = (int)(blockIdx.x % 8) * seg + (int)(blockIdx.x / 8);
+  if ((int)(blockIdx.x / 8) >= seg || item >= nwl) return;
+  const WorkItem it = wl[item];
+  const int Kp = RL::pad(k);
+  T* Ks = (T*)smem;
+  T* Vs = Ks + (size_t)Kp * RL::KS;
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, li = lane % 16, lg = lane / 16;
+  const int bh = it.be / m;
+  const T* Kh = K + (size_t)bh * N * D;
+  const T* Vh = V + (size_t)bh * N * D;
+  const int32_t* Ie = topk + (size_t)it.be * k;
+  RL::load(Ks, Vs, k, Kp, [&](int x) { return Kh + (size_t)Ie[x] * D; },
+           [&](int x) { return Vh + (size_t)Ie[x] * D; });
+  __syncthreads();
+
+  constexpr int GQ = 16 * IB;
+  const int ngroups = (it.count + GQ - 1) / GQ;
+  for (int gi = wave; gi < ngroups; gi += NW) {
+    Frag<T> qf[IB][D / 32];
+    int qn[IB];
+    float M[IB], Z[IB];
+    f32x4 acc[IB][D / 16];
+#pragma unroll
+    for (int b = 0; b < IB; ++b) {
+      const int local = gi * GQ + b * 16 + li;
+      qn[b] = local < it.count ? perm[it.start + local] : -1;
+#pragma unroll
+      for (int dc = 0; dc < D / 32; ++dc) {
+        if (qn[b] >= 0) load8(qf[b][dc], Q + ((size_t)bh * N + qn[b]) * D + dc * 32 + 8 * lg);
+        else zero(qf[b][dc]);
+      }
+      M[b] = M0;
+      Z[b] = 0.f;
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb) acc[b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    int x0 = 0;
+    for (; x0 + 32 <= k; x0 += 32) {
+      StepFrags<T, D> f;
+      RL::frags(f, Ks, Vs, Kp, x0, li, lg);
+      attn_step<IB, false>(f, qf, 32, lg, cscale, M, Z, acc, NoHook{});
+    }
+    if (x0 < k) {
+      StepFrags<T, D> f;
+      RL::frags(f, Ks, Vs, Kp, x0, li, lg);
+      attn_step<IB, true>(f, qf, k - x0, lg, cscale, M, Z, acc, NoHook{});
+    }
+#pragma unroll
+    for (int b = 0; b < IB; ++b) {
+      const float Zt = wave_sum_groups(Z[b]);
+      if (qn[b] < 0) continue;
+      const size_t qrow = (size_t)bh * N + qn[b];
+      // merge with the stored partial: weights 2^lse of the two parts
+      const float la = plse[qrow];
+      const float lb = M[b] + __builtin_amdgcn_logf(Zt);
+      const float mx = fmaxf(la, lb);
+      const float wa = __builtin_amdgcn_exp2f(la - mx), wb = __builtin_amdgcn_exp2f(lb - mx);
+      const float den = wa + wb;
+      const float ca = wa / den, cb_ = wb / (den * Zt);
+      P* o = po + qrow * D;
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb) {
+        const PV h = *(const PV*)(o + cb * 16 + 4 * lg);
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = ca * (float)h[r] + cb_ * acc[b][cb][r];
+        if (last) {
+          T* dst = O + qrow * D + cb * 16 + 4 * lg;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dst[r] = from_f32<T>(v[r]);
+        } else {
+          PV w;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) w[r] = (P)v[r];
+          *(PV*)(o + cb * 16 + 4 * lg) = w;
+        }
+      }
+      if (!last && lg == 0) plse[qrow] = mx + __builtin_amdgcn_logf(den);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+size_t resident_bytes(int dtype, int d, int E) {
+  const int Ep = (E + 31) / 32 * 32;
+  if (dtype == 1) return d == 64 ? Resident<__bf16, 64>::bytes(Ep) : Resident<__bf16, 32>::bytes(Ep);
+  return d == 64 ? Resident<float, 64>::bytes(Ep) : Resident<float, 32>::bytes(Ep);
+}
+
+template <typename T, int D, int SMAX>
+static void launch_route_shared_t(const Plan& p) {
+  constexpr int NW = 8;
+  const int hist_lds = (p.s * p.m <= 4096) ? 1 : 0;
+  const size_t lds = resident_bytes(p.dtype, D, p.m) + (hist_lds ? (size_t)p.s * p.m * 4 : 0);
+  auto fn = &k_route_shared<T, D, NW, SMAX>;
+  if (lds > 65536)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  dim3 grid((unsigned)((p.N + p.rs_qpw - 1) / p.rs_qpw), (unsigned)p.BH);
+  hipLaunchKernelGGL(fn, grid, dim3(NW * 64), lds, p.stream, (const T*)p.Q, (const T*)p.qt, (const T*)p.vtT, p.route,
+                     p.counts, p.plse, (typename PartT<T>::type*)p.po, p.N, p.m, p.s, p.BH, p.rs_qpw, hist_lds, p.cscale);
+}
+
+template <typename T, int D>
+static void launch_route_shared_d(const Plan& p) {
+  switch (p.smax) {
+    case 1: launch_route_shared_t<T, D, 1>(p); break;
+    case 2: launch_route_shared_t<T, D, 2>(p); break;
+    case 4: launch_route_shared_t<T, D, 4>(p); break;
+    default: launch_route_shared_t<T, D, 8>(p); break;
+  }
+}
+
+void launch_route_shared(const Plan& p) {
+  if (p.dtype == 0) {
+    if (p.d == 32) launch_route_shared_d<float, 32>(p); else launch_route_shared_d<float, 64>(p);
+  } else {
+    if (p.d == 32) launch_route_shared_d<__bf16, 32>(p); else launch_route_shared_d<__bf16, 64>(p);
+  }
+}
+
+template <typename T, int D, int NW, int IB>
+static void launch_expert_t(const Plan& p) {
+  const size_t lds = resident_bytes(p.dtype, D, p.k);
+  auto fn = &k_expert<T, D, NW, IB>;
+  if (lds > 65536)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  for (int t = 0; t < p.s; ++t) {
+    const int32_t* perm = p.perm + (size_t)t * p.BH * p.N;
+    const WorkItem* wl = p.wl + (size_t)t * p.UB;
+    hipLaunchKernelGGL(fn, dim3((unsigned)(p.UB + 8)), dim3(NW * 64), lds, p.stream, (const T*)p.Q, (const T*)p.K,
+                       (const T*)p.V, p.topk, perm, wl, p.wl_count + t, p.plse, (typename PartT<T>::type*)p.po, (T*)p.O, p.N, p.m, p.k,
+                       t == p.s - 1 ? 1 : 0, p.cscale);
+  }
+}
+
+template <typename T, int D>
+static void launch_expert_d(const Plan& p) {
+  if (p.ex_nw == 1 && p.ex_ib == 1) launch_expert_t<T, D, 1, 1>(p);
+  else if (p.ex_nw == 1) launch_expert_t<T, D, 1, 2>(p);
+  else if (p.ex_nw == 4) launch_expert_t<T, D, 4, 4>(p);
+  else launch_expert_t<T, D, 8, 4>(p);
+}
+
+void launch_expert(const Plan& p) {
+  if (p.dtype == 0) {
+    if (p.d == 32) launch_expert_t<float, 32, 1, 1>(p); else launch_expert_t<float, 64, 1, 1>(p);
+  } else {
+    if (p.d == 32) launch_expert_d<__bf16, 32>(p); else launch_expert_d<__bf16, 64>(p);
+  }
+}
+
+}  // namespace mita

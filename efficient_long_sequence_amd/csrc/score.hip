@@ -198,21 +198,9 @@ __global__ __launch_bounds__(NW * 64) void k_score(
     f.load_keys(cur, li, lg);
     f.load_vals(cur + TL::K_ELEMS, li, lg);
     const int nv = min(32, j_end - j0);
-    // all score tiles of the step first, so the softmax of one row block
-    // overlaps the matrix work of the others
-    float sc[IB][8];
-#pragma unroll
-    for (int b = 0; b < IB; ++b) step_scores(f, qf[b], sc[b]);
-    if (nv < 32) {
-#pragma unroll
-      for (int b = 0; b < IB; ++b)
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-          if (slot_key(t, lg) >= nv) sc[b][t] = -INFINITY;
-    }
-#pragma unroll
-    for (int b = 0; b < IB; ++b) {
-      const float mx = max8(sc[b]);
+    // per row block: every score of a small head is a candidate (DENSE);
+    // otherwise the scores >= tau are staged, one LDS reservation per lane
+    auto cands = [&](int b, const float* sc, float mx) {
       const int row = rbase + b * 16 + li;
       if constexpr (DENSE) {
         if (row < m) {
@@ -220,23 +208,22 @@ __global__ __launch_bounds__(NW * 64) void k_score(
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
             const int kl = slot_key(t, lg);
-            if (kl < nv) dst[kl] = ckey(sc[b][t], (uint32_t)(j0 + kl));
+            if (kl < nv) dst[kl] = ckey(sc[t], (uint32_t)(j0 + kl));
           }
         }
       } else if (wave_any(mx >= tau[b])) {
         uint32_t msk = 0;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) msk |= (sc[b][t] >= tau[b] ? 1u : 0u) << t;
+        for (int t = 0; t < 8; ++t) msk |= (sc[t] >= tau[b] ? 1u : 0u) << t;
         if (msk) {
-          // one LDS reservation per lane for all of its candidates
           int e = atomicAdd(s_ncand, __builtin_popcount(msk));
           const uint32_t rl = (uint32_t)(row - rt * R) << 23;
           while (msk) {
             const int t = __builtin_ctz(msk);
             msk &= msk - 1;
-            float v = sc[b][0];
+            float v = sc[0];
 #pragma unroll
-            for (int u = 1; u < 8; ++u) v = (t == u) ? sc[b][u] : v;
+            for (int u = 1; u < 8; ++u) v = (t == u) ? sc[u] : v;
             const int jl = j0 + slot_key(t, lg) - j_begin;
             if (e < cb_cap) {
               s_cand[e] = make_uint2(__float_as_uint(v), rl | (uint32_t)jl);
@@ -248,8 +235,9 @@ __global__ __launch_bounds__(NW * 64) void k_score(
           }
         }
       }
-      softmax_step(f, sc[b], mx, cscale, M[b], Z[b], acc[b]);
-    }
+    };
+    if (nv == 32) attn_step<IB, false>(f, qf, nv, lg, cscale, M, Z, acc, cands);
+    else attn_step<IB, true>(f, qf, nv, lg, cscale, M, Z, acc, cands);
     if (more) ld.store(nxt, nxt + TL::K_ELEMS);
     __syncthreads();
   }

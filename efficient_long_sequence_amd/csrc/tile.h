@@ -177,4 +177,35 @@ __device__ __forceinline__ float max8(const float* s) {
   return fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
 }
 
+// One 32-entry step for IB blocks of 16 queries: the score tiles of all
+// blocks first (so one block's softmax overlaps the others' matrix work),
+// then, per block, the hook `on(b, scores, lane_max)` (candidates, routing)
+// and the online-softmax update with P.V.  MASK marks the last, partial step:
+// entries at offsets >= nv get score -inf.
+template <int IB, bool MASK, typename T, int D, class On>
+__device__ __forceinline__ void attn_step(const StepFrags<T, D>& f, const Frag<T> (&qf)[IB][D / 32], int nv, int lg,
+                                          float cscale, float (&M)[IB], float (&Z)[IB], f32x4 (&acc)[IB][D / 16],
+                                          On on) {
+  float sc[IB][8];
+#pragma unroll
+  for (int b = 0; b < IB; ++b) step_scores(f, qf[b], sc[b]);
+  if constexpr (MASK) {
+#pragma unroll
+    for (int b = 0; b < IB; ++b)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (slot_key(t, lg) >= nv) sc[b][t] = -INFINITY;
+  }
+#pragma unroll
+  for (int b = 0; b < IB; ++b) {
+    const float mx = max8(sc[b]);
+    on(b, sc[b], mx);
+    softmax_step(f, sc[b], mx, cscale, M[b], Z[b], acc[b]);
+  }
+}
+
+struct NoHook {
+  __device__ __forceinline__ void operator()(int, const float*, float) const {}
+};
+
 }  // namespace mita
