@@ -34,39 +34,46 @@ METRIC = "MiTA fwd tokens/s (B·H·N) at N=64K/256K/1M; % of HBM and MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = {
-    "attend": ["attend.hip", "tile.h", "mita_dev.h"],
-    "score": ["score.hip", "tile.h", "mita_dev.h"],
-}
+COPY_FETCH_FACTOR_DEFAULT = 2.0  # see profiles/: FETCH_SIZE reads half of a plain copy's bytes
 
 
-def sources_sha(stage: str) -> str:
+def sources_sha() -> str:
+    """Hash of every kernel source: counter figures are only reported for the
+    kernels they were measured on."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES.get(stage, []):
-        with open(os.path.join(ROOT, "efficient_long_sequence_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    csrc = os.path.join(ROOT, "efficient_long_sequence_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
 def algorithmic(w, stage: str):
-    """Algorithmic flops and HBM bytes of one launch of a stage's kernel(s).
+    """Algorithmic flops and HBM bytes of one launch of a stage's kernel.
 
-    attend: per query, m + s*k logits and value sums of length d
-            (4 d (m + s k) flops); reads Q, the m*k gathered K and V rows,
-            Q~ and V~ (bf16), the expert index lists and the permutation,
-            writes O.
-    score:  per landmark row and key, one logit and one value sum
-            (4 d N m flops); reads K and V once, writes the v~ partials.
+    score:  every landmark row against every key: one logit and one value sum
+            of length d (4 d N m flops); reads K and V once and Q~, writes v~.
+    route:  every query against every landmark: the routing score, which is
+            also the shared logit, and the shared value sum (4 d N m flops);
+            reads Q, Q~, v~, writes the routes and the shared-part partial
+            (fp16 output and log2-sum-exp per query).
+    attend: every query against the k raw entries of each of its s experts
+            (4 d N s k flops); reads Q, the m*k gathered key and value rows,
+            the partial, the expert index lists and the permutation, writes O.
     """
     es = 2 if w.dtype == "bf16" else 4
+    ps = 2 if w.dtype == "bf16" else 4
     BH, N, d, m, k, s = w.B * w.H, w.N, w.d, w.m, w.k, w.s
-    if stage == "attend":
-        flops = 4.0 * d * N * (m + s * k) * BH
-        byts = BH * (2 * N * d * es + 2 * m * k * d * es + 2 * m * d * es + m * k * 4 + s * N * 4)
-    elif stage == "score":
+    if stage == "score":
         flops = 4.0 * d * N * m * BH
-        chunks = 1  # partial records are small next to K and V
-        byts = BH * (2 * N * d * es + m * d * es + m * chunks * (d + 4) * 4)
+        byts = BH * (2 * N * d * es + m * d * es + m * d * 4)
+    elif stage == "route":
+        flops = 4.0 * d * N * m * BH
+        byts = BH * (N * d * es + 2 * m * d * es + N * s * 4 + N * (d * ps + 4))
+    elif stage == "attend":
+        flops = 4.0 * d * N * s * k * BH
+        byts = BH * (N * d * es + 2 * m * k * d * es + N * (d * ps + 4) + m * k * 4 + s * N * 4 + N * d * es)
     else:
         return None, None
     return flops, float(byts)
@@ -112,37 +119,116 @@ def time_workload(w, steps: int, warmup: int):
                 host=host, q=q, k=k, v=v, pool=pool, ws=ws)
 
 
-def roofline(w, stages: dict):
-    dom = max(("attend", "score"), key=lambda s: stages.get(s, 0.0))
-    flops, byts = algorithmic(w, dom)
-    sec = stages[dom] * 1e-3
-    intensity = flops / byts
+STAGE_KERNEL = {"score": "k_score", "route": "k_route_shared", "attend": "k_expert"}
+
+
+def roofline_of(w, stages: dict, stage: str, traffic):
+    flops, byts = algorithmic(w, stage)
+    sec = stages[stage] * 1e-3
     peak_f = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
-    traffic = measured_traffic(w, dom)
-    if intensity > ridge:
+    if flops / byts > ridge:
         r = dict(bound="mfma", achieved=flops / sec / 1e12, peak=peak_f, unit="TFLOP/s")
     else:
         r = dict(bound="hbm", achieved=byts / sec / 1e9, peak=PEAK_HBM_GBS, unit="GB/s")
     r["frac"] = r["achieved"] / r["peak"]
     r["traffic"] = traffic
-    r.update(kernel=dom, kernel_ms=stages[dom], alg_flops=flops, alg_bytes=byts,
+    r.update(kernel=STAGE_KERNEL[stage], kernel_ms=stages[stage], alg_flops=flops, alg_bytes=byts,
              hbm_gbs_alg=byts / sec / 1e9, mfma_tflops_alg=flops / sec / 1e12)
     return r
 
 
+def roofline(w, stages: dict):
+    """Roofline of the dominant kernel, plus the other two heavy kernels."""
+    heavy = [s for s in ("score", "route", "attend") if stages.get(s, 0.0) > 0]
+    dom = max(heavy, key=lambda s: stages[s])
+    r = roofline_of(w, stages, dom, measured_traffic(w, dom))
+    r["others"] = {s: {k2: v for k2, v in roofline_of(w, stages, s, measured_traffic(w, s)).items()
+                       if k2 in ("bound", "achieved", "frac", "unit", "kernel", "kernel_ms", "traffic")}
+                   for s in heavy if s != dom}
+    return r
+
+
 def measured_traffic(w, stage: str):
-    """HBM bytes per launch from the committed counter summary, if it matches
-    this workload and the current kernel sources."""
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on this workload and on the current kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    ent = rec.get(f"{stage}:{w.name}")
-    if not ent or ent.get("sources_sha") != sources_sha(stage):
+    if rec.get("sources_sha") != sources_sha():
         return None
-    return ent.get("bytes_per_launch")
+    ent = rec.get("kernels", {}).get(f"{STAGE_KERNEL[stage]}:{w.name}")
+    return None if not ent else ent.get("bytes_per_launch")
+
+
+def ingest(trace_dir: str, fetch_dir: str, write_dir: str, workload: str, command: str):
+    """Turn rocprofv3 output (kernel-trace stats, FETCH_SIZE and WRITE_SIZE
+    counter runs of the same command with --copy-calib-mib) into the committed
+    text summaries under profiles/."""
+    import csv
+    import glob
+
+    def rows(d, pat):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", pat), recursive=True):
+            out += list(csv.DictReader(open(f)))
+        return out
+
+    def short(name):
+        n = name.split("(")[0]
+        for key in ("k_score", "k_expert", "k_route_shared", "k_route", "k_attend", "k_final", "k_pool", "k_scatter",
+                    "k_est", "k_tau", "k_scan", "k_zero", "k_fallback"):
+            if f"{len(key)}{key}I" in n or n.endswith(key) or f"::{key}" in n or f"{len(key)}{key}E" in n:
+                return key
+        return n[:48]
+
+    stats = rows(trace_dir, "*kernel_stats.csv")
+    counters = {}
+    for kind, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        acc = {}
+        for r in rows(d, "*counter_collection.csv"):
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        counters[kind] = acc
+    copy = [k for k in counters["FETCH_SIZE"] if "copyBuffer" in k]
+    calib = {}
+    if copy:
+        n_kib = None
+        for kind in ("FETCH_SIZE", "WRITE_SIZE"):
+            v = counters[kind][copy[0]][0]
+            calib[kind] = v
+    mib = int(command.split("--copy-calib-mib")[1].split()[0]) if "--copy-calib-mib" in command else 0
+    f_fac = (mib * 1024 / calib["FETCH_SIZE"]) if calib.get("FETCH_SIZE") else COPY_FETCH_FACTOR_DEFAULT
+    w_fac = (mib * 1024 / calib["WRITE_SIZE"]) if calib.get("WRITE_SIZE") else 1.0
+    kern = {}
+    for name, vals in counters["FETCH_SIZE"].items():
+        key = short(name)
+        if key.startswith("k_"):
+            fetch = sum(vals) / len(vals) * 1024 * f_fac
+            wv = counters["WRITE_SIZE"].get(name, [0.0])
+            write = sum(wv) / len(wv) * 1024 * w_fac
+            kern[f"{key}:{workload}"] = dict(fetch_bytes=fetch, write_bytes=write, bytes_per_launch=fetch + write)
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(dict(sources_sha=sources_sha(), workload=workload, command=command,
+                       fetch_factor=f_fac, write_factor=w_fac, kernels=kern), f, indent=1)
+    lines = [f"# rocprofv3 kernel trace and HBM traffic: mita_forward, {workload}", "",
+             "Command (run from /tmp, TMPDIR=/tmp, repository at $R):", "",
+             f"    rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- {command}",
+             f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- {command}",
+             f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o run -- {command}", "",
+             f"Counter calibration (plain {mib} MiB device copy in the same run): FETCH_SIZE x{f_fac:.3f}, "
+             f"WRITE_SIZE x{w_fac:.3f}.", f"Kernel sources hash: {sources_sha()}.", "",
+             "| kernel | calls | avg us | % time | HBM fetch MB | HBM write MB |", "|---|---|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        key = short(r["Name"])
+        t = kern.get(f"{key}:{workload}", {})
+        lines.append(f"| {key} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} | "
+                     f"{t.get('fetch_bytes', 0) / 1e6:.1f} | {t.get('write_bytes', 0) / 1e6:.1f} |")
+    with open(os.path.join(ROOT, "profiles", f"mita_forward_{workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def cpu_baseline(w, run):
@@ -203,7 +289,15 @@ def main():
     ap.add_argument("--workload", default=HEADLINE, choices=list(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", action="store_true", help="time only --workload")
+    ap.add_argument("--ingest", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/ summaries from rocprofv3 output of the same command")
+    ap.add_argument("--ingest-command", default="")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
+    if args.ingest:
+        ingest(*args.ingest, workload=args.workload, command=args.ingest_command)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(every head is independent: a multi-GPU run would shard heads with no communication)",
@@ -214,6 +308,14 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(2)
     w = WORKLOADS[args.workload]
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     run = time_workload(w, args.steps, args.warmup)
     others = []
     if not args.only:

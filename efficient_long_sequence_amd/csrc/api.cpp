@@ -101,7 +101,10 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
   p.smax = s <= 1 ? 1 : s <= 2 ? 2 : s <= 4 ? 4 : 8;
   const double avg = (double)N / m;  // queries per expert and slot, on average
   const size_t hist_bytes = (size_t)s * m <= 4096 ? (size_t)s * m * 4 : 0;
-  p.fast = (resident_bytes(p.dtype, d, m) + hist_bytes <= RES_MAX && resident_bytes(p.dtype, d, k) <= RES_MAX) ? 1 : 0;
+  // (the expert kernel also stages its k key indices and up to 2048 query
+  // indices in LDS)
+  p.fast = (resident_bytes(p.dtype, d, m) + hist_bytes <= RES_MAX &&
+            resident_bytes(p.dtype, d, k) + (size_t)(k + 32 + 2048) * 4 <= RES_MAX) ? 1 : 0;
   if (p.fast) {
     // routing workgroups: about 1024 in all, 512 queries at least
     long long qpw = ((long long)p.BH * N + 1023) / 1024;

@@ -48,39 +48,72 @@ struct Resident {
   __host__ __device__ static size_t bytes(int Ep) { return ((size_t)Ep * KS + (size_t)D * (Ep + 4)) * sizeof(T); }
 
   // Stage E entries: key row x from rk(x), value row from rv(x); rows E..Ep-1
-  // are zero.  Keys row-major [Ep][KS]; values transposed [D][Ep + 4].
+  // are zero.  Keys row-major [Ep][KS]; values transposed [D][Ep + 4].  Each
+  // thread issues its global loads in batches of 8 before the LDS stores, so
+  // a batch costs one memory latency instead of eight.
   template <class RK, class RV>
   __device__ static void load(T* Ks, T* Vs, int E, int Ep, RK rk, RV rv) {
-    const int vs = Ep + 4;
-    for (int i = threadIdx.x; i < Ep * CPR; i += blockDim.x) {
-      const int x = i / CPR, c = i % CPR;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (x < E) v = *(const uint4*)(rk(x) + c * EPC);
-      *(uint4*)(Ks + x * KS + c * EPC) = v;
+    constexpr int U = 8;
+    const int vs = Ep + 4, nt = blockDim.x, tid = threadIdx.x;
+    const int nk = Ep * CPR;
+    for (int base = 0; base < nk; base += U * nt) {
+      uint4 r[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = base + u * nt + tid, x = i / CPR;
+        r[u] = make_uint4(0, 0, 0, 0);
+        if (i < nk && x < E) r[u] = *(const uint4*)(rk(x) + (i % CPR) * EPC);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = base + u * nt + tid;
+        if (i < nk) *(uint4*)(Ks + (i / CPR) * KS + (i % CPR) * EPC) = r[u];
+      }
     }
     if constexpr (sizeof(T) == 2) {
-      for (int i = threadIdx.x; i < (Ep / 2) * CPR; i += blockDim.x) {
-        const int xp = i / CPR, c0 = (i % CPR) * EPC;
-        uint4 ra = make_uint4(0, 0, 0, 0), rb = make_uint4(0, 0, 0, 0);
-        if (2 * xp < E) ra = *(const uint4*)(rv(2 * xp) + c0);
-        if (2 * xp + 1 < E) rb = *(const uint4*)(rv(2 * xp + 1) + c0);
-        const uint32_t* a = (const uint32_t*)&ra;
-        const uint32_t* b = (const uint32_t*)&rb;
+      // two value rows per task, packed into 32-bit transposed writes
+      const int ntask = (Ep / 2) * CPR;
+      for (int base = 0; base < ntask; base += (U / 2) * nt) {
+        uint4 ra[U / 2], rb[U / 2];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          *(uint32_t*)(Vs + (c0 + 2 * u) * vs + 2 * xp) = (a[u] & 0xFFFFu) | (b[u] << 16);
-          *(uint32_t*)(Vs + (c0 + 2 * u + 1) * vs + 2 * xp) = (a[u] >> 16) | (b[u] & 0xFFFF0000u);
+        for (int u = 0; u < U / 2; ++u) {
+          const int i = base + u * nt + tid, xp = i / CPR, c0 = (i % CPR) * EPC;
+          ra[u] = make_uint4(0, 0, 0, 0);
+          rb[u] = make_uint4(0, 0, 0, 0);
+          if (i < ntask && 2 * xp < E) ra[u] = *(const uint4*)(rv(2 * xp) + c0);
+          if (i < ntask && 2 * xp + 1 < E) rb[u] = *(const uint4*)(rv(2 * xp + 1) + c0);
+        }
+#pragma unroll
+        for (int u = 0; u < U / 2; ++u) {
+          const int i = base + u * nt + tid, xp = i / CPR, c0 = (i % CPR) * EPC;
+          if (i >= ntask) continue;
+          const uint32_t* a = (const uint32_t*)&ra[u];
+          const uint32_t* b = (const uint32_t*)&rb[u];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            *(uint32_t*)(Vs + (c0 + 2 * w) * vs + 2 * xp) = (a[w] & 0xFFFFu) | (b[w] << 16);
+            *(uint32_t*)(Vs + (c0 + 2 * w + 1) * vs + 2 * xp) = (a[w] >> 16) | (b[w] & 0xFFFF0000u);
+          }
         }
       }
     } else {
-      for (int i = threadIdx.x; i < Ep * CPR; i += blockDim.x) {
-        const int x = i / CPR, c0 = (i % CPR) * EPC;
-        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (x < E) a = *(const float4*)(rv(x) + c0);
-        Vs[(c0 + 0) * vs + x] = a.x;
-        Vs[(c0 + 1) * vs + x] = a.y;
-        Vs[(c0 + 2) * vs + x] = a.z;
-        Vs[(c0 + 3) * vs + x] = a.w;
+      for (int base = 0; base < nk; base += U * nt) {
+        float4 r[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = base + u * nt + tid, x = i / CPR;
+          r[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (i < nk && x < E) r[u] = *(const float4*)(rv(x) + (i % CPR) * EPC);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = base + u * nt + tid, x = i / CPR, c0 = (i % CPR) * EPC;
+          if (i >= nk) continue;
+          Vs[(c0 + 0) * vs + x] = r[u].x;
+          Vs[(c0 + 1) * vs + x] = r[u].y;
+          Vs[(c0 + 2) * vs + x] = r[u].z;
+          Vs[(c0 + 3) * vs + x] = r[u].w;
+        }
       }
     }
   }
@@ -99,6 +132,21 @@ struct Resident {
     }
   }
 };
+
+// Query fragments of one group of 16*IB queries (rows given by qrow(b), or
+// -1 for an empty slot).
+template <typename T, int D, int IB, class QR>
+__device__ __forceinline__ void load_queries(Frag<T> (&qf)[IB][D / 32], const T* Q, int lg, QR qrow) {
+#pragma unroll
+  for (int b = 0; b < IB; ++b) {
+    const long long r = qrow(b);
+#pragma unroll
+    for (int dc = 0; dc < D / 32; ++dc) {
+      if (r >= 0) load8(qf[b][dc], Q + (size_t)r * D + dc * 32 + 8 * lg);
+      else zero(qf[b][dc]);
+    }
+  }
+}
 
 template <int S>
 __device__ __forceinline__ void list_insert(float* lv, int* lx, float v, int i) {
@@ -136,20 +184,25 @@ __global__ __launch_bounds__(NW * 64) void k_route_shared(
   __syncthreads();
 
   const int ngroups = (q1 - q0 + 63) / 64;
+  auto group_rows = [&](int gi) {
+    return [=](int b) -> long long { const int n = q0 + gi * 64 + b * 16 + li; return n < q1 ? n : -1; };
+  };
+  // the next group's query rows are fetched while the current one computes
+  Frag<T> qn[4][D / 32];
+  if (wave < ngroups) load_queries<T, D, 4>(qn, Qh, lg, group_rows(wave));
   for (int gi = wave; gi < ngroups; gi += NW) {
     const int qb = q0 + gi * 64;
     Frag<T> qf[4][D / 32];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int dc = 0; dc < D / 32; ++dc) qf[b][dc] = qn[b][dc];
+    if (gi + NW < ngroups) load_queries<T, D, 4>(qn, Qh, lg, group_rows(gi + NW));
     float lv[4][SMAX], M[4], Z[4];
     int lx[4][SMAX];
     f32x4 acc[4][D / 16];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const int n = qb + b * 16 + li;
-#pragma unroll
-      for (int dc = 0; dc < D / 32; ++dc) {
-        if (n < q1) load8(qf[b][dc], Qh + (size_t)n * D + dc * 32 + 8 * lg);
-        else zero(qf[b][dc]);
-      }
 #pragma unroll
       for (int t = 0; t < SMAX; ++t) { lv[b][t] = -INFINITY; lx[b][t] = 0x7FFFFFFF; }
       M[b] = M0;
@@ -251,27 +304,41 @@ __global__ __launch_bounds__(NW * 64) void k_expert(
   const int bh = it.be / m;
   const T* Kh = K + (size_t)bh * N * D;
   const T* Vh = V + (size_t)bh * N * D;
+  // the expert's key indices and the item's query indices, staged in LDS
+  int* s_idx = (int*)(smem + RL::bytes(Kp));
+  int* s_q = s_idx + Kp;
   const int32_t* Ie = topk + (size_t)it.be * k;
-  RL::load(Ks, Vs, k, Kp, [&](int x) { return Kh + (size_t)Ie[x] * D; },
-           [&](int x) { return Vh + (size_t)Ie[x] * D; });
+  for (int x = tid; x < k; x += NW * 64) s_idx[x] = Ie[x];
+  for (int x = tid; x < it.count; x += NW * 64) s_q[x] = perm[it.start + x];
+  __syncthreads();
+  RL::load(Ks, Vs, k, Kp, [&](int x) { return Kh + (size_t)s_idx[x] * D; },
+           [&](int x) { return Vh + (size_t)s_idx[x] * D; });
   __syncthreads();
 
   constexpr int GQ = 16 * IB;
   const int ngroups = (it.count + GQ - 1) / GQ;
+  const T* Qh = Q + (size_t)bh * N * D;
+  auto group_rows = [&](int gi) {
+    return [=](int b) -> long long { const int l = gi * GQ + b * 16 + li; return l < it.count ? s_q[l] : -1; };
+  };
+  // the next group's query rows are fetched while the current one computes
+  Frag<T> qnx[IB][D / 32];
+  if (wave < ngroups) load_queries<T, D, IB>(qnx, Qh, lg, group_rows(wave));
   for (int gi = wave; gi < ngroups; gi += NW) {
     Frag<T> qf[IB][D / 32];
     int qn[IB];
+#pragma unroll
+    for (int b = 0; b < IB; ++b) {
+#pragma unroll
+      for (int dc = 0; dc < D / 32; ++dc) qf[b][dc] = qnx[b][dc];
+      const int l = gi * GQ + b * 16 + li;
+      qn[b] = l < it.count ? s_q[l] : -1;
+    }
+    if (gi + NW < ngroups) load_queries<T, D, IB>(qnx, Qh, lg, group_rows(gi + NW));
     float M[IB], Z[IB];
     f32x4 acc[IB][D / 16];
 #pragma unroll
     for (int b = 0; b < IB; ++b) {
-      const int local = gi * GQ + b * 16 + li;
-      qn[b] = local < it.count ? perm[it.start + local] : -1;
-#pragma unroll
-      for (int dc = 0; dc < D / 32; ++dc) {
-        if (qn[b] >= 0) load8(qf[b][dc], Q + ((size_t)bh * N + qn[b]) * D + dc * 32 + 8 * lg);
-        else zero(qf[b][dc]);
-      }
       M[b] = M0;
       Z[b] = 0.f;
 #pragma unroll
@@ -363,7 +430,8 @@ void launch_route_shared(const Plan& p) {
 
 template <typename T, int D, int NW, int IB>
 static void launch_expert_t(const Plan& p) {
-  const size_t lds = resident_bytes(p.dtype, D, p.k);
+  const int Kp = (p.k + 31) / 32 * 32;
+  const size_t lds = resident_bytes(p.dtype, D, p.k) + (size_t)(Kp + p.T) * 4;
   auto fn = &k_expert<T, D, NW, IB>;
   if (lds > 65536)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
