@@ -37,6 +37,7 @@ __global__ __launch_bounds__(NW * 64) void k_attend(
   const WorkItem it = wl[blockIdx.x];
   const int bh = it.be / m;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, li = lane % 16, lg = lane / 16;
+  const Frag<T> one = ones_frag<T>(li);
   const T* Kh = K + (size_t)bh * N * D;
   const T* Vh = V + (size_t)bh * N * D;
   const T* Qth = Qt + (size_t)bh * m * D;
@@ -45,7 +46,8 @@ __global__ __launch_bounds__(NW * 64) void k_attend(
 
   Frag<T> qf[IB][D / 32];
   int qn[IB];
-  float M[IB], Z[IB];
+  float M[IB];
+  f32x4 Z[IB];
   f32x4 acc[IB][D / 16];
 #pragma unroll
   for (int b = 0; b < IB; ++b) {
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(NW * 64) void k_attend(
       else zero(qf[b][dc]);
     }
     M[b] = M0;
-    Z[b] = 0.f;
+    Z[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cb = 0; cb < D / 16; ++cb) acc[b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -96,15 +98,15 @@ __global__ __launch_bounds__(NW * 64) void k_attend(
     f.load_keys(cur, li, lg);
     f.load_vals(cur + TL::K_ELEMS, li, lg);
     const int nv = min(32, ne - x0);
-    if (nv == 32) attn_step<IB, false>(f, qf, nv, lg, cscale, M, Z, acc, NoHook{});
-    else attn_step<IB, true>(f, qf, nv, lg, cscale, M, Z, acc, NoHook{});
+    if (nv == 32) attn_step<IB, false>(f, one, qf, nv, lg, cscale, M, Z, acc, NoHook{});
+    else attn_step<IB, true>(f, one, qf, nv, lg, cscale, M, Z, acc, NoHook{});
     if (more) ld.store(nxt, nxt + TL::K_ELEMS);
     __syncthreads();
   }
 
 #pragma unroll
   for (int b = 0; b < IB; ++b) {
-    float Zt = wave_sum_groups(Z[b]);
+    float Zt = finish_z(Z[b], li);
     if (qn[b] < 0) continue;
     const size_t qrow = (size_t)bh * N + qn[b];
     if constexpr (!SLOT0) {

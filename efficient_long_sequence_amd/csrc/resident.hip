@@ -174,6 +174,7 @@ __global__ __launch_bounds__(NW * 64) void k_route_shared(
   T* Vs = Ks + (size_t)Mp * RL::KS;
   int* hist = (int*)(smem + RL::bytes(Mp));
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, li = lane % 16, lg = lane / 16;
+  const Frag<T> one = ones_frag<T>(li);
   const int bh = blockIdx.y;
   const int q0 = blockIdx.x * qpw, q1 = min(N, q0 + qpw);
   const T* Qh = Q + (size_t)bh * N * D;
@@ -198,7 +199,8 @@ __global__ __launch_bounds__(NW * 64) void k_route_shared(
 #pragma unroll
       for (int dc = 0; dc < D / 32; ++dc) qf[b][dc] = qn[b][dc];
     if (gi + NW < ngroups) load_queries<T, D, 4>(qn, Qh, lg, group_rows(gi + NW));
-    float lv[4][SMAX], M[4], Z[4];
+    float lv[4][SMAX], M[4];
+    f32x4 Z[4];
     int lx[4][SMAX];
     f32x4 acc[4][D / 16];
 #pragma unroll
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(NW * 64) void k_route_shared(
 #pragma unroll
       for (int t = 0; t < SMAX; ++t) { lv[b][t] = -INFINITY; lx[b][t] = 0x7FFFFFFF; }
       M[b] = M0;
-      Z[b] = 0.f;
+      Z[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int cb = 0; cb < D / 16; ++cb) acc[b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -221,12 +223,12 @@ __global__ __launch_bounds__(NW * 64) void k_route_shared(
     for (; x0 + 32 <= m; x0 += 32) {
       StepFrags<T, D> f;
       RL::frags(f, Ks, Vs, Mp, x0, li, lg);
-      attn_step<4, false>(f, qf, 32, lg, cscale, M, Z, acc, topsel);
+      attn_step<4, false>(f, one, qf, 32, lg, cscale, M, Z, acc, topsel);
     }
     if (x0 < m) {
       StepFrags<T, D> f;
       RL::frags(f, Ks, Vs, Mp, x0, li, lg);
-      attn_step<4, true>(f, qf, m - x0, lg, cscale, M, Z, acc, topsel);
+      attn_step<4, true>(f, one, qf, m - x0, lg, cscale, M, Z, acc, topsel);
     }
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
@@ -239,7 +241,7 @@ __global__ __launch_bounds__(NW * 64) void k_route_shared(
 #pragma unroll
         for (int t = 0; t < SMAX; ++t) list_insert<SMAX>(lv[b], lx[b], ov[t], ox[t]);
       }
-      const float Zt = wave_sum_groups(Z[b]);
+      const float Zt = finish_z(Z[b], li);
       const int n = qb + b * 16 + li;
       if (n >= q1) continue;
       const size_t qrow = (size_t)bh * N + n;
@@ -301,6 +303,7 @@ __global__ __launch_bounds__(NW * 64) void k_expert(
   T* Ks = (T*)smem;
   T* Vs = Ks + (size_t)Kp * RL::KS;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, li = lane % 16, lg = lane / 16;
+  const Frag<T> one = ones_frag<T>(li);
   const int bh = it.be / m;
   const T* Kh = K + (size_t)bh * N * D;
   const T* Vh = V + (size_t)bh * N * D;
@@ -335,12 +338,13 @@ __global__ __launch_bounds__(NW * 64) void k_expert(
       qn[b] = l < it.count ? s_q[l] : -1;
     }
     if (gi + NW < ngroups) load_queries<T, D, IB>(qnx, Qh, lg, group_rows(gi + NW));
-    float M[IB], Z[IB];
+    float M[IB];
+  f32x4 Z[IB];
     f32x4 acc[IB][D / 16];
 #pragma unroll
     for (int b = 0; b < IB; ++b) {
       M[b] = M0;
-      Z[b] = 0.f;
+      Z[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int cb = 0; cb < D / 16; ++cb) acc[b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -348,16 +352,16 @@ __global__ __launch_bounds__(NW * 64) void k_expert(
     for (; x0 + 32 <= k; x0 += 32) {
       StepFrags<T, D> f;
       RL::frags(f, Ks, Vs, Kp, x0, li, lg);
-      attn_step<IB, false>(f, qf, 32, lg, cscale, M, Z, acc, NoHook{});
+      attn_step<IB, false>(f, one, qf, 32, lg, cscale, M, Z, acc, NoHook{});
     }
     if (x0 < k) {
       StepFrags<T, D> f;
       RL::frags(f, Ks, Vs, Kp, x0, li, lg);
-      attn_step<IB, true>(f, qf, k - x0, lg, cscale, M, Z, acc, NoHook{});
+      attn_step<IB, true>(f, one, qf, k - x0, lg, cscale, M, Z, acc, NoHook{});
     }
 #pragma unroll
     for (int b = 0; b < IB; ++b) {
-      const float Zt = wave_sum_groups(Z[b]);
+      const float Zt = finish_z(Z[b], li);
       if (qn[b] < 0) continue;
       const size_t qrow = (size_t)bh * N + qn[b];
       // merge with the stored partial: weights 2^lse of the two parts

@@ -146,6 +146,7 @@ __global__ __launch_bounds__(NW * 64) void k_score(
   int* s_ncand = s_rowbase + R;
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, li = lane % 16, lg = lane / 16;
+  const Frag<T> one = ones_frag<T>(li);
   const int ch = blockIdx.x, rt = blockIdx.y, bh = blockIdx.z;
   const int rbase = rt * R + wave * 16 * IB;
   const T* Kh = K + (size_t)bh * N * D;
@@ -158,7 +159,8 @@ __global__ __launch_bounds__(NW * 64) void k_score(
   }
 
   Frag<T> qf[IB][D / 32];
-  float M[IB], Z[IB], tau[IB];
+  float M[IB], tau[IB];
+  f32x4 Z[IB];
   f32x4 acc[IB][D / 16];
 #pragma unroll
   for (int b = 0; b < IB; ++b) {
@@ -171,7 +173,7 @@ __global__ __launch_bounds__(NW * 64) void k_score(
     }
     M[b] = (mhat_in != nullptr && valid) ? mhat_in[(size_t)bh * m + row] * cscale : M0;
     tau[b] = DENSE ? -INFINITY : (valid ? tau_in[(size_t)bh * m + row] : INFINITY);
-    Z[b] = 0.f;
+    Z[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cb = 0; cb < D / 16; ++cb) acc[b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -236,8 +238,8 @@ __global__ __launch_bounds__(NW * 64) void k_score(
         }
       }
     };
-    if (nv == 32) attn_step<IB, false>(f, qf, nv, lg, cscale, M, Z, acc, cands);
-    else attn_step<IB, true>(f, qf, nv, lg, cscale, M, Z, acc, cands);
+    if (nv == 32) attn_step<IB, false>(f, one, qf, nv, lg, cscale, M, Z, acc, cands);
+    else attn_step<IB, true>(f, one, qf, nv, lg, cscale, M, Z, acc, cands);
     if (more) ld.store(nxt, nxt + TL::K_ELEMS);
     __syncthreads();
   }
@@ -245,7 +247,7 @@ __global__ __launch_bounds__(NW * 64) void k_score(
   // partial shared values of this chunk: (max, normaliser, 2 pad, unnormalised sums)
 #pragma unroll
   for (int b = 0; b < IB; ++b) {
-    const float Zt = wave_sum_groups(Z[b]);
+    const float Zt = finish_z(Z[b], li);
     const int row = rbase + b * 16 + li;
     if (row < m) {
       float* dst = vpart + (((size_t)bh * m + row) * C + ch) * (D + 4);

@@ -139,13 +139,27 @@ __device__ __forceinline__ void step_scores(const StepFrags<T, D>& f, const Frag
   for (int r = 0; r < 4; ++r) { sc[r] = s0[r]; sc[4 + r] = s1[r]; }
 }
 
+// A-operand block whose first row is all ones: multiplied with the
+// probability fragment it yields the softmax normaliser on the matrix cores
+// (row 0 of the output tile, i.e. element 0 in lane group 0), summing the
+// same rounded probabilities the P.V product uses.
+template <typename T>
+__device__ __forceinline__ Frag<T> ones_frag(int li) {
+  Frag<T> f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) f.v[t] = (T)(li == 0 ? 1.0f : 0.0f);
+  return f;
+}
+// The normaliser of query li (held by lane li of group 0), in every lane.
+__device__ __forceinline__ float finish_z(const f32x4& Z, int li) { return __shfl(Z[0], li); }
+
 // Online-softmax update of one 16-query block with the 8 raw scores of this
 // lane (already -inf where masked).  M is the running maximum in the scaled
-// log2 domain (identical in the four lane groups of a query), Z this lane's
-// share of the normaliser, acc the O^T accumulator.
+// log2 domain (identical in the four lane groups of a query), Z the
+// normaliser tile (see ones_frag), acc the O^T accumulator.
 template <typename T, int D>
-__device__ __forceinline__ void softmax_step(const StepFrags<T, D>& f, const float* sc, float mx_raw,
-                                             float cscale, float& M, float& Z, f32x4* acc) {
+__device__ __forceinline__ void softmax_step(const StepFrags<T, D>& f, const Frag<T>& one, const float* sc,
+                                             float mx_raw, float cscale, float& M, f32x4& Z, f32x4* acc) {
   const float xm = mx_raw * cscale;
   if (wave_any(xm > M + THRESH)) {
     // The decision uses the query's own maximum over its four lane groups,
@@ -154,7 +168,7 @@ __device__ __forceinline__ void softmax_step(const StepFrags<T, D>& f, const flo
     const float gm = wave_max_groups(xm);
     if (gm > M + THRESH) {
       const float alpha = __builtin_amdgcn_exp2f(M - gm);
-      Z *= alpha;
+      Z[0] *= alpha;
 #pragma unroll
       for (int cb = 0; cb < D / 16; ++cb)
 #pragma unroll
@@ -166,16 +180,151 @@ __device__ __forceinline__ void softmax_step(const StepFrags<T, D>& f, const flo
   float p[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t], cscale, nm));
-  Z += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
   Frag<T> pf;
   set8(pf, p);
 #pragma unroll
   for (int cb = 0; cb < D / 16; ++cb) mma16(acc[cb], f.va[cb], pf);
+  mma16(Z, one, pf);
 }
 
+
+// chained so the compiler forms three-input maxima (v_max3_f32)
 __device__ __forceinline__ float max8(const float* s) {
-  return fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+  float m = fmaxf(fmaxf(s[0], s[1]), s[2]);
+  m = fmaxf(fmaxf(m, s[3]), s[4]);
+  m = fmaxf(fmaxf(m, s[5]), s[6]);
+  return fmaxf(m, s[7]);
 }
+
+// Key and value operands of one 32-entry step, loaded separately so a
+// pipelined loop can hold the next step's keys beside the current values.
+template <typename T, int D>
+struct KFrags {
+  Frag<T> ka[2][D / 32];
+};
+template <typename T, int D>
+struct VFrags {
+  Frag<T> va[D / 16];
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void tile_scores(const KFrags<T, D>& kf, const Frag<T>* qf, float* sc) {
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int dc = 0; dc < D / 32; ++dc) {
+    mma16(s0, kf.ka[0][dc], qf[dc]);
+    mma16(s1, kf.ka[1][dc], qf[dc]);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) { sc[r] = s0[r]; sc[4 + r] = s1[r]; }
+}
+
+// Raise block b's running maximum when its own maximum exceeds it by more
+// than THRESH binades (rescaling the normaliser and accumulator).
+template <int D>
+__device__ __forceinline__ void rescale_if_needed(float xm, float& M, f32x4& Z, f32x4* acc) {
+  const float gm = wave_max_groups(xm);
+  if (gm > M + THRESH) {
+    const float alpha = __builtin_amdgcn_exp2f(M - gm);
+    Z[0] *= alpha;
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[cb][r] *= alpha;
+    M = gm;
+  }
+}
+
+// Probabilities of one block (no rescale check) and their P.V product.
+template <typename T, int D>
+__device__ __forceinline__ void probs_pv(const Frag<T>* va, const Frag<T>& one, const float* sc, float cscale,
+                                         float M, f32x4& Z, f32x4* acc) {
+  const float nm = -M;
+  float p[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t], cscale, nm));
+  Frag<T> pf;
+  set8(pf, p);
+#pragma unroll
+  for (int cb = 0; cb < D / 16; ++cb) mma16(acc[cb], va[cb], pf);
+  mma16(Z, one, pf);
+}
+
+// Whole pass over E resident entries, software-pipelined: each step first
+// runs the short branchy part for all row blocks (maxima, the hook
+// on(b, scores, lane max, x0), one rescale check), then one straight-line
+// section where block b's score tile of the next step goes to the matrix
+// cores while the vector units turn block b's current scores into
+// probabilities.  With no branch inside it the compiler interleaves the two
+// units within a wave.  loadk(kf, x0) / loadv(vf, x0) fetch the operands of
+// the step at entry x0.
+template <int IB, typename T, int D, class LK, class LV, class On>
+__device__ __forceinline__ void attn_run(LK loadk, LV loadv, int E, const Frag<T>& one,
+                                         const Frag<T> (&qf)[IB][D / 32], int lg, float cscale, float (&M)[IB],
+                                         f32x4 (&Z)[IB], f32x4 (&acc)[IB][D / 16], On on) {
+  const int nsteps = (E + 31) / 32;
+  KFrags<T, D> kf;
+  loadk(kf, 0);
+  float sc[IB][8];
+#pragma unroll
+  for (int b = 0; b < IB; ++b) tile_scores(kf, qf[b], sc[b]);
+  for (int st = 0; st < nsteps; ++st) {
+    const int x0 = st * 32;
+    const bool last = st + 1 == nsteps;
+    VFrags<T, D> vf;
+    loadv(vf, x0);
+    if (last) {
+      const int nv = E - x0;
+      if (nv < 32) {
+#pragma unroll
+        for (int b = 0; b < IB; ++b)
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            if (slot_key(t, lg) >= nv) sc[b][t] = -INFINITY;
+      }
+    } else {
+      loadk(kf, x0 + 32);
+    }
+    float xm[IB];
+    bool need = false;
+#pragma unroll
+    for (int b = 0; b < IB; ++b) {
+      const float mx = max8(sc[b]);
+      on(b, sc[b], mx, x0);
+      xm[b] = mx * cscale;
+      need |= xm[b] > M[b] + THRESH;
+    }
+    if (wave_any(need)) {
+#pragma unroll
+      for (int b = 0; b < IB; ++b) rescale_if_needed<D>(xm[b], M[b], Z[b], acc[b]);
+    }
+    if (!last) {
+#pragma unroll
+      for (int b = 0; b < IB; ++b) {
+        float cur[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) cur[t] = sc[b][t];
+        tile_scores(kf, qf[b], sc[b]);
+        probs_pv<T, D>(vf.va, one, cur, cscale, M[b], Z[b], acc[b]);
+      }
+      // ask the scheduler to alternate one matrix instruction with three
+      // vector instructions over the section
+      constexpr int NMFMA = IB * (2 * (D / 32) * (sizeof(T) == 2 ? 1 : 8) + (D / 16 + 1) * (sizeof(T) == 2 ? 1 : 8));
+#pragma unroll
+      for (int i = 0; i < NMFMA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < IB; ++b) probs_pv<T, D>(vf.va, one, sc[b], cscale, M[b], Z[b], acc[b]);
+    }
+  }
+}
+
+struct NoHook4 {
+  __device__ __forceinline__ void operator()(int, const float*, float, int) const {}
+};
 
 // One 32-entry step for IB blocks of 16 queries: the score tiles of all
 // blocks first (so one block's softmax overlaps the others' matrix work),
@@ -183,9 +332,9 @@ __device__ __forceinline__ float max8(const float* s) {
 // and the online-softmax update with P.V.  MASK marks the last, partial step:
 // entries at offsets >= nv get score -inf.
 template <int IB, bool MASK, typename T, int D, class On>
-__device__ __forceinline__ void attn_step(const StepFrags<T, D>& f, const Frag<T> (&qf)[IB][D / 32], int nv, int lg,
-                                          float cscale, float (&M)[IB], float (&Z)[IB], f32x4 (&acc)[IB][D / 16],
-                                          On on) {
+__device__ __forceinline__ void attn_step(const StepFrags<T, D>& f, const Frag<T>& one,
+                                          const Frag<T> (&qf)[IB][D / 32], int nv, int lg, float cscale,
+                                          float (&M)[IB], f32x4 (&Z)[IB], f32x4 (&acc)[IB][D / 16], On on) {
   float sc[IB][8];
 #pragma unroll
   for (int b = 0; b < IB; ++b) step_scores(f, qf[b], sc[b]);
@@ -200,7 +349,7 @@ __device__ __forceinline__ void attn_step(const StepFrags<T, D>& f, const Frag<T
   for (int b = 0; b < IB; ++b) {
     const float mx = max8(sc[b]);
     on(b, sc[b], mx);
-    softmax_step(f, sc[b], mx, cscale, M[b], Z[b], acc[b]);
+    softmax_step(f, one, sc[b], mx, cscale, M[b], Z[b], acc[b]);
   }
 }
 
