@@ -85,10 +85,11 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
     const long long est_target = 512;
     int gpb = ceil_div((long long)p.G * p.BH * p.sc_rt, est_target);
     p.est_gpb = gpb < 1 ? 1 : gpb;
-    // staged candidates per workgroup: the threshold admits about 2.5 k keys per row
+    // staged candidates per workgroup (split evenly over its waves): the
+    // threshold admits about 2.5 k keys per row; room for three times that
     const double expect = (double)p.sc_R * p.L * (2.5 * k / N);
     int cb = 256;
-    while (cb < 1.5 * expect && cb < 8192) cb <<= 1;
+    while (cb < 3.0 * expect && cb < 16384) cb <<= 1;
     p.cb = cb;
     // Test hook (host-forced): MITA_TEST_FORCE_FALLBACK=1 sets every candidate
     // threshold to +inf, so no row collects candidates and every row is

@@ -35,6 +35,13 @@ typedef _Float16 f16;
 template <typename T> struct PartT { typedef f16 type; };
 template <> struct PartT<float> { typedef float type; };
 
+// Row layout of the finished-part output: lane group g of a query holds
+// output dims cb*16 + 4g + r (cb < D/16, r < 4) in its accumulator tiles, and
+// stores them as one contiguous run at positions g*D/4 + cb*4 + r, so the
+// four lane groups of a query write (and later read) the whole row.
+template <int D>
+__device__ __forceinline__ int part_pos(int g, int cb) { return g * (D / 4) + cb * 4; }
+
 template <typename P> struct Vec4;
 template <> struct Vec4<f16> { typedef __attribute__((__vector_size__(4 * sizeof(f16)))) f16 type; };
 template <> struct Vec4<float> { typedef __attribute__((__vector_size__(4 * sizeof(float)))) float type; };
@@ -215,10 +222,22 @@ __global__ __launch_bounds__(NW * 64) void k_route_shared(
     int x0 = 0;
     // landmarks reach a lane in increasing order: strict '>' keeps the lower
     // index on ties
-    auto topsel = [&](int b, const float* sc, float) {
+    auto topsel = [&](int b, const float* sc, float mx) {
+      if constexpr (SMAX == 1) {
+        // top-1: the first of this lane's slots holding its maximum (slots
+        // ascend with the landmark index), taken when it beats the best so far
+        int tf = 7;
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-        if (sc[t] > lv[b][SMAX - 1]) list_insert<SMAX>(lv[b], lx[b], sc[t], x0 + slot_key(t, lg));
+        for (int t = 6; t >= 0; --t) tf = sc[t] == mx ? t : tf;
+        if (mx > lv[b][0]) {
+          lv[b][0] = mx;
+          lx[b][0] = x0 + 4 * lg + tf + (tf >= 4 ? 12 : 0);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          if (sc[t] > lv[b][SMAX - 1]) list_insert<SMAX>(lv[b], lx[b], sc[t], x0 + slot_key(t, lg));
+      }
     };
     for (; x0 + 32 <= m; x0 += 32) {
       StepFrags<T, D> f;
@@ -267,7 +286,7 @@ __global__ __launch_bounds__(NW * 64) void k_route_shared(
         PV h;
 #pragma unroll
         for (int r = 0; r < 4; ++r) h[r] = (P)(acc[b][cb][r] * inv);
-        *(PV*)(o + cb * 16 + 4 * lg) = h;
+        *(PV*)(o + part_pos<D>(lg, cb)) = h;
       }
     }
   }
@@ -374,7 +393,7 @@ __global__ __launch_bounds__(NW * 64) void k_expert(
       P* o = po + qrow * D;
 #pragma unroll
       for (int cb = 0; cb < D / 16; ++cb) {
-        const PV h = *(const PV*)(o + cb * 16 + 4 * lg);
+        const PV h = *(const PV*)(o + part_pos<D>(lg, cb));
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = ca * (float)h[r] + cb_ * acc[b][cb][r];
@@ -386,7 +405,7 @@ __global__ __launch_bounds__(NW * 64) void k_expert(
           PV w;
 #pragma unroll
           for (int r = 0; r < 4; ++r) w[r] = (P)v[r];
-          *(PV*)(o + cb * 16 + 4 * lg) = w;
+          *(PV*)(o + part_pos<D>(lg, cb)) = w;
         }
       }
       if (!last && lg == 0) plse[qrow] = mx + __builtin_amdgcn_logf(den);

@@ -128,8 +128,13 @@ __global__ __launch_bounds__(256) void k_tau(const float* __restrict__ gmax, flo
 // ---------------------------------------------------------------------------
 // fused scores, partial shared values and candidates
 // ---------------------------------------------------------------------------
+// Waves per SIMD the register budget must allow: the 16-row bf16 tiling keeps
+// two 8-wave workgroups per CU.
+template <typename T, int NW, int IB>
+constexpr int score_waves_per_eu() { return (sizeof(T) == 2 && NW == 8 && IB == 1) ? 4 : 2; }
+
 template <typename T, int D, int NW, int IB, bool DENSE>
-__global__ __launch_bounds__(NW * 64) void k_score(
+__global__ __launch_bounds__(NW * 64, (score_waves_per_eu<T, NW, IB>())) void k_score(
     const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ Qt,
     const float* __restrict__ tau_in, const float* __restrict__ mhat_in, float* __restrict__ vpart,
     uint64_t* __restrict__ cand, int* __restrict__ cand_cnt, int N, int m, int L, int C, int capg,
@@ -143,7 +148,7 @@ __global__ __launch_bounds__(NW * 64) void k_score(
   uint2* s_cand = (uint2*)(smem + 2 * TL::ELEMS * sizeof(T));
   int* s_rowcnt = (int*)(s_cand + cb_cap);
   int* s_rowbase = s_rowcnt + R;
-  int* s_ncand = s_rowbase + R;
+  int* s_wcnt = s_rowbase + R;  // staged entries per wave
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, li = lane % 16, lg = lane / 16;
   const Frag<T> one = ones_frag<T>(li);
@@ -152,10 +157,14 @@ __global__ __launch_bounds__(NW * 64) void k_score(
   const T* Kh = K + (size_t)bh * N * D;
   const T* Vh = V + (size_t)bh * N * D;
   const int j_begin = ch * L, j_end = min(N, j_begin + L);
+  // each wave stages its candidates in its own LDS segment, counted in a
+  // wave-uniform register, so no LDS atomics sit on the inner loop
+  const int seg = cb_cap / NW;
+  uint2* w_cand = s_cand + wave * seg;
+  int wcnt = 0;
 
   if constexpr (!DENSE) {
     for (int r = tid; r < R; r += NT) s_rowcnt[r] = 0;
-    if (tid == 0) *s_ncand = 0;
   }
 
   Frag<T> qf[IB][D / 32];
@@ -214,28 +223,31 @@ __global__ __launch_bounds__(NW * 64) void k_score(
           }
         }
       } else if (wave_any(mx >= tau[b])) {
-        uint32_t msk = 0;
+        // one ballot per key slot: the hits of a slot take the next entries
+        // of the wave's segment in lane order, and each hit's score comes
+        // straight from its register
+        const uint32_t rl = (uint32_t)(row - rt * R) << 23;
+        const float tb = tau[b];
+        int off = wcnt;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) msk |= (sc[t] >= tau[b] ? 1u : 0u) << t;
-        if (msk) {
-          int e = atomicAdd(s_ncand, __builtin_popcount(msk));
-          const uint32_t rl = (uint32_t)(row - rt * R) << 23;
-          while (msk) {
-            const int t = __builtin_ctz(msk);
-            msk &= msk - 1;
-            float v = sc[0];
-#pragma unroll
-            for (int u = 1; u < 8; ++u) v = (t == u) ? sc[u] : v;
+        for (int t = 0; t < 8; ++t) {
+          const bool hit = sc[t] >= tb;
+          const uint64_t bal = __builtin_amdgcn_ballot_w64(hit);
+          if (bal == 0) continue;
+          if (hit) {
+            const int e = off + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
             const int jl = j0 + slot_key(t, lg) - j_begin;
-            if (e < cb_cap) {
-              s_cand[e] = make_uint2(__float_as_uint(v), rl | (uint32_t)jl);
+            if (e < seg) {
+              w_cand[e] = make_uint2(__float_as_uint(sc[t]), rl | (uint32_t)jl);
             } else {
               const int pos = atomicAdd(cand_cnt + (size_t)bh * m + row, 1);
-              if (pos < capg) cand[((size_t)bh * m + row) * capg + pos] = ckey(v, (uint32_t)(j_begin + jl));
+              if (pos < capg) cand[((size_t)bh * m + row) * capg + pos] = ckey(sc[t], (uint32_t)(j_begin + jl));
             }
-            ++e;
           }
+          off += (int)__builtin_popcountll(bal);
         }
+        wcnt = off;
       }
     };
     if (nv == 32) attn_step<IB, false>(f, one, qf, nv, lg, cscale, M, Z, acc, cands);
@@ -259,8 +271,12 @@ __global__ __launch_bounds__(NW * 64) void k_score(
   }
 
   if constexpr (!DENSE) {
-    const int ns = min(*s_ncand, cb_cap);
-    for (int e = tid; e < ns; e += NT) atomicAdd(s_rowcnt + (s_cand[e].y >> 23), 1);
+    if (lane == 0) s_wcnt[wave] = min(wcnt, seg);
+    __syncthreads();
+    const int ns = NW * seg;
+    auto staged = [&](int e) { return e - (e / seg) * seg < s_wcnt[e / seg]; };
+    for (int e = tid; e < ns; e += NT)
+      if (staged(e)) atomicAdd(s_rowcnt + (s_cand[e].y >> 23), 1);
     __syncthreads();
     for (int r = tid; r < R; r += NT) {
       const int row = rt * R + r, c = s_rowcnt[r];
@@ -269,6 +285,7 @@ __global__ __launch_bounds__(NW * 64) void k_score(
     }
     __syncthreads();
     for (int e = tid; e < ns; e += NT) {
+      if (!staged(e)) continue;
       const uint2 v = s_cand[e];
       const int r = (int)(v.y >> 23), row = rt * R + r;
       const int pos = s_rowbase[r] + atomicAdd(s_rowcnt + r, 1);
@@ -423,7 +440,7 @@ static void launch_score_main(const Plan& p) {
   using TL = TileLayout<T, D>;
   constexpr int R = NW * 16 * IB;
   const bool dense = p.dense != 0;
-  const size_t lds = 2 * TL::ELEMS * sizeof(T) + (dense ? 0 : (size_t)p.cb * 8 + 2 * R * 4 + 16);
+  const size_t lds = 2 * TL::ELEMS * sizeof(T) + (dense ? 0 : (size_t)p.cb * 8 + 2 * R * 4 + NW * 4);
   dim3 grid((unsigned)p.C, (unsigned)p.sc_rt, (unsigned)p.BH);
   if (dense) {
     hipLaunchKernelGGL((k_score<T, D, NW, IB, true>), grid, dim3(NW * 64), lds, p.stream, (const T*)p.K,
