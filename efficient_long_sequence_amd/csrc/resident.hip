@@ -300,24 +300,97 @@ __global__ __launch_bounds__(NW * 64) void k_route_shared(
 }
 
 // ---------------------------------------------------------------------------
+// One group of IB blocks of 16 queries (query rows qn[b], -1 for an empty
+// slot) against the expert's k resident entries, merged with the stored
+// finished part.
+template <int IB, typename T, int D>
+__device__ __forceinline__ void expert_group(const Frag<T> (&qf)[IB][D / 32], const int (&qn)[IB], const T* Ks,
+                                             const T* Vs, int Kp, int k, const Frag<T>& one, size_t row0,
+                                             float* __restrict__ plse, typename PartT<T>::type* __restrict__ po,
+                                             T* __restrict__ O, int last, float cscale, int li, int lg) {
+  using RL = Resident<T, D>;
+  using P = typename PartT<T>::type;
+  using PV = typename Vec4<P>::type;
+  float M[IB];
+  f32x4 Z[IB];
+  f32x4 acc[IB][D / 16];
+#pragma unroll
+  for (int b = 0; b < IB; ++b) {
+    M[b] = M0;
+    Z[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb) acc[b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  int x0 = 0;
+  for (; x0 + 32 <= k; x0 += 32) {
+    StepFrags<T, D> f;
+    RL::frags(f, Ks, Vs, Kp, x0, li, lg);
+    attn_step<IB, false>(f, one, qf, 32, lg, cscale, M, Z, acc, NoHook{});
+  }
+  if (x0 < k) {
+    StepFrags<T, D> f;
+    RL::frags(f, Ks, Vs, Kp, x0, li, lg);
+    attn_step<IB, true>(f, one, qf, k - x0, lg, cscale, M, Z, acc, NoHook{});
+  }
+#pragma unroll
+  for (int b = 0; b < IB; ++b) {
+    const float Zt = finish_z(Z[b], li);
+    if (qn[b] < 0) continue;
+    const size_t qrow = row0 + qn[b];
+    // merge with the stored partial: weights 2^lse of the two parts
+    const float la = plse[qrow];
+    const float lb = M[b] + __builtin_amdgcn_logf(Zt);
+    const float mx = fmaxf(la, lb);
+    const float wa = __builtin_amdgcn_exp2f(la - mx), wb = __builtin_amdgcn_exp2f(lb - mx);
+    const float den = wa + wb;
+    const float ca = wa / den, cb_ = wb / (den * Zt);
+    P* o = po + qrow * D;
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb) {
+      const PV h = *(const PV*)(o + part_pos<D>(lg, cb));
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = ca * (float)h[r] + cb_ * acc[b][cb][r];
+      if (last) {
+        T* dst = O + qrow * D + cb * 16 + 4 * lg;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[r] = from_f32<T>(v[r]);
+      } else {
+        PV w;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r] = (P)v[r];
+        *(PV*)(o + part_pos<D>(lg, cb)) = w;
+      }
+    }
+    if (!last && lg == 0) plse[qrow] = mx + __builtin_amdgcn_logf(den);
+  }
+}
+
+template <int IBX, typename T, int D, class QR>
+__device__ __forceinline__ void expert_blocks(const T* Qh, QR qrow, const T* Ks, const T* Vs, int Kp, int k,
+                                              const Frag<T>& one, size_t row0, float* plse,
+                                              typename PartT<T>::type* po, T* O, int last, float cscale, int li,
+                                              int lg) {
+  Frag<T> qf[IBX][D / 32];
+  int qn[IBX];
+  load_queries<T, D, IBX>(qf, Qh, lg, qrow);
+#pragma unroll
+  for (int b = 0; b < IBX; ++b) qn[b] = (int)qrow(b);
+  expert_group<IBX, T, D>(qf, qn, Ks, Vs, Kp, k, one, row0, plse, po, O, last, cscale, li, lg);
+}
+
 template <typename T, int D, int NW, int IB>
-__global__ __launch_bounds__(NW * 64) void k_expert(
+__global__ __launch_bounds__(NW * 64, 2) void k_expert(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const int32_t* __restrict__ topk,
     const int32_t* __restrict__ perm, const WorkItem* __restrict__ wl, const int* __restrict__ wl_count,
     float* __restrict__ plse, typename PartT<T>::type* __restrict__ po, T* __restrict__ O, int N, int m, int k,
     int last, float cscale) {
   using RL = Resident<T, D>;
-  using P = typename PartT<T>::type;
-  using PV = typename Vec4<P>::type;
   extern __shared__ __align__(16) unsigned char smem[];
-  // Work items of one expert are consecutive in the list; hand each XCD (the
-  // hardware places workgroup i on XCD i mod 8) one contiguous eighth of the
-  // list so an expert's tiles share that XCD's L2.
-  const int nwl = *wl_count;
-  const int seg = (nwl + 7) / 8;
-  const int item = (int)(blockIdx.x % 8) * seg + (int)(blockIdx.x / 8);
-  if ((int)(blockIdx.x / 8) >= seg || item >= nwl) return;
-  const WorkItem it = wl[item];
+  // The list holds the largest items first; the hardware deals workgroups
+  // to the XCDs in turn, which spreads them evenly.
+  if ((int)blockIdx.x >= *wl_count) return;
+  const WorkItem it = wl[blockIdx.x];
   const int Kp = RL::pad(k);
   T* Ks = (T*)smem;
   T* Vs = Ks + (size_t)Kp * RL::KS;
@@ -338,79 +411,45 @@ __global__ __launch_bounds__(NW * 64) void k_expert(
   __syncthreads();
 
   constexpr int GQ = 16 * IB;
-  const int ngroups = (it.count + GQ - 1) / GQ;
   const T* Qh = Q + (size_t)bh * N * D;
+  const size_t row0 = (size_t)bh * N;
+  // whole rounds of full groups (one per wave) ...
+  const int nfull = it.count / (NW * GQ) * NW;
   auto group_rows = [&](int gi) {
-    return [=](int b) -> long long { const int l = gi * GQ + b * 16 + li; return l < it.count ? s_q[l] : -1; };
+    return [=](int b) -> long long { return s_q[gi * GQ + b * 16 + li]; };
   };
   // the next group's query rows are fetched while the current one computes
   Frag<T> qnx[IB][D / 32];
-  if (wave < ngroups) load_queries<T, D, IB>(qnx, Qh, lg, group_rows(wave));
-  for (int gi = wave; gi < ngroups; gi += NW) {
+  if (wave < nfull) load_queries<T, D, IB>(qnx, Qh, lg, group_rows(wave));
+  for (int gi = wave; gi < nfull; gi += NW) {
     Frag<T> qf[IB][D / 32];
     int qn[IB];
 #pragma unroll
     for (int b = 0; b < IB; ++b) {
 #pragma unroll
       for (int dc = 0; dc < D / 32; ++dc) qf[b][dc] = qnx[b][dc];
-      const int l = gi * GQ + b * 16 + li;
-      qn[b] = l < it.count ? s_q[l] : -1;
+      qn[b] = s_q[gi * GQ + b * 16 + li];
     }
-    if (gi + NW < ngroups) load_queries<T, D, IB>(qnx, Qh, lg, group_rows(gi + NW));
-    float M[IB];
-  f32x4 Z[IB];
-    f32x4 acc[IB][D / 16];
-#pragma unroll
-    for (int b = 0; b < IB; ++b) {
-      M[b] = M0;
-      Z[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int cb = 0; cb < D / 16; ++cb) acc[b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    int x0 = 0;
-    for (; x0 + 32 <= k; x0 += 32) {
-      StepFrags<T, D> f;
-      RL::frags(f, Ks, Vs, Kp, x0, li, lg);
-      attn_step<IB, false>(f, one, qf, 32, lg, cscale, M, Z, acc, NoHook{});
-    }
-    if (x0 < k) {
-      StepFrags<T, D> f;
-      RL::frags(f, Ks, Vs, Kp, x0, li, lg);
-      attn_step<IB, true>(f, one, qf, k - x0, lg, cscale, M, Z, acc, NoHook{});
-    }
-#pragma unroll
-    for (int b = 0; b < IB; ++b) {
-      const float Zt = finish_z(Z[b], li);
-      if (qn[b] < 0) continue;
-      const size_t qrow = (size_t)bh * N + qn[b];
-      // merge with the stored partial: weights 2^lse of the two parts
-      const float la = plse[qrow];
-      const float lb = M[b] + __builtin_amdgcn_logf(Zt);
-      const float mx = fmaxf(la, lb);
-      const float wa = __builtin_amdgcn_exp2f(la - mx), wb = __builtin_amdgcn_exp2f(lb - mx);
-      const float den = wa + wb;
-      const float ca = wa / den, cb_ = wb / (den * Zt);
-      P* o = po + qrow * D;
-#pragma unroll
-      for (int cb = 0; cb < D / 16; ++cb) {
-        const PV h = *(const PV*)(o + part_pos<D>(lg, cb));
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = ca * (float)h[r] + cb_ * acc[b][cb][r];
-        if (last) {
-          T* dst = O + qrow * D + cb * 16 + 4 * lg;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) dst[r] = from_f32<T>(v[r]);
-        } else {
-          PV w;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) w[r] = (P)v[r];
-          *(PV*)(o + part_pos<D>(lg, cb)) = w;
-        }
-      }
-      if (!last && lg == 0) plse[qrow] = mx + __builtin_amdgcn_logf(den);
-    }
+    if (gi + NW < nfull) load_queries<T, D, IB>(qnx, Qh, lg, group_rows(gi + NW));
+    expert_group<IB, T, D>(qf, qn, Ks, Vs, Kp, k, one, row0, plse, po, O, last, cscale, li, lg);
   }
+  // ... then the rest in blocks of 16 queries dealt to the waves in turn, so
+  // a short remainder keeps every wave busy on narrower groups
+  const int r0 = nfull * GQ;
+  const int nblk = (it.count - r0 + 15) / 16;
+  const int mine = nblk > wave ? (nblk - wave + NW - 1) / NW : 0;  // at most IB
+  auto rem_rows = [&](int b) -> long long {
+    const int l = r0 + (wave + b * NW) * 16 + li;
+    return l < it.count ? s_q[l] : -1;
+  };
+  if constexpr (IB >= 4) {
+    if (mine == 4) expert_blocks<4, T, D>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, last, cscale, li, lg);
+    if (mine == 3) expert_blocks<3, T, D>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, last, cscale, li, lg);
+  }
+  if constexpr (IB >= 2) {
+    if (mine == 2) expert_blocks<2, T, D>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, last, cscale, li, lg);
+  }
+  if (mine == 1) expert_blocks<1, T, D>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, last, cscale, li, lg);
 }
 
 // ---------------------------------------------------------------------------

@@ -148,17 +148,32 @@ __global__ __launch_bounds__(NW * 64) void k_route(const T* __restrict__ Q, cons
 
 // Exclusive prefix of the expert counts and the work list, for every slot.
 // One workgroup of 1024 threads; each thread owns a contiguous segment.
+// Work list order: first every item of a full T queries (experts in index
+// order, so an expert's items stay adjacent), then each expert's partial
+// item, larger ones first (a counting sort on the number of 16-query
+// blocks), so the longest items start first and the short ones fill the tail.
+constexpr int SCAN_BUCKETS = 128;  // T <= 2048 queries per item
+
 __global__ __launch_bounds__(1024) void k_scan(const int* __restrict__ counts, int* __restrict__ gpre,
                                                WorkItem* __restrict__ wl, int* __restrict__ wl_count,
                                                int E, int m, int s, int T, int UB) {
   __shared__ int sn[1024], stl[1024];
+  __shared__ int bcnt[SCAN_BUCKETS];
   const int tid = threadIdx.x;
   const int seg = (E + 1023) / 1024;
   const int lo = min(E, tid * seg), hi = min(E, lo + seg);
+  auto bucket = [&](int rem) { return min(SCAN_BUCKETS - 1, (rem + 15) / 16 - 1); };
   for (int t = 0; t < s; ++t) {
     const int* c = counts + (size_t)t * E;
+    if (tid < SCAN_BUCKETS) bcnt[tid] = 0;
+    __syncthreads();
     int n_sum = 0, t_sum = 0;
-    for (int x = lo; x < hi; ++x) { n_sum += c[x]; t_sum += (c[x] + T - 1) / T; }
+    for (int x = lo; x < hi; ++x) {
+      const int n = c[x];
+      n_sum += n;
+      t_sum += n / T;
+      if (n % T) atomicAdd(bcnt + bucket(n % T), 1);
+    }
     sn[tid] = n_sum;
     stl[tid] = t_sum;
     __syncthreads();
@@ -169,20 +184,25 @@ __global__ __launch_bounds__(1024) void k_scan(const int* __restrict__ counts, i
       stl[tid] += b;
       __syncthreads();
     }
+    const int nfull = stl[1023];
+    if (tid == 0) {  // partial items: bucket starts, largest bucket first
+      int acc = nfull;
+      for (int b = SCAN_BUCKETS - 1; b >= 0; --b) {
+        const int n = bcnt[b];
+        bcnt[b] = acc;
+        acc += n;
+      }
+      wl_count[t] = acc;
+    }
+    __syncthreads();
     int nb = sn[tid] - n_sum, tb = stl[tid] - t_sum;
-    if (tid == 1023) wl_count[t] = stl[1023];
     WorkItem* w = wl + (size_t)t * UB;
     for (int x = lo; x < hi; ++x) {
       const int n = c[x];
       gpre[(size_t)t * E + x] = nb;
-      for (int q = 0; q * T < n; ++q) {
-        WorkItem it;
-        it.start = nb + q * T;
-        it.count = min(T, n - q * T);
-        it.be = x;
-        it.pad = 0;
-        w[tb++] = it;
-      }
+      const int nf = n / T;
+      for (int q = 0; q < nf; ++q) w[tb++] = WorkItem{nb + q * T, T, x, 0};
+      if (n % T) w[atomicAdd(bcnt + bucket(n % T), 1)] = WorkItem{nb + nf * T, n % T, x, 0};
       nb += n;
     }
     __syncthreads();
