@@ -360,12 +360,47 @@ __global__ __launch_bounds__(256) void k_final(const float* __restrict__ vpart, 
     return;
   }
   if (tid == 0) fail[r] = 0;
-  const int P = next_pow2(cnt < 2 ? 2 : cnt);
   const uint64_t* src = cand + r * capg;
-  for (int j = tid; j < P; j += blockDim.x) a[j] = j < cnt ? src[j] : 0ull;
+  for (int j = tid; j < cnt; j += 256) a[j] = src[j];
+  // radix select of the k-th largest key, 8 bits a pass from the top; the
+  // keys are distinct, so exactly k of them reach the final prefix
+  __shared__ int hist[256];
+  __shared__ int s_b, s_above, s_in, s_nsel;
+  uint64_t prefix = 0, mask = 0;
+  int krem = k;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    hist[tid] = 0;
+    __syncthreads();
+    for (int j = tid; j < cnt; j += 256) {
+      const uint64_t key = a[j];
+      if ((key & mask) == prefix) atomicAdd(hist + ((int)(key >> shift) & 255), 1);
+    }
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {  // suffix sums over the buckets
+      const int v = tid + off < 256 ? hist[tid + off] : 0;
+      __syncthreads();
+      hist[tid] += v;
+      __syncthreads();
+    }
+    const int here = hist[tid], above = tid < 255 ? hist[tid + 1] : 0;
+    if (here >= krem && above < krem) { s_b = tid; s_above = above; s_in = here - above; }
+    __syncthreads();
+    prefix |= (uint64_t)s_b << shift;
+    mask |= (uint64_t)0xFF << shift;
+    krem -= s_above;
+    const bool whole = s_in == krem;  // the bucket's keys are all taken
+    __syncthreads();
+    if (whole) break;
+  }
+  uint64_t* sel = a + capg;
+  if (tid == 0) s_nsel = 0;
   __syncthreads();
-  block_bitonic_sort(a, P, true);
-  emit_topk(a, k, topk + r * k);
+  for (int j = tid; j < cnt; j += 256) {
+    const uint64_t key = a[j];
+    if ((key & mask) >= prefix) sel[atomicAdd(&s_nsel, 1)] = key;
+  }
+  __syncthreads();
+  emit_topk(sel, k, topk + r * k);
 }
 
 // Exact streaming top-k of one landmark row over all N keys (fp32 dot
@@ -458,7 +493,10 @@ static void launch_score_main(const Plan& p) {
 
 template <typename T, int D>
 static void launch_final_t(const Plan& p) {
-  const size_t lds = (size_t)next_pow2(p.capg < 2 ? 2 : p.capg) * 8;
+  const size_t lds = ((size_t)p.capg + next_pow2(p.k < 2 ? 2 : p.k)) * 8;
+  if (lds > 65536)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_final<T, D>), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
   hipLaunchKernelGGL((k_final<T, D>), dim3((unsigned)(p.BH * p.m)), dim3(256), lds, p.stream, p.vpart, p.cand,
                      p.cand_cnt, p.topk, p.vt32, (T*)p.vtT, p.fail, p.N, p.k, p.C, p.capg, p.dense);
   if (!p.dense) {
