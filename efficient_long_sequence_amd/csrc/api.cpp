@@ -52,6 +52,7 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
   p.gh = pool.grid_h; p.gw = pool.grid_w; p.lh = pool.land_h; p.lw = pool.land_w;
   p.m = m; p.k = k; p.s = s;
   p.cscale = (float)(1.4426950408889634 / std::sqrt((double)d));
+  p.cscale_sh = p.cscale;
 
   // landmark scoring: rows per workgroup tile
   if (p.dtype == 0 || m <= 64) { p.sc_nw = 4; p.sc_ib = 1; }
@@ -176,16 +177,18 @@ struct Timer {
 };
 
 mita_status run(const void* Q, const void* K, const void* V, void* O, mita_dtype dtype, int B, int H, int N,
-                int d, mita_pool pool, int m, int k, int s, const mita_debug* dbg, void* workspace,
+                int d, mita_pool pool, int m, int k, int s, int variant, const mita_debug* dbg, void* workspace,
                 size_t workspace_bytes, void* stream, void* const* events) {
   mita_status st = validate(Q, K, V, O, dtype, B, H, N, d, pool, m, k, s, true);
   if (st != MITA_OK) return st;
+  if (variant != MITA_VARIANT_PAPER && variant != MITA_VARIANT_OFFICIAL) return MITA_ERR_PARAM;
   if (!workspace) return MITA_ERR_NULL;
   if ((uintptr_t)workspace & 15u) return MITA_ERR_PARAM;
   Plan p = make_plan(dtype, B, H, N, d, pool, m, k, s, (char*)workspace);
   if (workspace_bytes < p.total_bytes) return MITA_ERR_WORKSPACE;
   p.Q = Q; p.K = K; p.V = V; p.O = O;
   p.stream = (hipStream_t)stream;
+  if (variant == MITA_VARIANT_OFFICIAL) p.cscale_sh = (float)(1.4426950408889634 / (double)d);
   const Timer tm{events, p.stream};
 
   (void)hipGetLastError();  // clear any earlier sticky launch error
@@ -240,14 +243,24 @@ size_t mita_workspace_bytes(mita_dtype dtype, int B, int H, int N, int d, mita_p
 mita_status mita_forward(const void* Q, const void* K, const void* V, void* O, mita_dtype dtype, int B, int H,
                          int N, int d, mita_pool pool, int m, int k, int s, const mita_debug* dbg, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  return run(Q, K, V, O, dtype, B, H, N, d, pool, m, k, s, dbg, workspace, workspace_bytes, stream, nullptr);
+  return run(Q, K, V, O, dtype, B, H, N, d, pool, m, k, s, MITA_VARIANT_PAPER, dbg, workspace, workspace_bytes,
+             stream, nullptr);
 }
 
 mita_status mita_forward_timed(const void* Q, const void* K, const void* V, void* O, mita_dtype dtype, int B,
                                int H, int N, int d, mita_pool pool, int m, int k, int s, const mita_debug* dbg,
                                void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
   if (!events) return MITA_ERR_NULL;
-  return run(Q, K, V, O, dtype, B, H, N, d, pool, m, k, s, dbg, workspace, workspace_bytes, stream, events);
+  return run(Q, K, V, O, dtype, B, H, N, d, pool, m, k, s, MITA_VARIANT_PAPER, dbg, workspace, workspace_bytes,
+             stream, events);
+}
+
+mita_status mita_forward_variant(const void* Q, const void* K, const void* V, void* O, mita_dtype dtype, int B,
+                                 int H, int N, int d, mita_pool pool, int m, int k, int s, mita_variant variant,
+                                 const mita_debug* dbg, void* workspace, size_t workspace_bytes, void* stream,
+                                 void* const* events) {
+  return run(Q, K, V, O, dtype, B, H, N, d, pool, m, k, s, (int)variant, dbg, workspace, workspace_bytes, stream,
+             events);
 }
 
 int mita_num_stages(void) { return ST_COUNT; }

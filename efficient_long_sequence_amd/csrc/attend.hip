@@ -29,7 +29,7 @@ __global__ __launch_bounds__(NW * 64) void k_attend(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ Qt,
     const T* __restrict__ VtT, const int32_t* __restrict__ topk, const int32_t* __restrict__ perm,
     const WorkItem* __restrict__ wl, const int* __restrict__ wl_count, float* __restrict__ part,
-    T* __restrict__ O, int N, int m, int k, int s, int slot, int BH, float cscale) {
+    T* __restrict__ O, int N, int m, int k, int s, int slot, int BH, float cscale, float cscale_sh) {
   constexpr int NT = NW * 64;
   using TL = TileLayout<T, D>;
   __shared__ __align__(16) T smem[2 * TL::ELEMS];
@@ -64,42 +64,44 @@ __global__ __launch_bounds__(NW * 64) void k_attend(
     for (int cb = 0; cb < D / 16; ++cb) acc[b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // shared entries first (slot 0 only), then the expert's entries from a
+  // fresh step, so every step has one logit scale (the shared logits may be
+  // scaled differently, see mita_forward_variant)
   const int m0 = SLOT0 ? m : 0;
-  const int ne = m0 + k;
-  auto rowK = [&](int x0) {
+  const int ns = (m0 + 31) / 32, nsteps = ns + (k + 31) / 32;
+  auto rowK = [&](int st) {
     return [=](int r) -> const T* {
-      const int x = x0 + r;
-      if (x >= ne) return nullptr;
-      return x < m0 ? Qth + (size_t)x * D : Kh + (size_t)Ie[x - m0] * D;
+      if (st < ns) { const int x = st * 32 + r; return x < m0 ? Qth + (size_t)x * D : nullptr; }
+      const int x = (st - ns) * 32 + r;
+      return x < k ? Kh + (size_t)Ie[x] * D : nullptr;
     };
   };
-  auto rowV = [&](int x0) {
+  auto rowV = [&](int st) {
     return [=](int r) -> const T* {
-      const int x = x0 + r;
-      if (x >= ne) return nullptr;
-      return x < m0 ? Vth + (size_t)x * D : Vh + (size_t)Ie[x - m0] * D;
+      if (st < ns) { const int x = st * 32 + r; return x < m0 ? Vth + (size_t)x * D : nullptr; }
+      const int x = (st - ns) * 32 + r;
+      return x < k ? Vh + (size_t)Ie[x] * D : nullptr;
     };
   };
 
   TileLoader<T, D, NT, true> ld;
   T* buf0 = smem;
   T* buf1 = smem + TL::ELEMS;
-  const int nsteps = (ne + 31) / 32;
   ld.load(rowK(0), rowV(0));
   ld.store(buf0, buf0 + TL::K_ELEMS);
   __syncthreads();
   for (int st = 0; st < nsteps; ++st) {
-    const int x0 = st * 32;
     T* cur = (st & 1) ? buf1 : buf0;
     T* nxt = (st & 1) ? buf0 : buf1;
     const bool more = st + 1 < nsteps;
-    if (more) ld.load(rowK(x0 + 32), rowV(x0 + 32));
+    if (more) ld.load(rowK(st + 1), rowV(st + 1));
     StepFrags<T, D> f;
     f.load_keys(cur, li, lg);
     f.load_vals(cur + TL::K_ELEMS, li, lg);
-    const int nv = min(32, ne - x0);
-    if (nv == 32) attn_step<IB, false>(f, one, qf, nv, lg, cscale, M, Z, acc, NoHook{});
-    else attn_step<IB, true>(f, one, qf, nv, lg, cscale, M, Z, acc, NoHook{});
+    const int nv = st < ns ? min(32, m0 - st * 32) : min(32, k - (st - ns) * 32);
+    const float sc = st < ns ? cscale_sh : cscale;
+    if (nv == 32) attn_step<IB, false>(f, one, qf, nv, lg, sc, M, Z, acc, NoHook{});
+    else attn_step<IB, true>(f, one, qf, nv, lg, sc, M, Z, acc, NoHook{});
     if (more) ld.store(nxt, nxt + TL::K_ELEMS);
     __syncthreads();
   }
@@ -152,11 +154,11 @@ static void launch_attend_t(const Plan& p) {
     if (t > 0)
       hipLaunchKernelGGL((k_attend<T, D, NW, IB, false>), dim3((unsigned)p.UB), dim3(NW * 64), 0, p.stream,
                          (const T*)p.Q, (const T*)p.K, (const T*)p.V, (const T*)p.qt, (const T*)p.vtT, p.topk, perm,
-                         wl, wlc, p.part, (T*)p.O, p.N, p.m, p.k, p.s, t, p.BH, p.cscale);
+                         wl, wlc, p.part, (T*)p.O, p.N, p.m, p.k, p.s, t, p.BH, p.cscale, p.cscale_sh);
     else
       hipLaunchKernelGGL((k_attend<T, D, NW, IB, true>), dim3((unsigned)p.UB), dim3(NW * 64), 0, p.stream,
                          (const T*)p.Q, (const T*)p.K, (const T*)p.V, (const T*)p.qt, (const T*)p.vtT, p.topk, perm,
-                         wl, wlc, p.part, (T*)p.O, p.N, p.m, p.k, p.s, t, p.BH, p.cscale);
+                         wl, wlc, p.part, (T*)p.O, p.N, p.m, p.k, p.s, t, p.BH, p.cscale, p.cscale_sh);
   }
 }
 

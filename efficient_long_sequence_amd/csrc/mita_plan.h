@@ -54,6 +54,7 @@ struct Plan {
   int rs_qpw;     // queries per routing workgroup (resident path)
   int ex_nw, ex_ib;  // expert kernel waves and 16-query blocks per query group
   float cscale;   // log2(e) / sqrt(d)
+  float cscale_sh;  // log2(e) times the scale of the shared logits (1/sqrt(d) or 1/d)
 
   // workspace regions
   void* qt;         // [BH, m, d] dtype

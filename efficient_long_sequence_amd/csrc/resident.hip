@@ -171,7 +171,7 @@ template <typename T, int D, int NW, int SMAX>
 __global__ __launch_bounds__(NW * 64) void k_route_shared(
     const T* __restrict__ Q, const T* __restrict__ Qt, const T* __restrict__ VtT, int32_t* __restrict__ route,
     int* __restrict__ counts, float* __restrict__ plse, typename PartT<T>::type* __restrict__ po, int N, int m, int s,
-    int BH, int qpw, int hist_lds, float cscale) {
+    int BH, int qpw, int hist_lds, float cscale) {  // cscale: log2(e) x the shared-logit scale
   using RL = Resident<T, D>;
   using P = typename PartT<T>::type;
   using PV = typename Vec4<P>::type;
@@ -469,7 +469,7 @@ static void launch_route_shared_t(const Plan& p) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   dim3 grid((unsigned)((p.N + p.rs_qpw - 1) / p.rs_qpw), (unsigned)p.BH);
   hipLaunchKernelGGL(fn, grid, dim3(NW * 64), lds, p.stream, (const T*)p.Q, (const T*)p.qt, (const T*)p.vtT, p.route,
-                     p.counts, p.plse, (typename PartT<T>::type*)p.po, p.N, p.m, p.s, p.BH, p.rs_qpw, hist_lds, p.cscale);
+                     p.counts, p.plse, (typename PartT<T>::type*)p.po, p.N, p.m, p.s, p.BH, p.rs_qpw, hist_lds, p.cscale_sh);
 }
 
 template <typename T, int D>

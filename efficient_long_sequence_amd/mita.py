@@ -24,7 +24,7 @@ STATUS = {
 }
 
 EXPORTS = [
-    "mita_workspace_bytes", "mita_forward", "mita_forward_timed", "mita_num_stages",
+    "mita_workspace_bytes", "mita_forward", "mita_forward_timed", "mita_forward_variant", "mita_num_stages",
     "mita_stage_name", "mita_events_create", "mita_events_destroy", "mita_events_elapsed",
     "mita_status_str", "mita_version",
 ]
@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
     L.mita_forward.argtypes = fwd
     L.mita_forward_timed.restype = c_int
     L.mita_forward_timed.argtypes = fwd + [ctypes.POINTER(vp)]
+    L.mita_forward_variant.restype = c_int
+    L.mita_forward_variant.argtypes = fwd[:13] + [c_int] + fwd[13:] + [ctypes.POINTER(vp)]
     L.mita_num_stages.restype = c_int
     L.mita_stage_name.restype = ctypes.c_char_p
     L.mita_stage_name.argtypes = [c_int]
@@ -130,14 +132,30 @@ class Events:
             self.arr = None
 
 
+# Scale of the shared logits q . q~ in the joint softmax: "paper" = 1/sqrt(d)
+# like every other logit; "official" = 1/d, the authors' code path (MiTA
+# tutorial, chapter 8, third check).
+VARIANTS = {"paper": 0, "official": 1}
+
+
+def official_params(grid_h: int, grid_w: int, pool_size: int, kv_topk: int):
+    """Pool and k from the authors' side-length parameters: their module
+    squares ``pool_size`` and ``kv_topk`` into m = pool_size**2 landmarks (a
+    pool_size x pool_size landmark grid) and k = kv_topk**2 keys per expert
+    (MiTA tutorial, chapter 8, third check)."""
+    return (grid_h, grid_w, pool_size, pool_size), kv_topk * kv_topk
+
+
 def forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, pool, k: int, s: int,
             debug: bool = False, workspace: torch.Tensor | None = None,
-            out: torch.Tensor | None = None, events: Events | None = None, m: int | None = None):
+            out: torch.Tensor | None = None, events: Events | None = None, m: int | None = None,
+            variant: str = "paper"):
     """MiTA forward pass on the GPU.
 
     Q, K, V: contiguous device tensors [B, H, N, d] (bf16 or fp32).
     pool: (grid_h, grid_w, land_h, land_w); m = land_h * land_w unless given
     (a mismatching m is passed through so the library can reject it).
+    variant: "paper" or "official" (scale of the shared logits, see VARIANTS).
     Returns O, or (O, DebugOut) when ``debug``.
     """
     L = lib()
@@ -168,7 +186,12 @@ def forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, pool, k: int, s: 
     args = (Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), dt, B, H, N, d, P, m, k, s,
             ctypes.byref(dbg_struct) if dbg_struct is not None else None,
             workspace.data_ptr(), workspace.numel(), stream)
-    if events is None:
+    if variant not in VARIANTS:
+        raise MitaError(3, f"unknown variant {variant!r}")
+    if variant != "paper":
+        code = L.mita_forward_variant(*args[:13], VARIANTS[variant], *args[13:],
+                                      events.arr if events is not None else None)
+    elif events is None:
         code = L.mita_forward(*args)
     else:
         code = L.mita_forward_timed(*args, events.arr)

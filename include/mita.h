@@ -22,8 +22,9 @@
  *     (row-major, as the tutorial's 2x4 grid example in chapter 5);
  *   - top-k and top-s ties go to the lowest index; I rows are returned in
  *     ascending key index, routes by score descending then landmark index;
- *   - every logit is scaled by 1/sqrt(d); the routing score is the unscaled
- *     q . q~ (same order);
+ *   - every logit is scaled by 1/sqrt(d) (mita_forward_variant can instead
+ *     scale the shared logits by 1/d, as the authors' code does); the routing
+ *     score is the unscaled q . q~ (same order);
  *   - non-causal: every query sees all m shared entries.
  *
  * Threading and ownership: the caller owns every buffer (inputs, outputs,
@@ -107,6 +108,28 @@ mita_status mita_forward_timed(const void* Q, const void* K, const void* V, void
                                mita_dtype dtype, int B, int H, int N, int d, mita_pool pool,
                                int m, int k, int s, const mita_debug* dbg, void* workspace,
                                size_t workspace_bytes, void* stream, void* const* events);
+
+/* Scale of the m shared logits q . q~_i in the step-6 softmax. */
+typedef enum {
+  /* 1/sqrt(d), like every other logit: the paper's eqs. 5-12 as the MiTA
+   * tutorial's chapter 4 states them. */
+  MITA_VARIANT_PAPER = 0,
+  /* 1/d: the authors' released code pre-scales the shared key by d^-1/2 and
+   * then applies the d^-1/2 logit scale (MiTA tutorial, chapter 8, third
+   * check).  Routed logits stay q . k / sqrt(d); pooling, landmark scores,
+   * top-k, shared values and routing are those of MITA_VARIANT_PAPER. */
+  MITA_VARIANT_OFFICIAL = 1
+} mita_variant;
+
+/* mita_forward / mita_forward_timed with the shared-logit scale chosen by
+ * `variant` (any other value returns MITA_ERR_PARAM before any launch).
+ * `events` is NULL, or 2 * mita_num_stages() handles as for
+ * mita_forward_timed. */
+mita_status mita_forward_variant(const void* Q, const void* K, const void* V, void* O,
+                                 mita_dtype dtype, int B, int H, int N, int d, mita_pool pool,
+                                 int m, int k, int s, mita_variant variant, const mita_debug* dbg,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 void* const* events);
 
 /* Number of timed stages and their names ("pool", "estimate", "score", ...). */
 int mita_num_stages(void);

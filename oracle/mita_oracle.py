@@ -42,8 +42,11 @@ Readings where the pages are silent (each listed in the design notes):
 * The routing score is the unscaled q . q~ (the 1/sqrt(d) scale is monotone).
 * With s >= 2, a key present in two chosen experts appears twice in K*_n
   (the pages count m + s k entries and let experts overlap).
-* Every logit is scaled by 1/sqrt(d) (tutorial ch.5 and ch.8 note that the
-  authors' code instead uses 1/d on the shared logits; not followed here).
+* Every logit is scaled by 1/sqrt(d) (tutorial ch.5).  The tutorial's ch.8
+  (third check) notes that the authors' code pre-scales the shared key by
+  d^-1/2 before the d^-1/2 logit scale, so its shared logits are q . q~ / d
+  while routed logits stay q . k / sqrt(d): ``variant="official"`` in
+  attend() and forward() follows that path and changes nothing else.
 
 Parity pins (tests/test_oracle_*.py): the tutorial's worked softmax fact
 (ch.1), the merge identity (ch.4), the m = k = N counterexample value
@@ -292,7 +295,7 @@ def _concat(Qt, Vt, K, V, I, experts):
 
 
 def attend(Q, K, V, Qt, Vt, I, e, R=None, counter: DotCounter | None = None,
-           check_weights: bool = True):
+           check_weights: bool = True, variant: str = "paper"):
     """O [N, d] given landmarks, shared values, experts I [m, k] and routes e [N, s].
 
     This is the conditional form of steps 6-7: the GPU's own I and e can be
@@ -300,7 +303,11 @@ def attend(Q, K, V, Qt, Vt, I, e, R=None, counter: DotCounter | None = None,
     they are evaluated together with one matrix product; each row is still
     exactly softmax(K* q / sqrt(d)) V*.  When R (the unscaled q . q~ scores
     of step 5) is given, the shared logits reuse it instead of recomputing.
+    variant="official" divides the m shared logits by d instead of sqrt(d)
+    (tutorial ch.8, third check); the routed logits keep 1/sqrt(d).
     """
+    if variant not in ("paper", "official"):
+        raise ValueError("variant must be 'paper' or 'official'")
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
@@ -310,6 +317,7 @@ def attend(Q, K, V, Qt, Vt, I, e, R=None, counter: DotCounter | None = None,
     m, k = I.shape
     s = e.shape[1]
     sq = math.sqrt(d)
+    sh = sq if variant == "paper" else float(d)
     O = np.empty((N, d))
     tuples, inv = np.unique(np.asarray(e), axis=0, return_inverse=True)
     inv = inv.reshape(-1)
@@ -320,7 +328,7 @@ def attend(Q, K, V, Qt, Vt, I, e, R=None, counter: DotCounter | None = None,
         raw = Q[ns] @ Ks[m:].T / sq
         if counter is not None:
             counter.query_raw += raw.size
-        shared = (R[ns] if R is not None else Q[ns] @ Qt.T) / sq
+        shared = (R[ns] if R is not None else Q[ns] @ Qt.T) / sh
         l = np.concatenate([shared, raw], axis=1)
         w = np.exp(l - l.max(axis=1, keepdims=True))
         w /= w.sum(axis=1, keepdims=True)
@@ -346,8 +354,9 @@ class HeadResult:
     counter: DotCounter = field(default_factory=DotCounter)
 
 
-def forward(Q, K, V, grid_h, grid_w, land_h, land_w, k, s, dtype="bf16", row_block=64):
-    """MiTA forward pass of one head, steps 1-7 in the pages' order.
+def forward(Q, K, V, grid_h, grid_w, land_h, land_w, k, s, dtype="bf16", row_block=64, variant="paper"):
+    """MiTA forward pass of one head, steps 1-7 in the pages' order
+    (``variant`` as in attend()).
 
     Q, K, V [N, d] hold values exactly representable in ``dtype``.  Landmark
     scores are evaluated in blocks of ``row_block`` landmark rows only to
@@ -378,5 +387,5 @@ def forward(Q, K, V, grid_h, grid_w, land_h, land_w, k, s, dtype="bf16", row_blo
         thr[rows] = tb
         Vt[rows] = shared_values(S, V)
     e, R, rt_gaps = route(Q, Qt, s, counter=cnt)
-    O = attend(Q, K, V, Qt, Vt, I, e, R=R, counter=cnt)
+    O = attend(Q, K, V, Qt, Vt, I, e, R=R, counter=cnt, variant=variant)
     return HeadResult(O, Qt, I, e, Vt, tk_gaps, rt_gaps, thr, cnt)

@@ -50,10 +50,10 @@ def to_host(t: torch.Tensor) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def run_gpu(Q, K, V, pool, k, s, dtype):
+def run_gpu(Q, K, V, pool, k, s, dtype, variant="paper"):
     """Q, K, V: float32 arrays [B, H, N, d] (dtype-exact). Returns O and debug outputs."""
     q, kk, v = (to_device(x, dtype) for x in (Q, K, V))
-    O, dbg = mita.forward(q, kk, v, pool, k, s, debug=True)
+    O, dbg = mita.forward(q, kk, v, pool, k, s, debug=True, variant=variant)
     torch.cuda.synchronize()
     return dict(O=to_host(O), topk=dbg.topk.cpu().numpy(), route=dbg.route.cpu().numpy(),
                 vtilde=dbg.vtilde.cpu().numpy().astype(np.float64), qtilde=to_host(dbg.qtilde))
@@ -130,7 +130,7 @@ def check_route_row(rrow: np.ndarray, got: np.ndarray, s: int) -> bool:
 
 
 def check_head(Qh, Kh, Vh, pool, k, s, dtype, gpu: dict, bh, stats: Stats,
-               rows=None, queries=None, full_o=True):
+               rows=None, queries=None, full_o=True, variant="paper"):
     """Compare one head; ``rows``/``queries`` sample landmark rows and queries
     (None = all)."""
     gh, gw, lh, lw = pool
@@ -171,7 +171,7 @@ def check_head(Qh, Kh, Vh, pool, k, s, dtype, gpu: dict, bh, stats: Stats,
     stats.routes += len(qs)
     stats.routes_exempt += int(route_exempt.sum())
     # output against the conditional oracle (GPU's I and e, oracle v~)
-    O_c = mo.attend(Qh[qs], Kh, Vh, Qt, Vt, I_gpu, e_gpu[qs])
+    O_c = mo.attend(Qh[qs], Kh, Vh, Qt, Vt, I_gpu, e_gpu[qs], variant=variant)
     do = np.abs(gpu["O"][b, h][qs] - O_c)
     stats.o_max = max(stats.o_max, float(do.max()))
     stats.o_mean = max(stats.o_mean, float(do.mean()))
@@ -180,7 +180,7 @@ def check_head(Qh, Kh, Vh, pool, k, s, dtype, gpu: dict, bh, stats: Stats,
         sel = ~route_exempt & ~row_exempt[e_gpu[qs]].any(axis=1)
         if sel.any():
             e_or = mo.route(Qh[qs][sel], Qt, s)[0]
-            O_u = mo.attend(Qh[qs][sel], Kh, Vh, Qt, Vt, I_or, e_or)
+            O_u = mo.attend(Qh[qs][sel], Kh, Vh, Qt, Vt, I_or, e_or, variant=variant)
             stats.o_strict_max = max(stats.o_strict_max, float(np.abs(gpu["O"][b, h][qs][sel] - O_u).max()))
     return stats
 
@@ -195,18 +195,18 @@ def assert_tolerances(stats: Stats, dtype: str):
         assert stats.o_mean <= tol["mean"], f"O mean-abs {stats.o_mean}"
 
 
-def run_and_check(Q, K, V, pool, k, s, dtype, heads=None, rows=None, queries=None, label=""):
+def run_and_check(Q, K, V, pool, k, s, dtype, heads=None, rows=None, queries=None, label="", variant="paper"):
     """Run the whole batch on the GPU, check the listed heads (default all)."""
     B, H = Q.shape[:2]
     t0 = time.time()
-    say(f"[gpu] {label} B={B} H={H} N={Q.shape[2]} d={Q.shape[3]} pool={pool} k={k} s={s} {dtype}")
-    gpu = run_gpu(Q, K, V, pool, k, s, dtype)
+    say(f"[gpu] {label} B={B} H={H} N={Q.shape[2]} d={Q.shape[3]} pool={pool} k={k} s={s} {dtype} {variant}")
+    gpu = run_gpu(Q, K, V, pool, k, s, dtype, variant)
     say(f"[gpu] {label} ran in {time.time() - t0:.2f}s; checking")
     stats = Stats()
     heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
     for (b, h) in heads:
         check_head(Q[b, h].astype(np.float64), K[b, h].astype(np.float64), V[b, h].astype(np.float64),
-                   pool, k, s, dtype, gpu, (b, h), stats, rows=rows, queries=queries)
+                   pool, k, s, dtype, gpu, (b, h), stats, rows=rows, queries=queries, variant=variant)
     assert_tolerances(stats, dtype)
     say(f"[gpu] {label} ok: rows {stats.rows} (exempt {stats.rows_exempt}), routes {stats.routes} "
         f"(exempt {stats.routes_exempt}), v~ max {stats.vt_max:.2e} mean {stats.vt_mean:.2e}, "

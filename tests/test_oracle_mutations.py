@@ -110,7 +110,7 @@ def _concat_dedup(Qt, Vt, K, V, I, experts):
     return np.concatenate([Qt, K[sel]]), np.concatenate([Vt, V[sel]])
 
 
-def _attend_separate_softmax(Q, K, V, Qt, Vt, I, e, R=None, counter=None, check_weights=True):
+def _attend_separate_softmax(Q, K, V, Qt, Vt, I, e, R=None, counter=None, check_weights=True, variant="paper"):
     # normalises the shared and routed parts separately and adds them: o1 + o2
     Q = np.asarray(Q, float)
     O = np.empty_like(Q)
