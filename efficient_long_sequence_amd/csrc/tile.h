@@ -33,9 +33,17 @@ struct TileLoader {
   static constexpr int VCH = WITH_V ? (32 / VROWS) * CPR : 0;
   static constexpr int VPT = WITH_V ? (VCH + NT - 1) / NT : 0;
   static constexpr int VS = L::VS;
+  // Split placement (bf16, when the block has room): key chunks go to the
+  // first threads and the value transpose, in tasks of two rows by four
+  // elements, to the last ones.  A SIMD runs waves w and w + NT/256 of the
+  // block, so each SIMD then carries one key-loading and one value-loading
+  // wave and the per-step barrier waits less for the slowest.
+  static constexpr int VFINE = WITH_V ? 16 * (D / 4) : 0;
+  static constexpr bool SPLIT = WITH_V && sizeof(T) == 2 && KCH + VFINE <= NT;
 
   uint4 kreg[KPT];
-  uint4 vreg[VPT > 0 ? VPT : 1][VROWS];
+  uint4 vreg[SPLIT ? 1 : (VPT > 0 ? VPT : 1)][SPLIT ? 1 : VROWS];
+  uint2 vfine[SPLIT ? 2 : 1];
 
   // rk(j) / rv(j): pointer to key / value row j of the step, or nullptr for a
   // row past the end (it is staged as zeros).
@@ -51,7 +59,17 @@ struct TileLoader {
         if (p) kreg[c] = *(const uint4*)(p + (i % CPR) * EPC);
       }
     }
-    if constexpr (WITH_V) {
+    if constexpr (SPLIT) {
+      const int i = tid - (NT - VFINE);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        vfine[r] = make_uint2(0, 0);
+        if (i >= 0) {
+          const T* p = rv(2 * (i / (D / 4)) + r);
+          if (p) vfine[r] = *(const uint2*)(p + (i % (D / 4)) * 4);
+        }
+      }
+    } else if constexpr (WITH_V) {
 #pragma unroll
       for (int c = 0; c < VPT; ++c) {
         const int i = tid + c * NT;
@@ -74,7 +92,20 @@ struct TileLoader {
       const int i = tid + c * NT;
       if (i < KCH) *(uint4*)(Ks + (i / CPR) * L::KS + (i % CPR) * EPC) = kreg[c];
     }
-    if constexpr (WITH_V) {
+    if constexpr (SPLIT) {
+      const int i = tid - (NT - VFINE);
+      if (i >= 0) {
+        const int jp = i / (D / 4), c0 = (i % (D / 4)) * 4;
+        const uint32_t* a = (const uint32_t*)&vfine[0];
+        const uint32_t* b = (const uint32_t*)&vfine[1];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          // elements 2u, 2u+1 of rows 2jp (a) and 2jp+1 (b)
+          *(uint32_t*)(Vs + (c0 + 2 * u) * VS + 2 * jp) = (a[u] & 0xFFFFu) | (b[u] << 16);
+          *(uint32_t*)(Vs + (c0 + 2 * u + 1) * VS + 2 * jp) = (a[u] >> 16) | (b[u] & 0xFFFF0000u);
+        }
+      }
+    } else if constexpr (WITH_V) {
 #pragma unroll
       for (int c = 0; c < VPT; ++c) {
         const int i = tid + c * NT;
