@@ -263,6 +263,19 @@ mita_status mita_forward_variant(const void* Q, const void* K, const void* V, vo
              events);
 }
 
+mita_status mita_dense_attention(const void* Q, const void* K, const void* V, void* O, mita_dtype dtype, int B,
+                                 int H, int N, int d, void* stream) {
+  if (!Q || !K || !V || !O) return MITA_ERR_NULL;
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return MITA_ERR_SHAPE;
+  if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15u) return MITA_ERR_PARAM;
+  if (dtype != MITA_F32 && dtype != MITA_BF16) return MITA_ERR_UNSUPPORTED;
+  if (d != 32 && d != 64) return MITA_ERR_UNSUPPORTED;
+  if ((long long)N > MAX_N || (long long)B * H > 65535) return MITA_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  launch_dense(Q, K, V, O, dtype == MITA_BF16 ? 1 : 0, B * H, N, d, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? MITA_OK : MITA_ERR_HIP;
+}
+
 int mita_num_stages(void) { return ST_COUNT; }
 
 const char* mita_stage_name(int stage) { return (stage >= 0 && stage < ST_COUNT) ? kStageNames[stage] : "?"; }

@@ -101,6 +101,9 @@ void launch_bucket(const Plan& p);
 void launch_attend(const Plan& p);
 void launch_route_shared(const Plan& p);
 void launch_expert(const Plan& p);
+// dense softmax attention over B*H heads (the full-attention baseline)
+void launch_dense(const void* Q, const void* K, const void* V, void* O, int dtype, int BH, int N, int d,
+                  hipStream_t stream);
 size_t resident_bytes(int dtype, int d, int E);
 // LDS a resident entry set may take (of 160 KB per compute unit).
 constexpr size_t RES_MAX = 150 * 1024;

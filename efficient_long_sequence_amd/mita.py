@@ -24,7 +24,7 @@ STATUS = {
 }
 
 EXPORTS = [
-    "mita_workspace_bytes", "mita_forward", "mita_forward_timed", "mita_forward_variant", "mita_num_stages",
+    "mita_workspace_bytes", "mita_forward", "mita_forward_timed", "mita_forward_variant", "mita_dense_attention", "mita_num_stages",
     "mita_stage_name", "mita_events_create", "mita_events_destroy", "mita_events_elapsed",
     "mita_status_str", "mita_version",
 ]
@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
     L.mita_forward_timed.argtypes = fwd + [ctypes.POINTER(vp)]
     L.mita_forward_variant.restype = c_int
     L.mita_forward_variant.argtypes = fwd[:13] + [c_int] + fwd[13:] + [ctypes.POINTER(vp)]
+    L.mita_dense_attention.restype = c_int
+    L.mita_dense_attention.argtypes = [vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, vp]
     L.mita_num_stages.restype = c_int
     L.mita_stage_name.restype = ctypes.c_char_p
     L.mita_stage_name.argtypes = [c_int]
@@ -130,6 +132,21 @@ class Events:
         if self.arr is not None:
             lib().mita_events_destroy(self.arr, 2 * self.n)
             self.arr = None
+
+
+def dense_attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, out: torch.Tensor | None = None):
+    """Full softmax attention softmax(Q K^T / sqrt(d)) V on the GPU (the
+    baseline of the pages' long-sequence throughput test); [B, H, N, d]."""
+    L = lib()
+    B, H, N, d = Q.shape
+    for t in (Q, K, V):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != Q.dtype or t.shape != Q.shape:
+            raise MitaError(2, "Q, K, V must be contiguous device tensors of one shape and dtype")
+    O = torch.empty_like(Q) if out is None else out
+    stream = torch.cuda.current_stream(Q.device).cuda_stream
+    _check(L.mita_dense_attention(Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), _dtype_code(Q.dtype),
+                                  B, H, N, d, stream))
+    return O
 
 
 # Scale of the shared logits q . q~ in the joint softmax: "paper" = 1/sqrt(d)

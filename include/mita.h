@@ -131,6 +131,19 @@ mita_status mita_forward_variant(const void* Q, const void* K, const void* V, vo
                                  void* workspace, size_t workspace_bytes, void* stream,
                                  void* const* events);
 
+/* Dense (full) softmax attention O = softmax(Q K^T / sqrt(d)) V for B*H
+ * independent heads, non-causal: the baseline of the pages' long-sequence
+ * throughput test (MiTA tutorial, chapter 7, "LRA and synthetic long
+ * sequences"; paper section 4.3, Fig. 5).  Q, K, V, O as for mita_forward
+ * (device, dtype, contiguous [B, H, N, d], 16-byte aligned); no workspace, no
+ * allocation, no synchronisation.  Errors: MITA_ERR_NULL (a NULL pointer),
+ * MITA_ERR_SHAPE (B, H, N or d <= 0), MITA_ERR_PARAM (misaligned pointer),
+ * MITA_ERR_UNSUPPORTED (d not in {32, 64}, unknown dtype, N > 2^26,
+ * B*H > 65535), MITA_ERR_HIP (launch failure); nothing is launched on a
+ * validation error. */
+mita_status mita_dense_attention(const void* Q, const void* K, const void* V, void* O,
+                                 mita_dtype dtype, int B, int H, int N, int d, void* stream);
+
 /* Number of timed stages and their names ("pool", "estimate", "score", ...). */
 int mita_num_stages(void);
 const char* mita_stage_name(int stage);

@@ -88,3 +88,29 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(mita, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         mita.lib()
+
+
+def test_forward_variant_rejects_unknown_variant_before_any_launch():
+    L = mita.lib()
+    P = mita.Pool(1, 4096, 1, 64)
+    args = (A, A, A, A, mita.BF16, 1, 2, 4096, 64, P, 64, 64, 1)
+    assert L.mita_forward_variant(*args, 2, None, A, 1 << 40, None, None) == 3
+    assert L.mita_forward_variant(*args, -1, None, A, 1 << 40, None, None) == 3
+    # the shape checks run first, with the same codes as mita_forward
+    bad = (A, A, A, A, mita.BF16, 1, 2, 4095, 64, P, 64, 64, 1)
+    assert L.mita_forward_variant(*bad, 1, None, A, 1 << 40, None, None) == 2
+    # and an undersized workspace is reported for a valid variant
+    assert L.mita_forward_variant(*args, 1, None, A, 16, None, None) == 5
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=0), 1), (dict(O=0), 1), (dict(B=0), 2), (dict(N=0), 2), (dict(d=-1), 2),
+    (dict(V=A + 4), 3), (dict(d=48), 4), (dict(dt=3), 4), (dict(N=(1 << 26) + 1), 4),
+    (dict(B=300, H=300), 4),
+])
+def test_dense_attention_rejects_invalid_arguments(kw, code):
+    a = dict(Q=A, K=A, V=A, O=A, dt=mita.BF16, B=1, H=2, N=4096, d=64)
+    a.update(kw)
+    got = mita.lib().mita_dense_attention(a["Q"], a["K"], a["V"], a["O"], a["dt"], a["B"], a["H"], a["N"],
+                                          a["d"], None)
+    assert got == code

@@ -1,0 +1,61 @@
+"""GPU parity of the dense-attention baseline (mita_dense_attention) through the C ABI.
+
+Full softmax attention is the oracle's joint softmax with every key as an
+entry: o_n = V^T softmax(K q_n / sqrt(d)) (oracle.attend_one with K* = K and
+V* = V).  Sizes span ragged 512-query blocks and 32-key steps, both head dims
+and both dtypes; the N = 64K case is checked on sampled queries.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from efficient_long_sequence_amd import mita, synth
+from oracle import mita_oracle as mo
+from tests import gpu_harness as gh_
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+CASES = {
+    # label: (B, H, N, d, kind, clusters, dtype, sampled queries or None)
+    "ragged_bf16_d64": (2, 2, 1000, 64, "clustered", 16, "bf16", None),
+    "ragged_bf16_d32": (1, 3, 777, 32, "iid", 0, "bf16", None),
+    "f32_d64": (1, 2, 300, 64, "iid", 0, "f32", None),
+    "f32_d32": (2, 1, 129, 32, "clustered", 4, "f32", None),
+    "tiny_n1": (1, 1, 1, 64, "iid", 0, "bf16", None),
+    "long_64k": (1, 2, 65536, 64, "runs", 64, "bf16", 256),
+}
+
+
+@pytest.mark.parametrize("label", list(CASES))
+def test_dense_attention_parity(label):
+    B, H, N, d, kind, nc, dtype, nq = CASES[label]
+    Q, K, V = synth.make(B, H, N, d, kind, nc, dtype, zlib.crc32(label.encode()) % 1000)
+    gh_.say(f"[gpu] dense {label} B={B} H={H} N={N} d={d} {dtype}")
+    q, k, v = (gh_.to_device(x, dtype) for x in (Q, K, V))
+    O = gh_.to_host(mita.dense_attention(q, k, v))
+    torch.cuda.synchronize()
+    tol = gh_.TOL[dtype]
+    worst, mean_acc, cnt = 0.0, 0.0, 0
+    for b in range(B):
+        for h in range(H):
+            qs = np.arange(N) if nq is None else np.sort(np.random.default_rng(b * H + h).choice(N, nq, replace=False))
+            Kh, Vh = K[b, h].astype(np.float64), V[b, h].astype(np.float64)
+            for n in qs:
+                o, w = mo.attend_one(Q[b, h, n].astype(np.float64), Kh, Vh)
+                err = np.abs(O[b, h, n] - o)
+                worst = max(worst, float(err.max()))
+                mean_acc += float(err.mean())
+                cnt += 1
+    gh_.say(f"[gpu] dense {label} ok: max {worst:.2e} mean {mean_acc / cnt:.2e}")
+    assert worst <= tol["max"]
+    if dtype == "bf16":
+        assert mean_acc / cnt <= tol["mean"]
