@@ -281,6 +281,76 @@ def cpu_baseline(w, run):
                         f"{est_total:.1f}s for all {w.B * w.H} heads"))
 
 
+# The pages' long-sequence throughput test (MiTA tutorial, ch.7, "LRA and
+# synthetic long sequences"; paper section 4.3, Fig. 5): a three-layer model
+# of width 128, m*k ~ N/4, batch chosen per length, speed-up of MiTA over full
+# attention.  Points: (N, m = k, batch); the speed-ups the pages report (on an
+# RTX 4090 with FlashAttention as the dense baseline) are context only.
+E2E_POINTS = [(16384, 64, 16), (65536, 128, 4), (262144, 256, 1), (1048576, 512, 1)]
+E2E_PAGES_SPEEDUP = {16384: 4.7, 65536: 19.0, 262144: 56.0, 1048576: 159.0}
+
+
+def e2e(points, reps_mita: int = 5, reps_dense: int = 2):
+    """Forward throughput of a 3-layer, width-128 Transformer (2 heads of 64,
+    pre-LayerNorm blocks, GELU MLP of width 512, random bf16 weights) with
+    MiTA attention (mita_forward) and with dense attention (our own
+    mita_dense_attention kernel); projections, norms and the MLP are library
+    calls shared by both.  Returns one dict per point."""
+    import torch
+    import torch.nn.functional as F
+    from efficient_long_sequence_amd import mita
+    dim, H, d, layers, hidden = 128, 2, 64, 3, 512
+    g = torch.Generator(device="cuda").manual_seed(0)
+
+    def w(i, o):
+        return (torch.randn(i, o, device="cuda", generator=g) * (1.0 / i ** 0.5)).to(torch.bfloat16).contiguous()
+
+    params = [dict(wqkv=w(dim, 3 * dim), wo=w(dim, dim), w1=w(dim, hidden), w2=w(hidden, dim)) for _ in range(layers)]
+
+    def run_model(x, attend):
+        B, N, _ = x.shape
+        for P in params:
+            h = F.layer_norm(x, (dim,))
+            qkv = (h @ P["wqkv"]).view(B, N, 3, H, d).permute(2, 0, 3, 1, 4).contiguous()
+            o = attend(qkv[0], qkv[1], qkv[2])
+            x = x + o.permute(0, 2, 1, 3).reshape(B, N, dim) @ P["wo"]
+            h = F.layer_norm(x, (dim,))
+            x = x + F.gelu(h @ P["w1"]) @ P["w2"]
+        return x
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / reps
+
+    out = []
+    for N, mk, B in points:
+        x = torch.randn(B, N, dim, device="cuda", generator=g).to(torch.bfloat16)
+        pool = (1, N, 1, mk)
+        ws = torch.empty(mita.workspace_bytes(torch.bfloat16, B, H, N, d, pool, mk, 1), dtype=torch.uint8,
+                         device="cuda")
+        mita_attn = lambda q, k, v: mita.forward(q, k, v, pool, mk, 1, workspace=ws)
+        t_mita = timed(lambda: run_model(x, mita_attn), reps_mita)
+        t_dense = timed(lambda: run_model(x, mita.dense_attention), reps_dense)
+        q = torch.randn(B, H, N, d, device="cuda", generator=g).to(torch.bfloat16)
+        ta_mita = timed(lambda: mita_attn(q, q, q), reps_mita)
+        ta_dense = timed(lambda: mita.dense_attention(q, q, q), reps_dense)
+        out.append(dict(N=N, batch=B, m=mk, k=mk, s=1, model_tokens_per_s_mita=B * N / t_mita,
+                        model_tokens_per_s_dense=B * N / t_dense, speedup_model=t_dense / t_mita,
+                        attention_ms_mita=1e3 * ta_mita, attention_ms_dense=1e3 * ta_dense,
+                        speedup_attention=ta_dense / ta_mita,
+                        dense_attention_tflops=4.0 * B * H * N * N * d / ta_dense * 1e-12,
+                        pages_reported_speedup=E2E_PAGES_SPEEDUP.get(N)))
+        print(json.dumps(out[-1]), file=sys.stderr, flush=True)
+        del x, ws, q
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -294,6 +364,9 @@ def main():
     ap.add_argument("--ingest-command", default="")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (calibrates HBM byte counters)")
+    ap.add_argument("--e2e", action="store_true",
+                    help="instead: the three-layer, width-128 model with MiTA vs dense attention at 16K-1M")
+    ap.add_argument("--e2e-max-n", type=int, default=1 << 20, help="largest sequence length of --e2e")
     args = ap.parse_args()
     if args.ingest:
         ingest(*args.ingest, workload=args.workload, command=args.ingest_command)
@@ -307,6 +380,12 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(2)
+    if args.e2e:
+        pts = [p for p in E2E_POINTS if p[0] <= args.e2e_max_n]
+        print(json.dumps(dict(metric="3-layer width-128 model forward tokens/s, MiTA vs dense attention",
+                              unit="tokens/s", n_gpus=1, dtype="bf16", data="synthetic, random weights",
+                              points=e2e(pts))), flush=True)
+        return
     w = WORKLOADS[args.workload]
     if args.copy_calib_mib:
         n = args.copy_calib_mib << 20

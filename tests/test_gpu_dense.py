@@ -59,3 +59,12 @@ def test_dense_attention_parity(label):
     assert worst <= tol["max"]
     if dtype == "bf16":
         assert mean_acc / cnt <= tol["mean"]
+
+
+def test_end_to_end_model_runs_both_attentions():
+    """The three-layer comparison model (bench.py --e2e) on one small point:
+    both attention kernels run inside it and the timings are finite."""
+    import bench
+    (r,) = bench.e2e([(4096, 32, 2)], reps_mita=1, reps_dense=1)
+    for key in ("model_tokens_per_s_mita", "model_tokens_per_s_dense", "attention_ms_mita", "attention_ms_dense"):
+        assert np.isfinite(r[key]) and r[key] > 0
