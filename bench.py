@@ -93,21 +93,22 @@ def make_device_inputs(w):
     return (Q, K, V), out
 
 
-def time_workload(w, steps: int, warmup: int):
+def time_workload(w, steps: int, warmup: int, variant: str = "paper", k: int | None = None, inputs=None):
     import torch
     from efficient_long_sequence_amd import mita
-    host, (q, k, v) = make_device_inputs(w)
+    host, (q, kk, v) = make_device_inputs(w) if inputs is None else inputs
+    k = w.k if k is None else k
     pool = (w.grid_h, w.grid_w, w.land_h, w.land_w)
-    ws = torch.empty(mita.workspace_bytes(q.dtype, w.B, w.H, w.N, w.d, pool, w.k, w.s), dtype=torch.uint8,
+    ws = torch.empty(mita.workspace_bytes(q.dtype, w.B, w.H, w.N, w.d, pool, k, w.s), dtype=torch.uint8,
                      device=q.device)
     out = torch.empty_like(q)
     for _ in range(warmup):
-        mita.forward(q, k, v, pool, w.k, w.s, workspace=ws, out=out)
+        mita.forward(q, kk, v, pool, k, w.s, workspace=ws, out=out, variant=variant)
     events = [mita.Events() for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        mita.forward(q, k, v, pool, w.k, w.s, workspace=ws, out=out, events=events[i])
+        mita.forward(q, kk, v, pool, k, w.s, workspace=ws, out=out, events=events[i], variant=variant)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     stages = {}
@@ -116,7 +117,7 @@ def time_workload(w, steps: int, warmup: int):
             stages[name] = stages.get(name, 0.0) + ms / steps
         ev.close()
     return dict(seconds=dt, ms_per_step=1e3 * dt / steps, tokens_per_s=w.tokens * steps / dt, stages=stages,
-                host=host, q=q, k=k, v=v, pool=pool, ws=ws)
+                host=host, q=q, k=kk, v=v, pool=pool, ws=ws)
 
 
 STAGE_KERNEL = {"score": "k_score", "route": "k_route_shared", "attend": "k_expert"}
@@ -351,6 +352,27 @@ def e2e(points, reps_mita: int = 5, reps_dense: int = 2):
     return out
 
 
+def ablation(steps: int, warmup: int):
+    """The pages' ablation with matched entries per query (republication,
+    "LRA" section): MiTA (m shared + s k routed entries) against routing only
+    (s k' routed entries, k' = k + m / s), on the long workloads."""
+    import torch
+    out = []
+    for name in LONG:
+        w = WORKLOADS[name]
+        inputs = make_device_inputs(w)
+        kk = w.k + w.m // w.s
+        full = time_workload(w, steps, warmup, inputs=inputs)
+        routed = time_workload(w, steps, warmup, variant="routed", k=kk, inputs=inputs)
+        out.append(dict(workload=name, entries_per_query=w.m + w.s * w.k, mita_tokens_per_s=full["tokens_per_s"],
+                        routed_only_k=kk, routed_only_tokens_per_s=routed["tokens_per_s"],
+                        speedup_of_shared_branch=routed["ms_per_step"] / full["ms_per_step"],
+                        mita_stages_ms=full["stages"], routed_only_stages_ms=routed["stages"]))
+        del inputs, full, routed
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -367,6 +389,8 @@ def main():
     ap.add_argument("--e2e", action="store_true",
                     help="instead: the three-layer, width-128 model with MiTA vs dense attention at 16K-1M")
     ap.add_argument("--e2e-max-n", type=int, default=1 << 20, help="largest sequence length of --e2e")
+    ap.add_argument("--ablation", action="store_true",
+                    help="instead: MiTA against the routing-only variant with matched entries per query")
     args = ap.parse_args()
     if args.ingest:
         ingest(*args.ingest, workload=args.workload, command=args.ingest_command)
@@ -380,6 +404,11 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(2)
+    if args.ablation:
+        print(json.dumps(dict(metric="MiTA vs routing-only forward tokens/s, entries per query matched",
+                              unit="tokens/s", n_gpus=1, dtype="bf16", data="synthetic",
+                              points=ablation(args.steps, args.warmup))), flush=True)
+        return
     if args.e2e:
         pts = [p for p in E2E_POINTS if p[0] <= args.e2e_max_n]
         print(json.dumps(dict(metric="3-layer width-128 model forward tokens/s, MiTA vs dense attention",

@@ -53,6 +53,7 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
   p.m = m; p.k = k; p.s = s;
   p.cscale = (float)(1.4426950408889634 / std::sqrt((double)d));
   p.cscale_sh = p.cscale;
+  p.shared = 1;
 
   // landmark scoring: rows per workgroup tile
   if (p.dtype == 0 || m <= 64) { p.sc_nw = 4; p.sc_ib = 1; }
@@ -181,7 +182,8 @@ mita_status run(const void* Q, const void* K, const void* V, void* O, mita_dtype
                 size_t workspace_bytes, void* stream, void* const* events) {
   mita_status st = validate(Q, K, V, O, dtype, B, H, N, d, pool, m, k, s, true);
   if (st != MITA_OK) return st;
-  if (variant != MITA_VARIANT_PAPER && variant != MITA_VARIANT_OFFICIAL) return MITA_ERR_PARAM;
+  if (variant != MITA_VARIANT_PAPER && variant != MITA_VARIANT_OFFICIAL && variant != MITA_VARIANT_ROUTED)
+    return MITA_ERR_PARAM;
   if (!workspace) return MITA_ERR_NULL;
   if ((uintptr_t)workspace & 15u) return MITA_ERR_PARAM;
   Plan p = make_plan(dtype, B, H, N, d, pool, m, k, s, (char*)workspace);
@@ -189,6 +191,7 @@ mita_status run(const void* Q, const void* K, const void* V, void* O, mita_dtype
   p.Q = Q; p.K = K; p.V = V; p.O = O;
   p.stream = (hipStream_t)stream;
   if (variant == MITA_VARIANT_OFFICIAL) p.cscale_sh = (float)(1.4426950408889634 / (double)d);
+  p.shared = variant == MITA_VARIANT_ROUTED ? 0 : 1;
   const Timer tm{events, p.stream};
 
   (void)hipGetLastError();  // clear any earlier sticky launch error
@@ -206,8 +209,8 @@ mita_status run(const void* Q, const void* K, const void* V, void* O, mita_dtype
   launch_final(p);
   tm.end(ST_FINAL);
   tm.begin(ST_ROUTE);
-  if (p.fast) launch_route_shared(p);
-  else launch_route(p);
+  if (p.fast && p.shared) launch_route_shared(p);
+  else launch_route(p);  // routing only (the shared part, if any, is done by the streaming attention)
   tm.end(ST_ROUTE);
   tm.begin(ST_BUCKET);
   launch_bucket(p);
@@ -222,7 +225,8 @@ mita_status run(const void* Q, const void* K, const void* V, void* O, mita_dtype
     if (dbg->topk) (void)hipMemcpyAsync(dbg->topk, p.topk, Mr * k * 4, hipMemcpyDeviceToDevice, p.stream);
     if (dbg->route)
       (void)hipMemcpyAsync(dbg->route, p.route, (size_t)p.BH * N * s * 4, hipMemcpyDeviceToDevice, p.stream);
-    if (dbg->vtilde) (void)hipMemcpyAsync(dbg->vtilde, p.vt32, Mr * d * 4, hipMemcpyDeviceToDevice, p.stream);
+    if (dbg->vtilde && p.shared)
+      (void)hipMemcpyAsync(dbg->vtilde, p.vt32, Mr * d * 4, hipMemcpyDeviceToDevice, p.stream);
     if (dbg->qtilde)
       (void)hipMemcpyAsync(dbg->qtilde, p.qt, Mr * d * p.esize, hipMemcpyDeviceToDevice, p.stream);
   }

@@ -29,7 +29,8 @@ __global__ __launch_bounds__(NW * 64) void k_attend(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ Qt,
     const T* __restrict__ VtT, const int32_t* __restrict__ topk, const int32_t* __restrict__ perm,
     const WorkItem* __restrict__ wl, const int* __restrict__ wl_count, float* __restrict__ part,
-    T* __restrict__ O, int N, int m, int k, int s, int slot, int BH, float cscale, float cscale_sh) {
+    T* __restrict__ O, int N, int m, int k, int s, int slot, int BH, int m_shared, float cscale,
+    float cscale_sh) {
   constexpr int NT = NW * 64;
   using TL = TileLayout<T, D>;
   __shared__ __align__(16) T smem[2 * TL::ELEMS];
@@ -64,10 +65,11 @@ __global__ __launch_bounds__(NW * 64) void k_attend(
     for (int cb = 0; cb < D / 16; ++cb) acc[b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // shared entries first (slot 0 only), then the expert's entries from a
+  // shared entries first (slot 0 only; none in the routing-only variant),
+  // then the expert's entries from a
   // fresh step, so every step has one logit scale (the shared logits may be
   // scaled differently, see mita_forward_variant)
-  const int m0 = SLOT0 ? m : 0;
+  const int m0 = SLOT0 ? m_shared : 0;
   const int ns = (m0 + 31) / 32, nsteps = ns + (k + 31) / 32;
   auto rowK = [&](int st) {
     return [=](int r) -> const T* {
@@ -154,11 +156,11 @@ static void launch_attend_t(const Plan& p) {
     if (t > 0)
       hipLaunchKernelGGL((k_attend<T, D, NW, IB, false>), dim3((unsigned)p.UB), dim3(NW * 64), 0, p.stream,
                          (const T*)p.Q, (const T*)p.K, (const T*)p.V, (const T*)p.qt, (const T*)p.vtT, p.topk, perm,
-                         wl, wlc, p.part, (T*)p.O, p.N, p.m, p.k, p.s, t, p.BH, p.cscale, p.cscale_sh);
+                         wl, wlc, p.part, (T*)p.O, p.N, p.m, p.k, p.s, t, p.BH, p.shared ? p.m : 0, p.cscale, p.cscale_sh);
     else
       hipLaunchKernelGGL((k_attend<T, D, NW, IB, true>), dim3((unsigned)p.UB), dim3(NW * 64), 0, p.stream,
                          (const T*)p.Q, (const T*)p.K, (const T*)p.V, (const T*)p.qt, (const T*)p.vtT, p.topk, perm,
-                         wl, wlc, p.part, (T*)p.O, p.N, p.m, p.k, p.s, t, p.BH, p.cscale, p.cscale_sh);
+                         wl, wlc, p.part, (T*)p.O, p.N, p.m, p.k, p.s, t, p.BH, p.shared ? p.m : 0, p.cscale, p.cscale_sh);
   }
 }
 

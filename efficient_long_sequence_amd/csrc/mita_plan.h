@@ -55,6 +55,7 @@ struct Plan {
   int ex_nw, ex_ib;  // expert kernel waves and 16-query blocks per query group
   float cscale;   // log2(e) / sqrt(d)
   float cscale_sh;  // log2(e) times the scale of the shared logits (1/sqrt(d) or 1/d)
+  int shared;       // 1: shared entries in the joint softmax; 0: routing-only variant
 
   // workspace regions
   void* qt;         // [BH, m, d] dtype

@@ -307,7 +307,8 @@ template <int IB, typename T, int D>
 __device__ __forceinline__ void expert_group(const Frag<T> (&qf)[IB][D / 32], const int (&qn)[IB], const T* Ks,
                                              const T* Vs, int Kp, int k, const Frag<T>& one, size_t row0,
                                              float* __restrict__ plse, typename PartT<T>::type* __restrict__ po,
-                                             T* __restrict__ O, int last, float cscale, int li, int lg) {
+                                             T* __restrict__ O, int merge_in, int last, float cscale, int li,
+                                             int lg) {
   using RL = Resident<T, D>;
   using P = typename PartT<T>::type;
   using PV = typename Vec4<P>::type;
@@ -337,8 +338,9 @@ __device__ __forceinline__ void expert_group(const Frag<T> (&qf)[IB][D / 32], co
     const float Zt = finish_z(Z[b], li);
     if (qn[b] < 0) continue;
     const size_t qrow = row0 + qn[b];
-    // merge with the stored partial: weights 2^lse of the two parts
-    const float la = plse[qrow];
+    // merge with the stored partial (none before the first routed slot of
+    // the routing-only variant): weights 2^lse of the two parts
+    const float la = merge_in ? plse[qrow] : M0;
     const float lb = M[b] + __builtin_amdgcn_logf(Zt);
     const float mx = fmaxf(la, lb);
     const float wa = __builtin_amdgcn_exp2f(la - mx), wb = __builtin_amdgcn_exp2f(lb - mx);
@@ -347,7 +349,8 @@ __device__ __forceinline__ void expert_group(const Frag<T> (&qf)[IB][D / 32], co
     P* o = po + qrow * D;
 #pragma unroll
     for (int cb = 0; cb < D / 16; ++cb) {
-      const PV h = *(const PV*)(o + part_pos<D>(lg, cb));
+      PV h = PV{};
+      if (merge_in) h = *(const PV*)(o + part_pos<D>(lg, cb));
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] = ca * (float)h[r] + cb_ * acc[b][cb][r];
@@ -369,14 +372,14 @@ __device__ __forceinline__ void expert_group(const Frag<T> (&qf)[IB][D / 32], co
 template <int IBX, typename T, int D, class QR>
 __device__ __forceinline__ void expert_blocks(const T* Qh, QR qrow, const T* Ks, const T* Vs, int Kp, int k,
                                               const Frag<T>& one, size_t row0, float* plse,
-                                              typename PartT<T>::type* po, T* O, int last, float cscale, int li,
-                                              int lg) {
+                                              typename PartT<T>::type* po, T* O, int merge_in, int last,
+                                              float cscale, int li, int lg) {
   Frag<T> qf[IBX][D / 32];
   int qn[IBX];
   load_queries<T, D, IBX>(qf, Qh, lg, qrow);
 #pragma unroll
   for (int b = 0; b < IBX; ++b) qn[b] = (int)qrow(b);
-  expert_group<IBX, T, D>(qf, qn, Ks, Vs, Kp, k, one, row0, plse, po, O, last, cscale, li, lg);
+  expert_group<IBX, T, D>(qf, qn, Ks, Vs, Kp, k, one, row0, plse, po, O, merge_in, last, cscale, li, lg);
 }
 
 template <typename T, int D, int NW, int IB>
@@ -384,7 +387,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_expert(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const int32_t* __restrict__ topk,
     const int32_t* __restrict__ perm, const WorkItem* __restrict__ wl, const int* __restrict__ wl_count,
     float* __restrict__ plse, typename PartT<T>::type* __restrict__ po, T* __restrict__ O, int N, int m, int k,
-    int last, float cscale) {
+    int merge_in, int last, float cscale) {
   using RL = Resident<T, D>;
   extern __shared__ __align__(16) unsigned char smem[];
   // The list holds the largest items first; the hardware deals workgroups
@@ -431,7 +434,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_expert(
       qn[b] = s_q[gi * GQ + b * 16 + li];
     }
     if (gi + NW < nfull) load_queries<T, D, IB>(qnx, Qh, lg, group_rows(gi + NW));
-    expert_group<IB, T, D>(qf, qn, Ks, Vs, Kp, k, one, row0, plse, po, O, last, cscale, li, lg);
+    expert_group<IB, T, D>(qf, qn, Ks, Vs, Kp, k, one, row0, plse, po, O, merge_in, last, cscale, li, lg);
   }
   // ... then the rest in blocks of 16 queries dealt to the waves in turn, so
   // a short remainder keeps every wave busy on narrower groups
@@ -443,13 +446,13 @@ __global__ __launch_bounds__(NW * 64, 2) void k_expert(
     return l < it.count ? s_q[l] : -1;
   };
   if constexpr (IB >= 4) {
-    if (mine == 4) expert_blocks<4, T, D>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, last, cscale, li, lg);
-    if (mine == 3) expert_blocks<3, T, D>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, last, cscale, li, lg);
+    if (mine == 4) expert_blocks<4, T, D>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, merge_in, last, cscale, li, lg);
+    if (mine == 3) expert_blocks<3, T, D>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, merge_in, last, cscale, li, lg);
   }
   if constexpr (IB >= 2) {
-    if (mine == 2) expert_blocks<2, T, D>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, last, cscale, li, lg);
+    if (mine == 2) expert_blocks<2, T, D>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, merge_in, last, cscale, li, lg);
   }
-  if (mine == 1) expert_blocks<1, T, D>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, last, cscale, li, lg);
+  if (mine == 1) expert_blocks<1, T, D>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, merge_in, last, cscale, li, lg);
 }
 
 // ---------------------------------------------------------------------------
@@ -502,7 +505,7 @@ static void launch_expert_t(const Plan& p) {
     const WorkItem* wl = p.wl + (size_t)t * p.UB;
     hipLaunchKernelGGL(fn, dim3((unsigned)(p.UB + 8)), dim3(NW * 64), lds, p.stream, (const T*)p.Q, (const T*)p.K,
                        (const T*)p.V, p.topk, perm, wl, p.wl_count + t, p.plse, (typename PartT<T>::type*)p.po, (T*)p.O, p.N, p.m, p.k,
-                       t == p.s - 1 ? 1 : 0, p.cscale);
+                       (t > 0 || p.shared) ? 1 : 0, t == p.s - 1 ? 1 : 0, p.cscale);
   }
 }
 

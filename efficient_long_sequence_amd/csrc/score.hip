@@ -133,7 +133,9 @@ __global__ __launch_bounds__(256) void k_tau(const float* __restrict__ gmax, flo
 template <typename T, int NW, int IB>
 constexpr int score_waves_per_eu() { return (sizeof(T) == 2 && NW == 8 && IB == 1) ? 4 : 2; }
 
-template <typename T, int D, int NW, int IB, bool DENSE>
+// SHARED = false (routing-only variant): keys only, no softmax, no P.V and no
+// shared-value partials; the scores feed the candidates alone.
+template <typename T, int D, int NW, int IB, bool DENSE, bool SHARED>
 __global__ __launch_bounds__(NW * 64, (score_waves_per_eu<T, NW, IB>())) void k_score(
     const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ Qt,
     const float* __restrict__ tau_in, const float* __restrict__ mhat_in, float* __restrict__ vpart,
@@ -194,7 +196,7 @@ __global__ __launch_bounds__(NW * 64, (score_waves_per_eu<T, NW, IB>())) void k_
     return [=](int r) -> const T* { const int j = j0 + r; return j < j_end ? Vh + (size_t)j * D : nullptr; };
   };
 
-  TileLoader<T, D, NT, true> ld;
+  TileLoader<T, D, NT, SHARED> ld;
   const int nsteps = (j_end - j_begin + 31) / 32;
   ld.load(rowK(j_begin), rowV(j_begin));
   ld.store(buf0, buf0 + TL::K_ELEMS);
@@ -207,7 +209,7 @@ __global__ __launch_bounds__(NW * 64, (score_waves_per_eu<T, NW, IB>())) void k_
     if (more) ld.load(rowK(j0 + 32), rowV(j0 + 32));
     StepFrags<T, D> f;
     f.load_keys(cur, li, lg);
-    f.load_vals(cur + TL::K_ELEMS, li, lg);
+    if constexpr (SHARED) f.load_vals(cur + TL::K_ELEMS, li, lg);
     const int nv = min(32, j_end - j0);
     // per row block: every score of a small head is a candidate (DENSE);
     // otherwise the scores >= tau are staged, one LDS reservation per lane
@@ -250,23 +252,31 @@ __global__ __launch_bounds__(NW * 64, (score_waves_per_eu<T, NW, IB>())) void k_
         wcnt = off;
       }
     };
-    if (nv == 32) attn_step<IB, false>(f, one, qf, nv, lg, cscale, M, Z, acc, cands);
-    else attn_step<IB, true>(f, one, qf, nv, lg, cscale, M, Z, acc, cands);
+    if constexpr (SHARED) {
+      if (nv == 32) attn_step<IB, false>(f, one, qf, nv, lg, cscale, M, Z, acc, cands);
+      else attn_step<IB, true>(f, one, qf, nv, lg, cscale, M, Z, acc, cands);
+    } else {
+      if (nv == 32) score_step<IB, false>(f, qf, nv, lg, cands);
+      else score_step<IB, true>(f, qf, nv, lg, cands);
+    }
     if (more) ld.store(nxt, nxt + TL::K_ELEMS);
     __syncthreads();
   }
 
   // partial shared values of this chunk: (max, normaliser, 2 pad, unnormalised sums)
+  if constexpr (SHARED) {
 #pragma unroll
-  for (int b = 0; b < IB; ++b) {
-    const float Zt = finish_z(Z[b], li);
-    const int row = rbase + b * 16 + li;
-    if (row < m) {
-      float* dst = vpart + (((size_t)bh * m + row) * C + ch) * (D + 4);
-      if (lg == 0) { dst[0] = M[b]; dst[1] = Zt; }
+    for (int b = 0; b < IB; ++b) {
+      const float Zt = finish_z(Z[b], li);
+      const int row = rbase + b * 16 + li;
+      if (row < m) {
+        float* dst = vpart + (((size_t)bh * m + row) * C + ch) * (D + 4);
+        if (lg == 0) { dst[0] = M[b]; dst[1] = Zt; }
 #pragma unroll
-      for (int cb = 0; cb < D / 16; ++cb)
-        *(float4*)(dst + 4 + cb * 16 + 4 * lg) = make_float4(acc[b][cb][0], acc[b][cb][1], acc[b][cb][2], acc[b][cb][3]);
+        for (int cb = 0; cb < D / 16; ++cb)
+          *(float4*)(dst + 4 + cb * 16 + 4 * lg) =
+              make_float4(acc[b][cb][0], acc[b][cb][1], acc[b][cb][2], acc[b][cb][3]);
+      }
     }
   }
 
@@ -313,7 +323,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void k_final(const float* __restrict__ vpart, const uint64_t* __restrict__ cand,
                                                const int* __restrict__ cand_cnt, int32_t* __restrict__ topk,
                                                float* __restrict__ vt32, T* __restrict__ vtT, int* __restrict__ fail,
-                                               int N, int k, int C, int capg, int dense) {
+                                               int N, int k, int C, int capg, int dense, int shared) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint64_t* a = (uint64_t*)smem;
   __shared__ float red[256];
@@ -322,37 +332,39 @@ __global__ __launch_bounds__(256) void k_final(const float* __restrict__ vpart, 
   const int tid = threadIdx.x;
   constexpr int NG = 256 / D;  // chunk groups
   const float* pr = vpart + r * C * (D + 4);
-  // largest chunk maximum
-  float mx = M0;
-  for (int c = tid; c < C; c += 256) mx = fmaxf(mx, pr[(size_t)c * (D + 4)]);
-  red[tid] = mx;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
+  if (shared) {
+    // shared values (not used by the routing-only variant): largest chunk maximum
+    float mx = M0;
+    for (int c = tid; c < C; c += 256) mx = fmaxf(mx, pr[(size_t)c * (D + 4)]);
+    red[tid] = mx;
     __syncthreads();
-  }
-  const float Mx = red[0];
-  __syncthreads();
-  // rescaled sums, chunk groups in parallel (rescaled-sum identity)
-  {
-    const int e = tid % D, cg = tid / D;
-    float zs = 0.f, sv = 0.f;
-    for (int c = cg; c < C; c += NG) {
-      const float* q = pr + (size_t)c * (D + 4);
-      const float w = __builtin_amdgcn_exp2f(q[0] - Mx);
-      zs += q[1] * w;
-      sv += q[4 + e] * w;
+    for (int off = 128; off > 0; off >>= 1) {
+      if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
+      __syncthreads();
     }
-    red[tid] = sv;
-    if (e == 0) zred[cg] = zs;
-  }
-  __syncthreads();
-  if (tid < D) {
-    float sv = 0.f, zs = 0.f;
-    for (int g = 0; g < NG; ++g) { sv += red[g * D + tid]; zs += zred[g]; }
-    const float v = sv / zs;
-    vt32[r * D + tid] = v;
-    vtT[r * D + tid] = from_f32<T>(v);
+    const float Mx = red[0];
+    __syncthreads();
+    // rescaled sums, chunk groups in parallel (rescaled-sum identity)
+    {
+      const int e = tid % D, cg = tid / D;
+      float zs = 0.f, sv = 0.f;
+      for (int c = cg; c < C; c += NG) {
+        const float* q = pr + (size_t)c * (D + 4);
+        const float w = __builtin_amdgcn_exp2f(q[0] - Mx);
+        zs += q[1] * w;
+        sv += q[4 + e] * w;
+      }
+      red[tid] = sv;
+      if (e == 0) zred[cg] = zs;
+    }
+    __syncthreads();
+    if (tid < D) {
+      float sv = 0.f, zs = 0.f;
+      for (int g = 0; g < NG; ++g) { sv += red[g * D + tid]; zs += zred[g]; }
+      const float v = sv / zs;
+      vt32[r * D + tid] = v;
+      vtT[r * D + tid] = from_f32<T>(v);
+    }
   }
   const int cnt = dense ? N : cand_cnt[r];
   if (cnt < k || cnt > capg) {
@@ -470,25 +482,31 @@ static void launch_score_t(const Plan& p) {
   }
 }
 
-template <typename T, int D, int NW, int IB>
-static void launch_score_main(const Plan& p) {
+template <typename T, int D, int NW, int IB, bool SHARED>
+static void launch_score_s(const Plan& p) {
   using TL = TileLayout<T, D>;
   constexpr int R = NW * 16 * IB;
   const bool dense = p.dense != 0;
   const size_t lds = 2 * TL::ELEMS * sizeof(T) + (dense ? 0 : (size_t)p.cb * 8 + 2 * R * 4 + NW * 4);
   dim3 grid((unsigned)p.C, (unsigned)p.sc_rt, (unsigned)p.BH);
   if (dense) {
-    hipLaunchKernelGGL((k_score<T, D, NW, IB, true>), grid, dim3(NW * 64), lds, p.stream, (const T*)p.K,
+    hipLaunchKernelGGL((k_score<T, D, NW, IB, true, SHARED>), grid, dim3(NW * 64), lds, p.stream, (const T*)p.K,
                        (const T*)p.V, (const T*)p.qt, nullptr, nullptr, p.vpart, p.cand, p.cand_cnt, p.N, p.m, p.L,
                        p.C, p.capg, 0, p.cscale);
     return;
   }
   if (lds > 65536)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_score<T, D, NW, IB, false>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_score<T, D, NW, IB, false, SHARED>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL((k_score<T, D, NW, IB, false>), grid, dim3(NW * 64), lds, p.stream, (const T*)p.K,
+  hipLaunchKernelGGL((k_score<T, D, NW, IB, false, SHARED>), grid, dim3(NW * 64), lds, p.stream, (const T*)p.K,
                      (const T*)p.V, (const T*)p.qt, p.tau, p.force_fallback ? nullptr : p.mhat, p.vpart, p.cand,
                      p.cand_cnt, p.N, p.m, p.L, p.C, p.capg, p.cb, p.cscale);
+}
+
+template <typename T, int D, int NW, int IB>
+static void launch_score_main(const Plan& p) {
+  if (p.shared) launch_score_s<T, D, NW, IB, true>(p);
+  else launch_score_s<T, D, NW, IB, false>(p);
 }
 
 template <typename T, int D>
@@ -498,7 +516,7 @@ static void launch_final_t(const Plan& p) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_final<T, D>), hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)lds);
   hipLaunchKernelGGL((k_final<T, D>), dim3((unsigned)(p.BH * p.m)), dim3(256), lds, p.stream, p.vpart, p.cand,
-                     p.cand_cnt, p.topk, p.vt32, (T*)p.vtT, p.fail, p.N, p.k, p.C, p.capg, p.dense);
+                     p.cand_cnt, p.topk, p.vt32, (T*)p.vtT, p.fail, p.N, p.k, p.C, p.capg, p.dense, p.shared);
   if (!p.dense) {
     const size_t lds2 = (size_t)next_pow2(2 * p.k + 256) * 8;
     hipLaunchKernelGGL((k_fallback<T, D>), dim3((unsigned)(p.BH * p.m)), dim3(256), lds2, p.stream,

@@ -388,4 +388,24 @@ struct NoHook {
   __device__ __forceinline__ void operator()(int, const float*, float) const {}
 };
 
+// Scores of one 32-entry step for IB blocks and the hook on(b, scores,
+// lane_max), with no softmax (keys only; the step's value operands are not
+// needed).  MASK as for attn_step.
+template <int IB, bool MASK, typename T, int D, class On>
+__device__ __forceinline__ void score_step(const StepFrags<T, D>& f, const Frag<T> (&qf)[IB][D / 32], int nv,
+                                           int lg, On on) {
+  float sc[IB][8];
+#pragma unroll
+  for (int b = 0; b < IB; ++b) step_scores(f, qf[b], sc[b]);
+  if constexpr (MASK) {
+#pragma unroll
+    for (int b = 0; b < IB; ++b)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (slot_key(t, lg) >= nv) sc[b][t] = -INFINITY;
+  }
+#pragma unroll
+  for (int b = 0; b < IB; ++b) on(b, sc[b], max8(sc[b]));
+}
+
 }  // namespace mita

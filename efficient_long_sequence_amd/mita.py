@@ -149,10 +149,12 @@ def dense_attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, out: torc
     return O
 
 
-# Scale of the shared logits q . q~ in the joint softmax: "paper" = 1/sqrt(d)
-# like every other logit; "official" = 1/d, the authors' code path (MiTA
-# tutorial, chapter 8, third check).
-VARIANTS = {"paper": 0, "official": 1}
+# Entries and scales of the joint softmax: "paper" = shared logits 1/sqrt(d)
+# like every other logit; "official" = shared logits 1/d, the authors' code
+# path (MiTA tutorial, chapter 8, third check); "routed" = the routing-only
+# ablation with no shared entries (the pages match entries per query by
+# passing k + m / s as k).
+VARIANTS = {"paper": 0, "official": 1, "routed": 2}
 
 
 def official_params(grid_h: int, grid_w: int, pool_size: int, kv_topk: int):
@@ -172,7 +174,8 @@ def forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, pool, k: int, s: 
     Q, K, V: contiguous device tensors [B, H, N, d] (bf16 or fp32).
     pool: (grid_h, grid_w, land_h, land_w); m = land_h * land_w unless given
     (a mismatching m is passed through so the library can reject it).
-    variant: "paper" or "official" (scale of the shared logits, see VARIANTS).
+    variant: "paper", "official" or "routed" (see VARIANTS); with "routed" the
+    debug v~ is not written (left as allocated).
     Returns O, or (O, DebugOut) when ``debug``.
     """
     L = lib()
@@ -194,7 +197,7 @@ def forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, pool, k: int, s: 
         dbg = DebugOut(
             topk=torch.empty((B, H, m, k), dtype=torch.int32, device=dev),
             route=torch.empty((B, H, N, s), dtype=torch.int32, device=dev),
-            vtilde=torch.empty((B, H, m, d), dtype=torch.float32, device=dev),
+            vtilde=torch.zeros((B, H, m, d), dtype=torch.float32, device=dev),
             qtilde=torch.empty((B, H, m, d), dtype=Q.dtype, device=dev),
         )
         dbg_struct = Debug(dbg.topk.data_ptr(), dbg.route.data_ptr(), dbg.vtilde.data_ptr(),

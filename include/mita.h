@@ -109,7 +109,7 @@ mita_status mita_forward_timed(const void* Q, const void* K, const void* V, void
                                int m, int k, int s, const mita_debug* dbg, void* workspace,
                                size_t workspace_bytes, void* stream, void* const* events);
 
-/* Scale of the m shared logits q . q~_i in the step-6 softmax. */
+/* Which entries and logit scales the step-6 softmax uses. */
 typedef enum {
   /* 1/sqrt(d), like every other logit: the paper's eqs. 5-12 as the MiTA
    * tutorial's chapter 4 states them. */
@@ -118,7 +118,13 @@ typedef enum {
    * then applies the d^-1/2 logit scale (MiTA tutorial, chapter 8, third
    * check).  Routed logits stay q . k / sqrt(d); pooling, landmark scores,
    * top-k, shared values and routing are those of MITA_VARIANT_PAPER. */
-  MITA_VARIANT_OFFICIAL = 1
+  MITA_VARIANT_OFFICIAL = 1,
+  /* Routing-only ablation (no shared branch): each query's softmax runs over
+   * the s*k keys of its routed experts alone, with 1/sqrt(d).  Pooling,
+   * landmark top-k and routing are unchanged; shared values are not computed
+   * and dbg->vtilde is not written.  The pages' ablation matches the entries
+   * per query (MiTA republication, "LRA" section): pass k + m/s as k. */
+  MITA_VARIANT_ROUTED = 2
 } mita_variant;
 
 /* mita_forward / mita_forward_timed with the shared-logit scale chosen by

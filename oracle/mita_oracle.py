@@ -47,6 +47,10 @@ Readings where the pages are silent (each listed in the design notes):
   d^-1/2 before the d^-1/2 logit scale, so its shared logits are q . q~ / d
   while routed logits stay q . k / sqrt(d): ``variant="official"`` in
   attend() and forward() follows that path and changes nothing else.
+* ``variant="routed"`` is the routing-only ablation the pages compare with
+  (republication, "LRA" section): no shared entries, the softmax runs over
+  the s k routed keys alone; entries per query are matched by the caller
+  (k + m / s).
 
 Parity pins (tests/test_oracle_*.py): the tutorial's worked softmax fact
 (ch.1), the merge identity (ch.4), the m = k = N counterexample value
@@ -305,9 +309,10 @@ def attend(Q, K, V, Qt, Vt, I, e, R=None, counter: DotCounter | None = None,
     of step 5) is given, the shared logits reuse it instead of recomputing.
     variant="official" divides the m shared logits by d instead of sqrt(d)
     (tutorial ch.8, third check); the routed logits keep 1/sqrt(d).
+    variant="routed" drops the m shared entries (routing-only ablation).
     """
-    if variant not in ("paper", "official"):
-        raise ValueError("variant must be 'paper' or 'official'")
+    if variant not in ("paper", "official", "routed"):
+        raise ValueError("variant must be 'paper', 'official' or 'routed'")
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
@@ -328,13 +333,16 @@ def attend(Q, K, V, Qt, Vt, I, e, R=None, counter: DotCounter | None = None,
         raw = Q[ns] @ Ks[m:].T / sq
         if counter is not None:
             counter.query_raw += raw.size
-        shared = (R[ns] if R is not None else Q[ns] @ Qt.T) / sh
-        l = np.concatenate([shared, raw], axis=1)
+        if variant == "routed":
+            l, vals = raw, Vs[m:]
+        else:
+            shared = (R[ns] if R is not None else Q[ns] @ Qt.T) / sh
+            l, vals = np.concatenate([shared, raw], axis=1), Vs
         w = np.exp(l - l.max(axis=1, keepdims=True))
         w /= w.sum(axis=1, keepdims=True)
         if check_weights:
             assert np.allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-12)
-        O[ns] = w @ Vs
+        O[ns] = w @ vals
     return O
 
 

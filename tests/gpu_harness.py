@@ -159,9 +159,10 @@ def check_head(Qh, Kh, Vh, pool, k, s, dtype, gpu: dict, bh, stats: Stats,
                 row_exempt[r] = check_topk_row(S[j], I_gpu[r], k)
                 stats.rows += 1
                 stats.rows_exempt += int(row_exempt[r])
-    dv = np.abs(gpu["vtilde"][b, h][rows] - Vt[rows])
-    stats.vt_max = max(stats.vt_max, float(dv.max()))
-    stats.vt_mean = max(stats.vt_mean, float(dv.mean()))
+    if variant != "routed":  # the routing-only variant computes no shared values
+        dv = np.abs(gpu["vtilde"][b, h][rows] - Vt[rows])
+        stats.vt_max = max(stats.vt_max, float(dv.max()))
+        stats.vt_mean = max(stats.vt_mean, float(dv.mean()))
     # routing
     qs = np.arange(N) if queries is None else np.asarray(queries)
     R = Qh[qs] @ Qt.T

@@ -94,7 +94,7 @@ def test_forward_variant_rejects_unknown_variant_before_any_launch():
     L = mita.lib()
     P = mita.Pool(1, 4096, 1, 64)
     args = (A, A, A, A, mita.BF16, 1, 2, 4096, 64, P, 64, 64, 1)
-    assert L.mita_forward_variant(*args, 2, None, A, 1 << 40, None, None) == 3
+    assert L.mita_forward_variant(*args, 3, None, A, 1 << 40, None, None) == 3
     assert L.mita_forward_variant(*args, -1, None, A, 1 << 40, None, None) == 3
     # the shape checks run first, with the same codes as mita_forward
     bad = (A, A, A, A, mita.BF16, 1, 2, 4095, 64, P, 64, 64, 1)

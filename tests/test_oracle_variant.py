@@ -97,3 +97,44 @@ def test_variant_pins_catch_planted_mistakes(monkeypatch, mistake):
     monkeypatch.setattr(mo, "attend", mistake)
     with pytest.raises(AssertionError):
         test_official_closed_form_k_equals_n(4, 8, 2, 2, 4)
+
+
+# ---------------------------------------------------------------------------
+# routing-only ablation: no shared entries
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("gh,gw,lh,lw,d", [(1, 37, 1, 1, 8), (4, 8, 2, 2, 4), (1, 50, 1, 5, 16)])
+def test_routed_closed_form_is_dense_attention(gh, gw, lh, lw, d):
+    """k = N, s = 1 and no shared entries: every query attends to all N keys,
+    which is plain dense attention over K and V."""
+    N = gh * gw
+    rng = np.random.default_rng(11 * N + d)
+    Q, K, V = _rand_head(rng, N, d)
+    r = mo.forward(Q, K, V, gh, gw, lh, lw, N, 1, dtype="bf16", variant="routed")
+    np.testing.assert_allclose(r.O, _dense_fp64(Q, K, V), rtol=1e-11, atol=1e-12)
+
+
+def test_routed_softmax_runs_over_the_routed_keys_only():
+    rng = np.random.default_rng(5)
+    Q, K, V = _rand_head(rng, 96, 8)
+    a = mo.forward(Q, K, V, 1, 96, 1, 6, 5, 2, dtype="bf16")
+    b = mo.forward(Q, K, V, 1, 96, 1, 6, 5, 2, dtype="bf16", variant="routed")
+    for x, y in ((a.Qt, b.Qt), (a.I, b.I), (a.e, b.e)):
+        np.testing.assert_array_equal(x, y)
+    for n in (0, 41, 95):
+        sel = np.concatenate([b.I[e] for e in b.e[n]])
+        logits = K[sel] @ Q[n] / math.sqrt(8.0)
+        w = np.exp(logits - logits.max())
+        np.testing.assert_allclose(b.O[n], (w / w.sum()) @ V[sel], rtol=1e-12, atol=1e-13)
+    assert np.abs(a.O - b.O).max() > 1e-3
+
+
+def _routed_keeps_shared(*a, **kw):
+    if kw.get("variant") == "routed":
+        kw["variant"] = "paper"
+    return _orig_attend(*a, **kw)
+
+
+def test_routed_pin_catches_a_kept_shared_branch(monkeypatch):
+    monkeypatch.setattr(mo, "attend", _routed_keeps_shared)
+    with pytest.raises(AssertionError):
+        test_routed_closed_form_is_dense_attention(4, 8, 2, 2, 4)
