@@ -227,136 +227,6 @@ __device__ __forceinline__ float max8(const float* s) {
   return fmaxf(m, s[7]);
 }
 
-// Key and value operands of one 32-entry step, loaded separately so a
-// pipelined loop can hold the next step's keys beside the current values.
-template <typename T, int D>
-struct KFrags {
-  Frag<T> ka[2][D / 32];
-};
-template <typename T, int D>
-struct VFrags {
-  Frag<T> va[D / 16];
-};
-
-template <typename T, int D>
-__device__ __forceinline__ void tile_scores(const KFrags<T, D>& kf, const Frag<T>* qf, float* sc) {
-  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int dc = 0; dc < D / 32; ++dc) {
-    mma16(s0, kf.ka[0][dc], qf[dc]);
-    mma16(s1, kf.ka[1][dc], qf[dc]);
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) { sc[r] = s0[r]; sc[4 + r] = s1[r]; }
-}
-
-// Raise block b's running maximum when its own maximum exceeds it by more
-// than THRESH binades (rescaling the normaliser and accumulator).
-template <int D>
-__device__ __forceinline__ void rescale_if_needed(float xm, float& M, f32x4& Z, f32x4* acc) {
-  const float gm = wave_max_groups(xm);
-  if (gm > M + THRESH) {
-    const float alpha = __builtin_amdgcn_exp2f(M - gm);
-    Z[0] *= alpha;
-#pragma unroll
-    for (int cb = 0; cb < D / 16; ++cb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[cb][r] *= alpha;
-    M = gm;
-  }
-}
-
-// Probabilities of one block (no rescale check) and their P.V product.
-template <typename T, int D>
-__device__ __forceinline__ void probs_pv(const Frag<T>* va, const Frag<T>& one, const float* sc, float cscale,
-                                         float M, f32x4& Z, f32x4* acc) {
-  const float nm = -M;
-  float p[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t], cscale, nm));
-  Frag<T> pf;
-  set8(pf, p);
-#pragma unroll
-  for (int cb = 0; cb < D / 16; ++cb) mma16(acc[cb], va[cb], pf);
-  mma16(Z, one, pf);
-}
-
-// Whole pass over E resident entries, software-pipelined: each step first
-// runs the short branchy part for all row blocks (maxima, the hook
-// on(b, scores, lane max, x0), one rescale check), then one straight-line
-// section where block b's score tile of the next step goes to the matrix
-// cores while the vector units turn block b's current scores into
-// probabilities.  With no branch inside it the compiler interleaves the two
-// units within a wave.  loadk(kf, x0) / loadv(vf, x0) fetch the operands of
-// the step at entry x0.
-template <int IB, typename T, int D, class LK, class LV, class On>
-__device__ __forceinline__ void attn_run(LK loadk, LV loadv, int E, const Frag<T>& one,
-                                         const Frag<T> (&qf)[IB][D / 32], int lg, float cscale, float (&M)[IB],
-                                         f32x4 (&Z)[IB], f32x4 (&acc)[IB][D / 16], On on) {
-  const int nsteps = (E + 31) / 32;
-  KFrags<T, D> kf;
-  loadk(kf, 0);
-  float sc[IB][8];
-#pragma unroll
-  for (int b = 0; b < IB; ++b) tile_scores(kf, qf[b], sc[b]);
-  for (int st = 0; st < nsteps; ++st) {
-    const int x0 = st * 32;
-    const bool last = st + 1 == nsteps;
-    VFrags<T, D> vf;
-    loadv(vf, x0);
-    if (last) {
-      const int nv = E - x0;
-      if (nv < 32) {
-#pragma unroll
-        for (int b = 0; b < IB; ++b)
-#pragma unroll
-          for (int t = 0; t < 8; ++t)
-            if (slot_key(t, lg) >= nv) sc[b][t] = -INFINITY;
-      }
-    } else {
-      loadk(kf, x0 + 32);
-    }
-    float xm[IB];
-    bool need = false;
-#pragma unroll
-    for (int b = 0; b < IB; ++b) {
-      const float mx = max8(sc[b]);
-      on(b, sc[b], mx, x0);
-      xm[b] = mx * cscale;
-      need |= xm[b] > M[b] + THRESH;
-    }
-    if (wave_any(need)) {
-#pragma unroll
-      for (int b = 0; b < IB; ++b) rescale_if_needed<D>(xm[b], M[b], Z[b], acc[b]);
-    }
-    if (!last) {
-#pragma unroll
-      for (int b = 0; b < IB; ++b) {
-        float cur[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) cur[t] = sc[b][t];
-        tile_scores(kf, qf[b], sc[b]);
-        probs_pv<T, D>(vf.va, one, cur, cscale, M[b], Z[b], acc[b]);
-      }
-      // ask the scheduler to alternate one matrix instruction with three
-      // vector instructions over the section
-      constexpr int NMFMA = IB * (2 * (D / 32) * (sizeof(T) == 2 ? 1 : 8) + (D / 16 + 1) * (sizeof(T) == 2 ? 1 : 8));
-#pragma unroll
-      for (int i = 0; i < NMFMA; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < IB; ++b) probs_pv<T, D>(vf.va, one, sc[b], cscale, M[b], Z[b], acc[b]);
-    }
-  }
-}
-
-struct NoHook4 {
-  __device__ __forceinline__ void operator()(int, const float*, float, int) const {}
-};
-
 // One 32-entry step for IB blocks of 16 queries: the score tiles of all
 // blocks first (so one block's softmax overlaps the others' matrix work),
 // then, per block, the hook `on(b, scores, lane_max)` (candidates, routing)
