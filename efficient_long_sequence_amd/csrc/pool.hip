@@ -45,12 +45,25 @@ __global__ __launch_bounds__(256) void k_pool(const T* __restrict__ Q, T* __rest
 #pragma unroll
   for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
   const T* base = Q + (size_t)bh * N * D + chunk * EPC;
-  for (int w = tslot; w < W; w += TPP) {
-    const long long n = (long long)(r0 + w / wc) * gw + c0 + w % wc;
-    const uint4 raw = *(const uint4*)(base + (size_t)n * D);
-    const T* v = (const T*)&raw;
+  // four independent loads in flight per thread before they are accumulated
+  constexpr int U = 4;
+  for (int w0 = tslot; w0 < W; w0 += U * TPP) {
+    uint4 raw[U];
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[e] += (double)(float)v[e];
+    for (int u = 0; u < U; ++u) {
+      const int w = w0 + u * TPP;
+      raw[u] = make_uint4(0, 0, 0, 0);
+      if (w < W) {
+        const long long n = (long long)(r0 + w / wc) * gw + c0 + w % wc;
+        raw[u] = *(const uint4*)(base + (size_t)n * D);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const T* v = (const T*)&raw[u];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[e] += (double)(float)v[e];
+    }
   }
   __shared__ double red[256][EPC];
 #pragma unroll

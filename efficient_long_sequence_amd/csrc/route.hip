@@ -209,21 +209,29 @@ __global__ __launch_bounds__(1024) void k_scan(const int* __restrict__ counts, i
   }
 }
 
-// Each workgroup counts its 256 queries per expert in LDS, reserves one
+// Each workgroup counts its SC_QPW queries per expert in LDS, reserves one
 // contiguous range per expert with a single global atomic, and writes the
 // queries there (queries that share an expert in a block cost one atomic).
+constexpr int SC_QPT = 8;              // queries per thread
+constexpr int SC_QPW = 256 * SC_QPT;   // queries per workgroup
+
 __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ route, const int* __restrict__ gpre,
                                                  int* __restrict__ cursor, int32_t* __restrict__ perm, int N,
                                                  int m, int s, int BH) {
   extern __shared__ int s_cnt[];  // [m] counts, then [m] bases
   int* s_base = s_cnt + m;
   const int bh = blockIdx.y;
-  const int n = blockIdx.x * 256 + threadIdx.x;
+  const int n0 = blockIdx.x * SC_QPW + threadIdx.x;
   for (int t = 0; t < s; ++t) {
     for (int x = threadIdx.x; x < m; x += 256) s_cnt[x] = 0;
     __syncthreads();
-    const int e = n < N ? route[((size_t)bh * N + n) * s + t] : -1;
-    const int r = e >= 0 ? atomicAdd(s_cnt + e, 1) : 0;
+    int e[SC_QPT], r[SC_QPT];
+#pragma unroll
+    for (int u = 0; u < SC_QPT; ++u) {
+      const int n = n0 + u * 256;
+      e[u] = n < N ? route[((size_t)bh * N + n) * s + t] : -1;
+      r[u] = e[u] >= 0 ? atomicAdd(s_cnt + e[u], 1) : 0;
+    }
     __syncthreads();
     const size_t xb = ((size_t)t * BH + bh) * m;
     for (int x = threadIdx.x; x < m; x += 256) {
@@ -231,7 +239,9 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ rou
       if (c) s_base[x] = gpre[xb + x] + atomicAdd(cursor + xb + x, c);
     }
     __syncthreads();
-    if (e >= 0) perm[(size_t)t * BH * N + s_base[e] + r] = n;
+#pragma unroll
+    for (int u = 0; u < SC_QPT; ++u)
+      if (e[u] >= 0) perm[(size_t)t * BH * N + s_base[e[u]] + r[u]] = n0 + u * 256;
     __syncthreads();
   }
 }
@@ -269,7 +279,7 @@ void launch_bucket(const Plan& p) {
   const int E = p.BH * p.m;
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, p.stream, p.counts, p.gpre, p.wl, p.wl_count, E, p.m, p.s,
                      p.T, p.UB);
-  dim3 grid((unsigned)((p.N + 255) / 256), (unsigned)p.BH);
+  dim3 grid((unsigned)((p.N + SC_QPW - 1) / SC_QPW), (unsigned)p.BH);
   hipLaunchKernelGGL(k_scatter, grid, dim3(256), (size_t)2 * p.m * sizeof(int), p.stream, p.route, p.gpre, p.cursor,
                      p.perm, p.N, p.m, p.s, p.BH);
 }
