@@ -336,18 +336,17 @@ __global__ __launch_bounds__(256) void k_final(const float* __restrict__ vpart, 
     // shared values (not used by the routing-only variant): largest chunk maximum
     float mx = M0;
     for (int c = tid; c < C; c += 256) mx = fmaxf(mx, pr[(size_t)c * (D + 4)]);
-    red[tid] = mx;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    if ((tid & 63) == 0) red[tid >> 6] = mx;
     __syncthreads();
-    for (int off = 128; off > 0; off >>= 1) {
-      if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
-      __syncthreads();
-    }
-    const float Mx = red[0];
+    const float Mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     __syncthreads();
     // rescaled sums, chunk groups in parallel (rescaled-sum identity)
     {
       const int e = tid % D, cg = tid / D;
       float zs = 0.f, sv = 0.f;
+#pragma unroll 4
       for (int c = cg; c < C; c += NG) {
         const float* q = pr + (size_t)c * (D + 4);
         const float w = __builtin_amdgcn_exp2f(q[0] - Mx);
@@ -388,14 +387,24 @@ __global__ __launch_bounds__(256) void k_final(const float* __restrict__ vpart, 
       if ((key & mask) == prefix) atomicAdd(hist + ((int)(key >> shift) & 255), 1);
     }
     __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {  // suffix sums over the buckets
-      const int v = tid + off < 256 ? hist[tid + off] : 0;
-      __syncthreads();
-      hist[tid] += v;
-      __syncthreads();
+    if (tid < 64) {
+      // one wave finds the bucket b with S(b) >= krem > S(b + 1), S(b) =
+      // keys in buckets >= b: lane l holds buckets 4l..4l+3, suffix sums
+      // across lanes by shuffles
+      const int h0 = hist[4 * tid], h1 = hist[4 * tid + 1], h2 = hist[4 * tid + 2], h3 = hist[4 * tid + 3];
+      const int own = h0 + h1 + h2 + h3;
+      int incl = own;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_down(incl, off);
+        if (tid + off < 64) incl += v;
+      }
+      const int s4 = incl - own, s3 = s4 + h3, s2 = s3 + h2, s1 = s2 + h1, s0 = s1 + h0;
+      if (s3 >= krem && s4 < krem) { s_b = 4 * tid + 3; s_above = s4; s_in = h3; }
+      if (s2 >= krem && s3 < krem) { s_b = 4 * tid + 2; s_above = s3; s_in = h2; }
+      if (s1 >= krem && s2 < krem) { s_b = 4 * tid + 1; s_above = s2; s_in = h1; }
+      if (s0 >= krem && s1 < krem) { s_b = 4 * tid; s_above = s1; s_in = h0; }
     }
-    const int here = hist[tid], above = tid < 255 ? hist[tid + 1] : 0;
-    if (here >= krem && above < krem) { s_b = tid; s_above = above; s_in = here - above; }
     __syncthreads();
     prefix |= (uint64_t)s_b << shift;
     mask |= (uint64_t)0xFF << shift;
