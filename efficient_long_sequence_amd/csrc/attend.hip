@@ -47,7 +47,7 @@ __global__ __launch_bounds__(NW * 64) void k_attend(
 
   Frag<T> qf[IB][D / 32];
   int qn[IB];
-  float M[IB];
+  RunMax M[IB];
   f32x4 Z[IB];
   f32x4 acc[IB][D / 16];
 #pragma unroll
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(NW * 64) void k_attend(
       if (qn[b] >= 0) load8(qf[b][dc], Q + ((size_t)bh * N + qn[b]) * D + dc * 32 + 8 * lg);
       else zero(qf[b][dc]);
     }
-    M[b] = M0;
+    M[b].set(M0, cscale_sh);
     Z[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cb = 0; cb < D / 16; ++cb) acc[b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -102,6 +102,10 @@ __global__ __launch_bounds__(NW * 64) void k_attend(
     f.load_vals(cur + TL::K_ELEMS, li, lg);
     const int nv = st < ns ? min(32, m0 - st * 32) : min(32, k - (st - ns) * 32);
     const float sc = st < ns ? cscale_sh : cscale;
+    if (st == ns && ns > 0) {  // the logit scale may change with the routed entries
+#pragma unroll
+      for (int b = 0; b < IB; ++b) M[b].set(M[b].M, cscale);
+    }
     if (nv == 32) attn_step<IB, false>(f, one, qf, nv, lg, sc, M, Z, acc, NoHook{});
     else attn_step<IB, true>(f, one, qf, nv, lg, sc, M, Z, acc, NoHook{});
     if (more) ld.store(nxt, nxt + TL::K_ELEMS);
@@ -115,12 +119,12 @@ __global__ __launch_bounds__(NW * 64) void k_attend(
     const size_t qrow = (size_t)bh * N + qn[b];
     if constexpr (!SLOT0) {
       float* dst = part + ((size_t)(slot - 1) * BH * N + qrow) * (D + 4);
-      if (lg == 0) { dst[0] = M[b]; dst[1] = Zt; }
+      if (lg == 0) { dst[0] = M[b].M; dst[1] = Zt; }
 #pragma unroll
       for (int cb = 0; cb < D / 16; ++cb)
         *(float4*)(dst + 4 + cb * 16 + 4 * lg) = make_float4(acc[b][cb][0], acc[b][cb][1], acc[b][cb][2], acc[b][cb][3]);
     } else {
-      float Mx = M[b];
+      float Mx = M[b].M;
       for (int t = 1; t < s; ++t) {
         const float* src = part + ((size_t)(t - 1) * BH * N + qrow) * (D + 4);
         const float Mt = src[0], Zp = src[1];

@@ -33,7 +33,7 @@ __global__ __launch_bounds__(NW * 64) void k_dense(const T* __restrict__ Q, cons
   const Frag<T> one = ones_frag<T>(li);
 
   Frag<T> qf[IB][D / 32];
-  float M[IB];
+  RunMax M[IB];
   f32x4 Z[IB];
   f32x4 acc[IB][D / 16];
 #pragma unroll
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(NW * 64) void k_dense(const T* __restrict__ Q, cons
       if (n < N) load8(qf[b][dc], Q + hb + (size_t)n * D + dc * 32 + 8 * lg);
       else zero(qf[b][dc]);
     }
-    M[b] = M0;
+    M[b].set(M0, cscale);
     Z[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cb = 0; cb < D / 16; ++cb) acc[b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};

@@ -206,7 +206,8 @@ __global__ __launch_bounds__(NW * 64) void k_route_shared(
 #pragma unroll
       for (int dc = 0; dc < D / 32; ++dc) qf[b][dc] = qn[b][dc];
     if (gi + NW < ngroups) load_queries<T, D, 4>(qn, Qh, lg, group_rows(gi + NW));
-    float lv[4][SMAX], M[4];
+    float lv[4][SMAX];
+    RunMax M[4];
     f32x4 Z[4];
     int lx[4][SMAX];
     f32x4 acc[4][D / 16];
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(NW * 64) void k_route_shared(
     for (int b = 0; b < 4; ++b) {
 #pragma unroll
       for (int t = 0; t < SMAX; ++t) { lv[b][t] = -INFINITY; lx[b][t] = 0x7FFFFFFF; }
-      M[b] = M0;
+      M[b].set(M0, cscale);
       Z[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int cb = 0; cb < D / 16; ++cb) acc[b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -277,7 +278,7 @@ __global__ __launch_bounds__(NW * 64) void k_route_shared(
             else atomicAdd(counts + ((size_t)t * BH + bh) * m + e, 1);
           }
         }
-        plse[qrow] = M[b] + __builtin_amdgcn_logf(Zt);
+        plse[qrow] = M[b].M + __builtin_amdgcn_logf(Zt);
       }
       const float inv = 1.0f / Zt;
       P* o = po + qrow * D;
@@ -312,12 +313,12 @@ __device__ __forceinline__ void expert_group(const Frag<T> (&qf)[IB][D / 32], co
   using RL = Resident<T, D>;
   using P = typename PartT<T>::type;
   using PV = typename Vec4<P>::type;
-  float M[IB];
+  RunMax M[IB];
   f32x4 Z[IB];
   f32x4 acc[IB][D / 16];
 #pragma unroll
   for (int b = 0; b < IB; ++b) {
-    M[b] = M0;
+    M[b].set(M0, cscale);
     Z[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cb = 0; cb < D / 16; ++cb) acc[b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -341,7 +342,7 @@ __device__ __forceinline__ void expert_group(const Frag<T> (&qf)[IB][D / 32], co
     // merge with the stored partial (none before the first routed slot of
     // the routing-only variant): weights 2^lse of the two parts
     const float la = merge_in ? plse[qrow] : M0;
-    const float lb = M[b] + __builtin_amdgcn_logf(Zt);
+    const float lb = M[b].M + __builtin_amdgcn_logf(Zt);
     const float mx = fmaxf(la, lb);
     const float wa = __builtin_amdgcn_exp2f(la - mx), wb = __builtin_amdgcn_exp2f(lb - mx);
     const float den = wa + wb;

@@ -170,7 +170,8 @@ __global__ __launch_bounds__(NW * 64, (score_waves_per_eu<T, NW, IB>())) void k_
   }
 
   Frag<T> qf[IB][D / 32];
-  float M[IB], tau[IB];
+  float tau[IB];
+  RunMax M[IB];
   f32x4 Z[IB];
   f32x4 acc[IB][D / 16];
 #pragma unroll
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(NW * 64, (score_waves_per_eu<T, NW, IB>())) void k_
       if (valid) load8(qf[b][dc], Qt + ((size_t)bh * m + row) * D + dc * 32 + 8 * lg);
       else zero(qf[b][dc]);
     }
-    M[b] = (mhat_in != nullptr && valid) ? mhat_in[(size_t)bh * m + row] * cscale : M0;
+    M[b].set((mhat_in != nullptr && valid) ? mhat_in[(size_t)bh * m + row] * cscale : M0, cscale);
     tau[b] = DENSE ? -INFINITY : (valid ? tau_in[(size_t)bh * m + row] : INFINITY);
     Z[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -271,7 +272,7 @@ __global__ __launch_bounds__(NW * 64, (score_waves_per_eu<T, NW, IB>())) void k_
       const int row = rbase + b * 16 + li;
       if (row < m) {
         float* dst = vpart + (((size_t)bh * m + row) * C + ch) * (D + 4);
-        if (lg == 0) { dst[0] = M[b]; dst[1] = Zt; }
+        if (lg == 0) { dst[0] = M[b].M; dst[1] = Zt; }
 #pragma unroll
         for (int cb = 0; cb < D / 16; ++cb)
           *(float4*)(dst + 4 + cb * 16 + 4 * lg) =

@@ -184,30 +184,42 @@ __device__ __forceinline__ Frag<T> ones_frag(int li) {
 // The normaliser of query li (held by lane li of group 0), in every lane.
 __device__ __forceinline__ float finish_z(const f32x4& Z, int li) { return __shfl(Z[0], li); }
 
+// Running maximum of one 16-query block: M in the scaled log2 domain
+// (identical in the four lane groups of a query) and Mt = (M + THRESH) /
+// cscale, the raw score above which the maximum is raised, so the common
+// step compares raw lane maxima with no scaling.
+struct RunMax {
+  float M, Mt;
+  __device__ __forceinline__ void set(float m, float cscale) {
+    M = m;
+    Mt = (m + THRESH) / cscale;
+  }
+};
+
 // Online-softmax update of one 16-query block with the 8 raw scores of this
-// lane (already -inf where masked).  M is the running maximum in the scaled
-// log2 domain (identical in the four lane groups of a query), Z the
+// lane (already -inf where masked) and their maximum mx_raw.  Z is the
 // normaliser tile (see ones_frag), acc the O^T accumulator.
 template <typename T, int D>
 __device__ __forceinline__ void softmax_step(const StepFrags<T, D>& f, const Frag<T>& one, const float* sc,
-                                             float mx_raw, float cscale, float& M, f32x4& Z, f32x4* acc) {
-  const float xm = mx_raw * cscale;
-  if (wave_any(xm > M + THRESH)) {
-    // The decision uses the query's own maximum over its four lane groups,
-    // so each query's running maximum (and every rounding that follows from
-    // it) is independent of which other queries share the wave.
-    const float gm = wave_max_groups(xm);
-    if (gm > M + THRESH) {
-      const float alpha = __builtin_amdgcn_exp2f(M - gm);
+                                             float mx_raw, float cscale, RunMax& R, f32x4& Z, f32x4* acc) {
+  if (wave_any(mx_raw > R.Mt)) {
+    // The decision uses the query's own maximum over its four lane groups
+    // with the same comparison, so each query's running maximum (and every
+    // rounding that follows from it) is independent of which other queries
+    // share the wave.
+    const float gm = wave_max_groups(mx_raw);
+    if (gm > R.Mt) {
+      const float nm = gm * cscale;
+      const float alpha = __builtin_amdgcn_exp2f(R.M - nm);
       Z[0] *= alpha;
 #pragma unroll
       for (int cb = 0; cb < D / 16; ++cb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[cb][r] *= alpha;
-      M = gm;
+      R.set(nm, cscale);
     }
   }
-  const float nm = -M;
+  const float nm = -R.M;
   float p[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t], cscale, nm));
@@ -217,7 +229,6 @@ __device__ __forceinline__ void softmax_step(const StepFrags<T, D>& f, const Fra
   for (int cb = 0; cb < D / 16; ++cb) mma16(acc[cb], f.va[cb], pf);
   mma16(Z, one, pf);
 }
-
 
 // chained so the compiler forms three-input maxima (v_max3_f32)
 __device__ __forceinline__ float max8(const float* s) {
@@ -235,7 +246,7 @@ __device__ __forceinline__ float max8(const float* s) {
 template <int IB, bool MASK, typename T, int D, class On>
 __device__ __forceinline__ void attn_step(const StepFrags<T, D>& f, const Frag<T>& one,
                                           const Frag<T> (&qf)[IB][D / 32], int nv, int lg, float cscale,
-                                          float (&M)[IB], f32x4 (&Z)[IB], f32x4 (&acc)[IB][D / 16], On on) {
+                                          RunMax (&M)[IB], f32x4 (&Z)[IB], f32x4 (&acc)[IB][D / 16], On on) {
   float sc[IB][8];
 #pragma unroll
   for (int b = 0; b < IB; ++b) step_scores(f, qf[b], sc[b]);
