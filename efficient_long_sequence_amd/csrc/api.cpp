@@ -38,6 +38,8 @@ mita_status validate(const void* Q, const void* K, const void* V, void* O, mita_
   if (s > MAX_S || m > MAX_M || (long long)N > MAX_N) return MITA_ERR_UNSUPPORTED;
   if (N > NSMALL && k > MAX_K_SPARSE) return MITA_ERR_UNSUPPORTED;
   if ((long long)B * H > 65535) return MITA_ERR_UNSUPPORTED;
+  // query positions of a slot (bucket offsets, work items) are 32-bit
+  if ((long long)B * H * N > 0x7FFFFFFFLL) return MITA_ERR_UNSUPPORTED;
   return MITA_OK;
 }
 
@@ -128,7 +130,7 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
     else { p.at_nw = 8; p.at_ib = 4; }
     p.T = p.at_nw * 16 * p.at_ib;
   }
-  p.UB = p.BH * (ceil_div(N, p.T) + m);
+  p.UB = (int)((long long)p.BH * (ceil_div(N, p.T) + m));  // <= B*H*N/16 + B*H*m: fits (see validate)
 
   // workspace
   const size_t BH = p.BH, Mr = (size_t)p.BH * m;

@@ -55,7 +55,8 @@ typedef enum {
                                landmark grid larger than the token grid */
   MITA_ERR_PARAM = 3,       /* k not in [1, N]; s not in [1, m]; pointer not 16-byte aligned */
   MITA_ERR_UNSUPPORTED = 4, /* d not in {32, 64}; unknown dtype; s > 8; m > 4096;
-                               N > 2^26; k > 2048 when N > 8192 */
+                               N > 2^26; k > 2048 when N > 8192; B*H > 65535;
+                               B*H*N > 2^31 - 1 */
   MITA_ERR_WORKSPACE = 5,   /* workspace smaller than mita_workspace_bytes() */
   MITA_ERR_HIP = 6          /* the HIP runtime reported an error while enqueueing */
 } mita_status;

@@ -51,6 +51,8 @@ def _fwd(**kw):
     (dict(d=48), 4), (dict(dt=7), 4), (dict(s=9, m=64), 4),
     (dict(N=1 << 20, pool=(1, 1 << 20, 1, 64), k=4096), 4),
     (dict(m=4097 * 1, pool=(1, 8192, 1, 4097), N=8192), 4),
+    # more than 2^31 - 1 tokens in all: 64 * 512 * 2^16 = 2^31
+    (dict(B=64, H=512, N=1 << 16, pool=(1, 1 << 16, 1, 64)), 4),
     (dict(wsb=100), 5),
 ])
 def test_invalid_arguments_are_rejected(kw, code):
