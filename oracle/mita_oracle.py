@@ -98,7 +98,10 @@ def bf16_round(x) -> np.ndarray:
 
 
 def round_to_dtype(x, dtype: str) -> np.ndarray:
-    """Round float64 to the input dtype's value set ("f32" or "bf16")."""
+    """Round float64 to the input dtype's value set ("f32" or "bf16"; "f64"
+    keeps every value, for finite-difference checks of the backward pass)."""
+    if dtype == "f64":
+        return np.asarray(x, dtype=np.float64).copy()
     if dtype == "f32":
         return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
     if dtype == "bf16":
