@@ -19,7 +19,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-mita_status validate(const void* Q, const void* K, const void* V, void* O, mita_dtype dtype, int B, int H,
+mita_status validate(const void* Q, const void* K, const void* V, const void* O, mita_dtype dtype, int B, int H,
                      int N, int d, mita_pool pool, int m, int k, int s, bool check_ptrs) {
   if (check_ptrs && (!Q || !K || !V || !O)) return MITA_ERR_NULL;
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return MITA_ERR_SHAPE;
@@ -168,6 +168,19 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
   return p;
 }
 
+bool valid_variant(int v) {
+  return v == MITA_VARIANT_PAPER || v == MITA_VARIANT_OFFICIAL || v == MITA_VARIANT_ROUTED;
+}
+
+mita_status check_saved(const mita_saved* sv, int variant) {
+  if (!sv || !sv->qtilde || !sv->topk || !sv->route || !sv->lse || !sv->out_f32) return MITA_ERR_NULL;
+  const bool shared = variant != MITA_VARIANT_ROUTED;
+  if (shared && (!sv->vtilde || !sv->lse_landmark)) return MITA_ERR_NULL;
+  if (((uintptr_t)sv->qtilde | (uintptr_t)sv->out_f32 | (shared ? (uintptr_t)sv->vtilde : 0)) & 15u)
+    return MITA_ERR_PARAM;
+  return MITA_OK;
+}
+
 struct Timer {
   void* const* ev;
   hipStream_t st;
@@ -181,11 +194,12 @@ struct Timer {
 
 mita_status run(const void* Q, const void* K, const void* V, void* O, mita_dtype dtype, int B, int H, int N,
                 int d, mita_pool pool, int m, int k, int s, int variant, const mita_debug* dbg, void* workspace,
-                size_t workspace_bytes, void* stream, void* const* events) {
+                size_t workspace_bytes, void* stream, void* const* events, const mita_saved* sv = nullptr,
+                bool want_saved = false) {
   mita_status st = validate(Q, K, V, O, dtype, B, H, N, d, pool, m, k, s, true);
   if (st != MITA_OK) return st;
-  if (variant != MITA_VARIANT_PAPER && variant != MITA_VARIANT_OFFICIAL && variant != MITA_VARIANT_ROUTED)
-    return MITA_ERR_PARAM;
+  if (!valid_variant(variant)) return MITA_ERR_PARAM;
+  if (want_saved && (st = check_saved(sv, variant)) != MITA_OK) return st;
   if (!workspace) return MITA_ERR_NULL;
   if ((uintptr_t)workspace & 15u) return MITA_ERR_PARAM;
   Plan p = make_plan(dtype, B, H, N, d, pool, m, k, s, (char*)workspace);
@@ -194,6 +208,11 @@ mita_status run(const void* Q, const void* K, const void* V, void* O, mita_dtype
   p.stream = (hipStream_t)stream;
   if (variant == MITA_VARIANT_OFFICIAL) p.cscale_sh = (float)(1.4426950408889634 / (double)d);
   p.shared = variant == MITA_VARIANT_ROUTED ? 0 : 1;
+  if (sv) {
+    p.lse_out = sv->lse;
+    p.lse_lm = p.shared ? sv->lse_landmark : nullptr;
+    p.o32 = sv->out_f32;
+  }
   const Timer tm{events, p.stream};
 
   (void)hipGetLastError();  // clear any earlier sticky launch error
@@ -232,7 +251,81 @@ mita_status run(const void* Q, const void* K, const void* V, void* O, mita_dtype
     if (dbg->qtilde)
       (void)hipMemcpyAsync(dbg->qtilde, p.qt, Mr * d * p.esize, hipMemcpyDeviceToDevice, p.stream);
   }
+  if (sv) {
+    const size_t Mr = (size_t)p.BH * m;
+    (void)hipMemcpyAsync(sv->qtilde, p.qt, Mr * d * p.esize, hipMemcpyDeviceToDevice, p.stream);
+    if (p.shared) (void)hipMemcpyAsync(sv->vtilde, p.vt32, Mr * d * 4, hipMemcpyDeviceToDevice, p.stream);
+    (void)hipMemcpyAsync(sv->topk, p.topk, Mr * k * 4, hipMemcpyDeviceToDevice, p.stream);
+    (void)hipMemcpyAsync(sv->route, p.route, (size_t)p.BH * N * s * 4, hipMemcpyDeviceToDevice, p.stream);
+  }
   return hipGetLastError() == hipSuccess ? MITA_OK : MITA_ERR_HIP;
+}
+
+// Sizes, launch shapes and workspace regions of one backward call.
+BPlan make_bplan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int m, int k, int s, char* base) {
+  BPlan p;
+  std::memset(&p, 0, sizeof(p));
+  p.dtype = dtype == MITA_BF16 ? 1 : 0;
+  p.esize = p.dtype ? 2 : 4;
+  p.BH = B * H; p.N = N; p.d = d;
+  p.gh = pool.grid_h; p.gw = pool.grid_w; p.lh = pool.land_h; p.lw = pool.land_w;
+  p.m = m; p.k = k; p.s = s;
+  p.shared = 1;
+  p.cnat = (float)(1.0 / std::sqrt((double)d));
+  p.cnat_sh = p.cnat;
+  p.cscale = (float)(1.4426950408889634 / std::sqrt((double)d));
+  p.cscale_sh = p.cscale;
+  p.R = backward_rows(p.dtype);
+  // landmark-row passes: about 1024 workgroups in all, whole 32-entry steps
+  auto chunks = [&](int& L, int& C) {
+    const long long rt = ceil_div(m, p.R);
+    long long c = ceil_div(1024, rt * p.BH);
+    c = c < 1 ? 1 : c;
+    const long long cmax = ceil_div(N, 32);
+    c = c > cmax ? cmax : c;
+    L = ceil_div(N, c);
+    L = (L + 31) / 32 * 32;
+    C = ceil_div(N, L);
+  };
+  chunks(p.L1, p.C1);
+  chunks(p.L4, p.C4);
+  // query grouping: tiles of R queries
+  Plan& b = p.bk;
+  b.dtype = p.dtype; b.esize = p.esize; b.B = B; b.H = H; b.BH = p.BH; b.N = N; b.d = d;
+  b.m = m; b.k = k; b.s = s;
+  b.T = p.R;
+  b.UB = (int)((long long)p.BH * (ceil_div(N, b.T) + m));
+
+  const size_t BH = p.BH, Mr = (size_t)p.BH * m, Nr = (size_t)p.BH * N;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    char* ptr = base ? base + off : nullptr;
+    off = align_up(off + bytes, 256);
+    return ptr;
+  };
+  const size_t zoff = off;
+  b.counts = (int*)take((size_t)s * Mr * 4);
+  b.cursor = (int*)take((size_t)s * Mr * 4);
+  p.dKacc = (float*)take(Nr * d * 4);
+  p.dVacc = (float*)take(Nr * d * 4);
+  p.zero_begin = base ? base + zoff : nullptr;
+  p.zero_bytes = off - zoff;
+  p.Dn = (float*)take(Nr * 4);
+  b.route = (int32_t*)take(Nr * s * 4);
+  b.gpre = (int*)take((size_t)s * Mr * 4);
+  b.perm = (int32_t*)take((size_t)s * Nr * 4);
+  b.wl = (WorkItem*)take((size_t)s * b.UB * sizeof(WorkItem));
+  b.wl_count = (int*)take(MAX_S * 4);
+  p.part1 = (float*)take(BH * p.C1 * m * 2 * d * 4);
+  p.part4 = (float*)take(BH * p.C4 * m * d * 4);
+  p.dqt = (float*)take(Mr * d * 4);
+  p.dvt = (float*)take(Mr * d * 4);
+  p.dvtT = take(Mr * d * p.esize);
+  p.vt = take(Mr * d * p.esize);
+  p.delta = (float*)take(Mr * 4);
+  p.qpart = (float*)take(s > 1 ? (size_t)(s - 1) * Nr * d * 4 : 0);
+  p.total_bytes = off;
+  return p;
 }
 
 const char* const kStageNames[ST_COUNT] = {"pool", "estimate", "score", "select", "route", "bucket", "attend"};
@@ -279,6 +372,54 @@ mita_status mita_dense_attention(const void* Q, const void* K, const void* V, vo
   if ((long long)N > MAX_N || (long long)B * H > 65535) return MITA_ERR_UNSUPPORTED;
   (void)hipGetLastError();
   launch_dense(Q, K, V, O, dtype == MITA_BF16 ? 1 : 0, B * H, N, d, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? MITA_OK : MITA_ERR_HIP;
+}
+
+mita_status mita_forward_train(const void* Q, const void* K, const void* V, void* O, mita_dtype dtype, int B,
+                               int H, int N, int d, mita_pool pool, int m, int k, int s, mita_variant variant,
+                               const mita_saved* saved, void* workspace, size_t workspace_bytes, void* stream) {
+  return run(Q, K, V, O, dtype, B, H, N, d, pool, m, k, s, (int)variant, nullptr, workspace, workspace_bytes, stream,
+             nullptr, saved, true);
+}
+
+size_t mita_backward_workspace_bytes(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int m, int k,
+                                     int s) {
+  if (validate(nullptr, nullptr, nullptr, nullptr, dtype, B, H, N, d, pool, m, k, s, false) != MITA_OK) return 0;
+  return make_bplan(dtype, B, H, N, d, pool, m, k, s, nullptr).total_bytes;
+}
+
+mita_status mita_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO, void* dQ,
+                          void* dK, void* dV, mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int m,
+                          int k, int s, mita_variant variant, const mita_saved* saved, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  mita_status st = validate(Q, K, V, O, dtype, B, H, N, d, pool, m, k, s, true);
+  if (st != MITA_OK) return st;
+  if (!dO || !dQ || !dK || !dV) return MITA_ERR_NULL;
+  if (((uintptr_t)dO | (uintptr_t)dQ | (uintptr_t)dK | (uintptr_t)dV) & 15u) return MITA_ERR_PARAM;
+  if (!valid_variant((int)variant)) return MITA_ERR_PARAM;
+  if ((st = check_saved(saved, (int)variant)) != MITA_OK) return st;
+  if (!workspace) return MITA_ERR_NULL;
+  if ((uintptr_t)workspace & 15u) return MITA_ERR_PARAM;
+  BPlan p = make_bplan(dtype, B, H, N, d, pool, m, k, s, (char*)workspace);
+  if (workspace_bytes < p.total_bytes) return MITA_ERR_WORKSPACE;
+  p.shared = variant == MITA_VARIANT_ROUTED ? 0 : 1;
+  if (variant == MITA_VARIANT_OFFICIAL) {
+    p.cnat_sh = (float)(1.0 / (double)d);
+    p.cscale_sh = (float)(1.4426950408889634 / (double)d);
+  }
+  p.Q = Q; p.K = K; p.V = V; p.O = O; p.dO = dO;
+  p.dQ = dQ; p.dK = dK; p.dV = dV;
+  p.qt = saved->qtilde;
+  p.vt32 = p.shared ? saved->vtilde : nullptr;
+  p.o32 = saved->out_f32;
+  p.topk = saved->topk;
+  p.route = saved->route;
+  p.lse = saved->lse;
+  p.lse_lm = p.shared ? saved->lse_landmark : nullptr;
+  p.stream = (hipStream_t)stream;
+  p.bk.stream = p.stream;
+  (void)hipGetLastError();
+  launch_backward(p);
   return hipGetLastError() == hipSuccess ? MITA_OK : MITA_ERR_HIP;
 }
 

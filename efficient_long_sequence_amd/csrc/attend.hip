@@ -29,8 +29,8 @@ __global__ __launch_bounds__(NW * 64) void k_attend(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ Qt,
     const T* __restrict__ VtT, const int32_t* __restrict__ topk, const int32_t* __restrict__ perm,
     const WorkItem* __restrict__ wl, const int* __restrict__ wl_count, float* __restrict__ part,
-    T* __restrict__ O, int N, int m, int k, int s, int slot, int BH, int m_shared, float cscale,
-    float cscale_sh) {
+    T* __restrict__ O, float* __restrict__ lse_out, float* __restrict__ o32, int N, int m, int k, int s, int slot, int BH, int m_shared,
+    float cscale, float cscale_sh) {
   constexpr int NT = NW * 64;
   using TL = TileLayout<T, D>;
   __shared__ __align__(16) T smem[2 * TL::ELEMS];
@@ -141,12 +141,18 @@ __global__ __launch_bounds__(NW * 64) void k_attend(
         }
         Mx = nM;
       }
+      if (lse_out && lg == 0) lse_out[qrow] = Mx + __builtin_amdgcn_logf(Zt);  // kept for the backward pass
       const float inv = 1.0f / Zt;
       T* dst = O + qrow * D;
 #pragma unroll
       for (int cb = 0; cb < D / 16; ++cb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) dst[cb * 16 + 4 * lg + r] = from_f32<T>(acc[b][cb][r] * inv);
+      if (o32)
+#pragma unroll
+        for (int cb = 0; cb < D / 16; ++cb)
+          *(float4*)(o32 + qrow * D + cb * 16 + 4 * lg) =
+              make_float4(acc[b][cb][0] * inv, acc[b][cb][1] * inv, acc[b][cb][2] * inv, acc[b][cb][3] * inv);
     }
   }
 }
@@ -160,11 +166,11 @@ static void launch_attend_t(const Plan& p) {
     if (t > 0)
       hipLaunchKernelGGL((k_attend<T, D, NW, IB, false>), dim3((unsigned)p.UB), dim3(NW * 64), 0, p.stream,
                          (const T*)p.Q, (const T*)p.K, (const T*)p.V, (const T*)p.qt, (const T*)p.vtT, p.topk, perm,
-                         wl, wlc, p.part, (T*)p.O, p.N, p.m, p.k, p.s, t, p.BH, p.shared ? p.m : 0, p.cscale, p.cscale_sh);
+                         wl, wlc, p.part, (T*)p.O, p.lse_out, p.o32, p.N, p.m, p.k, p.s, t, p.BH, p.shared ? p.m : 0, p.cscale, p.cscale_sh);
     else
       hipLaunchKernelGGL((k_attend<T, D, NW, IB, true>), dim3((unsigned)p.UB), dim3(NW * 64), 0, p.stream,
                          (const T*)p.Q, (const T*)p.K, (const T*)p.V, (const T*)p.qt, (const T*)p.vtT, p.topk, perm,
-                         wl, wlc, p.part, (T*)p.O, p.N, p.m, p.k, p.s, t, p.BH, p.shared ? p.m : 0, p.cscale, p.cscale_sh);
+                         wl, wlc, p.part, (T*)p.O, p.lse_out, p.o32, p.N, p.m, p.k, p.s, t, p.BH, p.shared ? p.m : 0, p.cscale, p.cscale_sh);
   }
 }
 

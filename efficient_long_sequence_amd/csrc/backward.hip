@@ -1,0 +1,747 @@
+// Backward pass of MiTA: dQ, dK and dV of sum(O * dO).
+//
+// What is differentiated is the forward of MiTA tutorial (iwxt.cn) ch.4
+// (steps 1-6) as trained end to end (ch.7, LRA training).  The top-k keys of
+// each landmark and the top-s landmarks of each query are choices, constant
+// wherever they are unique, so they pass no gradient and are taken from the
+// forward (its saved experts and routes); q~'s rounding to the input dtype is
+// taken as the identity, so pooling's adjoint spreads d q~_i / |W_i| over the
+// tokens of window W_i.
+//
+// Every softmax here is already finished: the forward kept each one's
+// log2-sum-exp L, so a probability is exp2(score * cscale - L) with no
+// running maximum.  The gradient of a softmax entry t is
+// dS_t = P_t (dP_t - delta), with dP_t = g . w_t (g the upstream gradient of
+// the softmax's output, w_t the entry's value) and delta = g . output.
+//
+// One step shape serves every pass: a workgroup keeps 16*IB*NW "stationary"
+// rows in registers (matrix-core columns) and streams 32 "entries" at a time
+// through double-buffered LDS.  Per step it forms S = X.Y and dP = W.Z (X, W
+// the rows' two vectors; Y, Z the entries'), then P and dS, and accumulates
+// dX += c dS Y and, when asked, dW += P Z, with c the logit scale.  The entry
+// vectors are staged twice, row-major (operands of S and dP) and transposed
+// (operands of the accumulations); the slot permutation of the forward's
+// layout cancels in every contraction.  The passes:
+//
+//   joint softmax, landmark rows over all queries    X q~, W v~,  Y q,  Z dO   -> dq~, dv~  (chunk partials)
+//   joint softmax, expert key rows over its queries  X k,  W v,   Y q,  Z dO   -> dk, dv    (atomic adds)
+//   shared values, key rows over all landmarks       X k,  W v,   Y q~, Z dv~  -> dk, dv    (+ the above, final)
+//   shared values, landmark rows over all keys       X q~, W dv~, Y k,  Z v    -> dq~       (chunk partials)
+//   joint softmax, query rows over [q~; expert keys] X q,  W dO,  Y,    Z      -> dq        (+ pooling's adjoint)
+//
+// In the shared-value softmax the stationary-landmark pass takes L and delta
+// per row; every other pass takes them per entry (each entry is a query or a
+// landmark row whose softmax it belongs to).
+#include <cmath>
+
+#include "mita_dev.h"
+#include "mita_plan.h"
+#include "tile.h"
+
+namespace mita {
+
+// LDS of one step: Y (row-major + transposed), Z (likewise), then L and delta
+// of the 32 entries.
+template <typename T, int D>
+struct GradLds {
+  using TL = TileLayout<T, D>;
+  static constexpr size_t TILE_BYTES = (size_t)TL::ELEMS * sizeof(T);
+  static constexpr size_t STEP_BYTES = 2 * TILE_BYTES + 64 * sizeof(float);
+  static_assert(TILE_BYTES % 16 == 0, "tiles must stay 16-byte aligned");
+  __device__ static T* y(unsigned char* b) { return (T*)b; }
+  __device__ static T* z(unsigned char* b) { return (T*)(b + TILE_BYTES); }
+  __device__ static float* ent(unsigned char* b) { return (float*)(b + 2 * TILE_BYTES); }
+};
+
+template <typename T, int D, int NT, bool WANT_W, bool ENT>
+struct GradLoader {
+  using GL = GradLds<T, D>;
+  using TL = TileLayout<T, D>;
+  TileLoader<T, D, NT, true> ly;
+  TileLoader<T, D, NT, WANT_W> lz;
+  float2 e;
+  template <class RY, class RZ, class RE>
+  __device__ __forceinline__ void load(RY ry, RZ rz, RE re) {
+    ly.load(ry, ry);
+    lz.load(rz, rz);
+    if constexpr (ENT) {
+      if (threadIdx.x < 32) e = re((int)threadIdx.x);
+    }
+  }
+  __device__ __forceinline__ void store(unsigned char* b) const {
+    T* y = GL::y(b);
+    T* z = GL::z(b);
+    ly.store(y, y + TL::K_ELEMS);
+    lz.store(z, z + TL::K_ELEMS);
+    if constexpr (ENT) {
+      if (threadIdx.x < 32) {
+        float* f = GL::ent(b);
+        f[threadIdx.x] = e.x;
+        f[32 + threadIdx.x] = e.y;
+      }
+    }
+  }
+};
+
+// One 32-entry step for IB blocks of 16 stationary rows.  ROWL: L and delta
+// per stationary row (Lr, Dr: this lane's row) instead of per entry (Le, De
+// in LDS).  MASK: entries at offsets >= nv are absent.
+template <int IB, bool MASK, bool ROWL, bool WANT_W, typename T, int D>
+__device__ __forceinline__ void grad_step(const StepFrags<T, D>& fy, const StepFrags<T, D>& fz,
+                                          const Frag<T> (&xf)[IB][D / 32], const Frag<T> (&wf)[IB][D / 32],
+                                          int nv, int lg, float cscale, float cnat, const float (&Lr)[IB],
+                                          const float (&Dr)[IB], const float* Le, const float* De,
+                                          f32x4 (&ax)[IB][D / 16], f32x4 (&aw)[IB][D / 16]) {
+  float le[8], de[8];
+  if constexpr (!ROWL) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int j = slot_key(t, lg);
+      le[t] = Le[j];
+      de[t] = De[j];
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < IB; ++b) {
+    float sc[8], dp[8];
+    step_scores(fy, xf[b], sc);
+    step_scores(fz, wf[b], dp);
+    float p[8], ds[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float L = ROWL ? Lr[b] : le[t];
+      const float dl = ROWL ? Dr[b] : de[t];
+      float pt = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t], cscale, -L));
+      if (MASK && slot_key(t, lg) >= nv) pt = 0.f;
+      p[t] = pt;
+      ds[t] = pt * (dp[t] - dl) * cnat;
+    }
+    Frag<T> df;
+    set8(df, ds);
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb) mma16(ax[b][cb], fy.va[cb], df);
+    if constexpr (WANT_W) {
+      Frag<T> pf;
+      set8(pf, p);
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb) mma16(aw[b][cb], fz.va[cb], pf);
+    }
+  }
+}
+
+// Streams nsteps steps of entries from `src` through LDS and applies
+// grad_step to the wave's blocks.  src.ry(st) / src.rz(st): row pointer
+// functions of step st (nullptr past the end); src.re(st): (L, delta) of an
+// entry; src.nv(st), src.cscale(st), src.cnat(st).  Ends with a barrier.
+template <int IB, bool ROWL, bool WANT_W, bool ENT, int NT, typename T, int D, class Src>
+__device__ __forceinline__ void grad_stream(unsigned char* smem, int nsteps, const Src& src,
+                                            const Frag<T> (&xf)[IB][D / 32], const Frag<T> (&wf)[IB][D / 32],
+                                            const float (&Lr)[IB], const float (&Dr)[IB],
+                                            f32x4 (&ax)[IB][D / 16], f32x4 (&aw)[IB][D / 16], int li, int lg) {
+  using GL = GradLds<T, D>;
+  using TL = TileLayout<T, D>;
+  GradLoader<T, D, NT, WANT_W, ENT> ld;
+  unsigned char* b0 = smem;
+  unsigned char* b1 = smem + GL::STEP_BYTES;
+  if (nsteps > 0) {
+    ld.load(src.ry(0), src.rz(0), src.re(0));
+    ld.store(b0);
+  }
+  __syncthreads();
+  for (int st = 0; st < nsteps; ++st) {
+    unsigned char* cur = (st & 1) ? b1 : b0;
+    unsigned char* nxt = (st & 1) ? b0 : b1;
+    const bool more = st + 1 < nsteps;
+    if (more) ld.load(src.ry(st + 1), src.rz(st + 1), src.re(st + 1));
+    StepFrags<T, D> fy, fz;
+    const T* y = GL::y(cur);
+    const T* z = GL::z(cur);
+    fy.load_keys(y, li, lg);
+    fy.load_vals(y + TL::K_ELEMS, li, lg);
+    fz.load_keys(z, li, lg);
+    if constexpr (WANT_W) fz.load_vals(z + TL::K_ELEMS, li, lg);
+    const float* Le = GL::ent(cur);
+    const int nv = src.nv(st);
+    const float cs = src.cscale(st), cn = src.cnat(st);
+    if (nv >= 32) grad_step<IB, false, ROWL, WANT_W>(fy, fz, xf, wf, nv, lg, cs, cn, Lr, Dr, Le, Le + 32, ax, aw);
+    else grad_step<IB, true, ROWL, WANT_W>(fy, fz, xf, wf, nv, lg, cs, cn, Lr, Dr, Le, Le + 32, ax, aw);
+    if (more) ld.store(nxt);
+    __syncthreads();
+  }
+}
+
+// Entries = rows [j0, j1) of Y and Z (one head's base pointers); per-entry L
+// and delta from Lv, Dv when given.
+template <typename T, int D>
+struct SrcRows {
+  const T* Y;
+  const T* Z;
+  const float* Lv;
+  const float* Dv;
+  int j0, j1;
+  float cs, cn;
+  __device__ auto ry(int st) const {
+    const T* b = Y;
+    const int a = j0 + st * 32, e = j1;
+    return [=](int r) -> const T* { const int j = a + r; return j < e ? b + (size_t)j * D : nullptr; };
+  }
+  __device__ auto rz(int st) const {
+    const T* b = Z;
+    const int a = j0 + st * 32, e = j1;
+    return [=](int r) -> const T* { const int j = a + r; return j < e ? b + (size_t)j * D : nullptr; };
+  }
+  __device__ auto re(int st) const {
+    const float* l = Lv;
+    const float* d = Dv;
+    const int a = j0 + st * 32, e = j1;
+    return [=](int r) -> float2 { const int j = a + r; return j < e ? make_float2(l[j], d[j]) : make_float2(0.f, 0.f); };
+  }
+  __device__ int nv(int st) const { return min(32, j1 - j0 - st * 32); }
+  __device__ float cscale(int) const { return cs; }
+  __device__ float cnat(int) const { return cn; }
+};
+
+// Entries = the rows idx[0 .. cnt) of Y and Z (queries of one expert).
+template <typename T, int D>
+struct SrcPerm {
+  const T* Y;
+  const T* Z;
+  const float* Lv;
+  const float* Dv;
+  const int32_t* idx;
+  int cnt;
+  float cs, cn;
+  __device__ auto ry(int st) const {
+    const T* b = Y;
+    const int32_t* ix = idx;
+    const int a = st * 32, e = cnt;
+    return [=](int r) -> const T* { const int x = a + r; return x < e ? b + (size_t)ix[x] * D : nullptr; };
+  }
+  __device__ auto rz(int st) const {
+    const T* b = Z;
+    const int32_t* ix = idx;
+    const int a = st * 32, e = cnt;
+    return [=](int r) -> const T* { const int x = a + r; return x < e ? b + (size_t)ix[x] * D : nullptr; };
+  }
+  __device__ auto re(int st) const {
+    const float* l = Lv;
+    const float* d = Dv;
+    const int32_t* ix = idx;
+    const int a = st * 32, e = cnt;
+    return [=](int r) -> float2 {
+      const int x = a + r;
+      if (x >= e) return make_float2(0.f, 0.f);
+      const int n = ix[x];
+      return make_float2(l[n], d[n]);
+    };
+  }
+  __device__ int nv(int st) const { return min(32, cnt - st * 32); }
+  __device__ float cscale(int) const { return cs; }
+  __device__ float cnat(int) const { return cn; }
+};
+
+// Entries of one query tile: the m0 shared entries (q~, v~; padded to whole
+// steps, so each step has one logit scale), then the expert's k keys.
+template <typename T, int D>
+struct SrcJoint {
+  const T* qt;
+  const T* vt;
+  const T* K;
+  const T* V;
+  const int32_t* Ie;
+  int m0, ns, k, N;
+  float cs, cn, cs_sh, cn_sh;
+  __device__ auto ry(int st) const { return rows(st, qt, K); }
+  __device__ auto rz(int st) const { return rows(st, vt, V); }
+  __device__ auto rows(int st, const T* shared, const T* raw) const {
+    const int32_t* I = Ie;
+    const int ns_ = ns, m0_ = m0, k_ = k, n1 = N - 1;
+    return [=](int r) -> const T* {
+      if (st < ns_) {
+        const int x = st * 32 + r;
+        return x < m0_ ? shared + (size_t)x * D : nullptr;
+      }
+      const int x = (st - ns_) * 32 + r;
+      // indices come from the forward; the clamp only keeps other contents in bounds
+      return x < k_ ? raw + (size_t)min(max(I[x], 0), n1) * D : nullptr;
+    };
+  }
+  __device__ auto re(int) const { return [](int) -> float2 { return make_float2(0.f, 0.f); }; }
+  __device__ int nv(int st) const { return st < ns ? min(32, m0 - st * 32) : min(32, k - (st - ns) * 32); }
+  __device__ float cscale(int st) const { return st < ns ? cs_sh : cs; }
+  __device__ float cnat(int st) const { return st < ns ? cn_sh : cn; }
+};
+
+template <typename T, int D, int IB, class RowPtr>
+__device__ __forceinline__ void load_rows(Frag<T> (&f)[IB][D / 32], int lg, RowPtr row) {
+#pragma unroll
+  for (int b = 0; b < IB; ++b) {
+    const T* p = row(b);
+#pragma unroll
+    for (int dc = 0; dc < D / 32; ++dc) {
+      if (p) load8(f[b][dc], p + dc * 32 + 8 * lg);
+      else zero(f[b][dc]);
+    }
+  }
+}
+
+template <int IB, int D>
+__device__ __forceinline__ void zero_acc(f32x4 (&a)[IB][D / 16]) {
+#pragma unroll
+  for (int b = 0; b < IB; ++b)
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb) a[b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// ---------------------------------------------------------------------------
+// Landmark rows over one chunk of entries (all heads' chunks in the grid).
+// JOINT: entries are queries (Y q, Z dO, per-entry lse and dO . o); outputs
+// the chunk's dq~ (scaled by the shared-logit scale) and dv~.  Otherwise
+// entries are keys (Y k, Z v) and L, delta are the landmark rows'; output
+// the chunk's dq~ of the shared-value softmax.
+template <typename T, int D, int NW, int IB, bool JOINT>
+__global__ __launch_bounds__(NW * 64, 2) void k_bwd_lm(const T* __restrict__ Y, const T* __restrict__ Z,
+                                                       const T* __restrict__ X, const T* __restrict__ W,
+                                                       const float* __restrict__ Lv, const float* __restrict__ Dv,
+                                                       float* __restrict__ part, int N, int m, int L, int C,
+                                                       float cscale, float cnat) {
+  constexpr int NT = NW * 64, PW = JOINT ? 2 * D : D;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, li = lane % 16, lg = lane / 16;
+  const int chunk = blockIdx.y, bh = blockIdx.z;
+  const int i0 = blockIdx.x * (NW * 16 * IB) + wave * 16 * IB;
+  Frag<T> xf[IB][D / 32], wf[IB][D / 32];
+  float Lr[IB], Dr[IB];
+  f32x4 ax[IB][D / 16], aw[IB][D / 16];
+  auto rowp = [&](const T* base) {
+    return [=](int b) -> const T* { const int i = i0 + b * 16 + li; return i < m ? base + ((size_t)bh * m + i) * D : nullptr; };
+  };
+  load_rows<T, D, IB>(xf, lg, rowp(X));
+  load_rows<T, D, IB>(wf, lg, rowp(W));
+#pragma unroll
+  for (int b = 0; b < IB; ++b) {
+    const int i = i0 + b * 16 + li;
+    Lr[b] = (!JOINT && i < m) ? Lv[(size_t)bh * m + i] : 0.f;
+    Dr[b] = (!JOINT && i < m) ? Dv[(size_t)bh * m + i] : 0.f;
+  }
+  zero_acc<IB, D>(ax);
+  zero_acc<IB, D>(aw);
+  const int j0 = chunk * L, j1 = min(N, j0 + L);
+  const SrcRows<T, D> src{Y + (size_t)bh * N * D, Z + (size_t)bh * N * D, JOINT ? Lv + (size_t)bh * N : nullptr,
+                          JOINT ? Dv + (size_t)bh * N : nullptr, j0, j1, cscale, cnat};
+  grad_stream<IB, !JOINT, JOINT, JOINT, NT, T, D>(smem, (j1 - j0 + 31) / 32, src, xf, wf, Lr, Dr, ax, aw, li, lg);
+#pragma unroll
+  for (int b = 0; b < IB; ++b) {
+    const int i = i0 + b * 16 + li;
+    if (i >= m) continue;
+    float* dst = part + (((size_t)bh * C + chunk) * m + i) * PW;
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb) {
+      *(float4*)(dst + cb * 16 + 4 * lg) = make_float4(ax[b][cb][0], ax[b][cb][1], ax[b][cb][2], ax[b][cb][3]);
+      if constexpr (JOINT)
+        *(float4*)(dst + D + cb * 16 + 4 * lg) = make_float4(aw[b][cb][0], aw[b][cb][1], aw[b][cb][2], aw[b][cb][3]);
+    }
+  }
+}
+
+// Key rows.  ROUTED: the k keys of expert e (grid y = slot * m + e) over the
+// queries routed to it in that slot; adds dk, dv to the fp32 accumulators.
+// Otherwise: every key over the nent landmark rows of the shared-value
+// softmax (nent = 0 in the routing-only variant); writes dK, dV = the
+// accumulators plus this part, in the input dtype.
+template <typename T, int D, int NW, int IB, bool ROUTED>
+__global__ __launch_bounds__(NW * 64, 2) void k_bwd_keys(
+    const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ Ysrc, const T* __restrict__ Zsrc,
+    const float* __restrict__ Lv, const float* __restrict__ Dv, const int32_t* __restrict__ topk,
+    const int32_t* __restrict__ perm, const int* __restrict__ gpre, const int* __restrict__ counts,
+    float* __restrict__ dKacc, float* __restrict__ dVacc, T* __restrict__ dK, T* __restrict__ dV, int N, int m,
+    int k, int nent, int BH, float cscale, float cnat) {
+  constexpr int NT = NW * 64;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, li = lane % 16, lg = lane / 16;
+  const int r0 = blockIdx.x * (NW * 16 * IB) + wave * 16 * IB;
+  int bh, cnt = 0, start = 0, slot = 0, e = 0;
+  if constexpr (ROUTED) {
+    bh = blockIdx.z;
+    slot = blockIdx.y / m;
+    e = blockIdx.y % m;
+    const size_t x = ((size_t)slot * BH + bh) * m + e;
+    cnt = counts[x];
+    if (cnt == 0) return;  // uniform over the block
+    start = gpre[x];
+  } else {
+    bh = blockIdx.y;
+  }
+  const int nrows = ROUTED ? k : N;
+  int jr[IB];
+#pragma unroll
+  for (int b = 0; b < IB; ++b) {
+    const int r = r0 + b * 16 + li;
+    if constexpr (ROUTED) jr[b] = r < k ? min(max(topk[((size_t)bh * m + e) * k + r], 0), N - 1) : -1;
+    else jr[b] = r < N ? r : -1;
+  }
+  (void)nrows;
+  Frag<T> xf[IB][D / 32], wf[IB][D / 32];
+  load_rows<T, D, IB>(xf, lg, [&](int b) -> const T* { return jr[b] >= 0 ? K + ((size_t)bh * N + jr[b]) * D : nullptr; });
+  load_rows<T, D, IB>(wf, lg, [&](int b) -> const T* { return jr[b] >= 0 ? V + ((size_t)bh * N + jr[b]) * D : nullptr; });
+  float Lr[IB] = {}, Dr[IB] = {};
+  f32x4 ax[IB][D / 16], aw[IB][D / 16];
+  zero_acc<IB, D>(ax);
+  zero_acc<IB, D>(aw);
+  if constexpr (ROUTED) {
+    const SrcPerm<T, D> src{Ysrc + (size_t)bh * N * D, Zsrc + (size_t)bh * N * D, Lv + (size_t)bh * N,
+                            Dv + (size_t)bh * N, perm + (size_t)slot * BH * N + start, cnt, cscale, cnat};
+    grad_stream<IB, false, true, true, NT, T, D>(smem, (cnt + 31) / 32, src, xf, wf, Lr, Dr, ax, aw, li, lg);
+  } else {
+    const SrcRows<T, D> src{Ysrc + (size_t)bh * m * D, Zsrc + (size_t)bh * m * D, Lv + (size_t)bh * m,
+                            Dv + (size_t)bh * m, 0, nent, cscale, cnat};
+    grad_stream<IB, false, true, true, NT, T, D>(smem, (nent + 31) / 32, src, xf, wf, Lr, Dr, ax, aw, li, lg);
+  }
+#pragma unroll
+  for (int b = 0; b < IB; ++b) {
+    if (jr[b] < 0) continue;
+    const size_t o = ((size_t)bh * N + jr[b]) * D;
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb) {
+      const int c0 = cb * 16 + 4 * lg;
+      if constexpr (ROUTED) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          unsafeAtomicAdd(dKacc + o + c0 + r, ax[b][cb][r]);
+          unsafeAtomicAdd(dVacc + o + c0 + r, aw[b][cb][r]);
+        }
+      } else {
+        const float4 gk = *(const float4*)(dKacc + o + c0);
+        const float4 gv = *(const float4*)(dVacc + o + c0);
+        const float vk[4] = {gk.x, gk.y, gk.z, gk.w}, vv[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          dK[o + c0 + r] = from_f32<T>(vk[r] + ax[b][cb][r]);
+          dV[o + c0 + r] = from_f32<T>(vv[r] + aw[b][cb][r]);
+        }
+      }
+    }
+  }
+}
+
+// Query rows of one work item (expert e, a tile of the queries routed to it
+// in `slot`) over the tile's joint-softmax entries.  Slots >= 1 store their
+// dq part; the slot-0 pass (launched last) adds the m_shared shared entries,
+// the stored parts and pooling's adjoint, and writes dQ.
+template <typename T, int D, int NW, int IB, bool SLOT0>
+__global__ __launch_bounds__(NW * 64, 2) void k_bwd_q(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
+    const T* __restrict__ qt, const T* __restrict__ vt, const float* __restrict__ lse, const float* __restrict__ Dn,
+    const int32_t* __restrict__ topk, const int32_t* __restrict__ perm, const WorkItem* __restrict__ wl,
+    const int* __restrict__ wl_count, const float* __restrict__ dqt, float* __restrict__ qpart, T* __restrict__ dQ,
+    int N, int m, int k, int s, int slot, int BH, int m_shared, int gh, int gw, int lh, int lw, float cscale,
+    float cscale_sh, float cnat, float cnat_sh) {
+  constexpr int NT = NW * 64;
+  extern __shared__ __align__(16) unsigned char smem[];
+  if ((int)blockIdx.x >= *wl_count) return;
+  const WorkItem it = wl[blockIdx.x];
+  const int bh = it.be / m;
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, li = lane % 16, lg = lane / 16;
+  int qn[IB];
+#pragma unroll
+  for (int b = 0; b < IB; ++b) {
+    const int local = wave * 16 * IB + b * 16 + li;
+    qn[b] = local < it.count ? perm[it.start + local] : -1;
+  }
+  const size_t row0 = (size_t)bh * N;
+  Frag<T> xf[IB][D / 32], wf[IB][D / 32];
+  load_rows<T, D, IB>(xf, lg, [&](int b) -> const T* { return qn[b] >= 0 ? Q + (row0 + qn[b]) * D : nullptr; });
+  load_rows<T, D, IB>(wf, lg, [&](int b) -> const T* { return qn[b] >= 0 ? dO + (row0 + qn[b]) * D : nullptr; });
+  float Lr[IB], Dr[IB];
+#pragma unroll
+  for (int b = 0; b < IB; ++b) {
+    Lr[b] = qn[b] >= 0 ? lse[row0 + qn[b]] : 0.f;
+    Dr[b] = qn[b] >= 0 ? Dn[row0 + qn[b]] : 0.f;
+  }
+  f32x4 ax[IB][D / 16], aw[IB][D / 16];
+  zero_acc<IB, D>(ax);
+  const int m0 = SLOT0 ? m_shared : 0;
+  const int ns = (m0 + 31) / 32;
+  const SrcJoint<T, D> src{qt + (size_t)bh * m * D, vt + (size_t)bh * m * D, K + row0 * D, V + row0 * D,
+                           topk + (size_t)it.be * k, m0, ns, k, N, cscale, cnat, cscale_sh, cnat_sh};
+  grad_stream<IB, true, false, false, NT, T, D>(smem, ns + (k + 31) / 32, src, xf, wf, Lr, Dr, ax, aw, li, lg);
+
+#pragma unroll
+  for (int b = 0; b < IB; ++b) {
+    if (qn[b] < 0) continue;
+    const size_t qrow = row0 + qn[b];
+    if constexpr (!SLOT0) {
+      float* dst = qpart + ((size_t)(slot - 1) * BH * N + qrow) * D;
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb)
+        *(float4*)(dst + cb * 16 + 4 * lg) = make_float4(ax[b][cb][0], ax[b][cb][1], ax[b][cb][2], ax[b][cb][3]);
+    } else {
+      float v[D / 16][4];
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[cb][r] = ax[b][cb][r];
+      for (int t = 1; t < s; ++t) {
+        const float* src_ = qpart + ((size_t)(t - 1) * BH * N + qrow) * D;
+#pragma unroll
+        for (int cb = 0; cb < D / 16; ++cb) {
+          const float4 a = *(const float4*)(src_ + cb * 16 + 4 * lg);
+          v[cb][0] += a.x; v[cb][1] += a.y; v[cb][2] += a.z; v[cb][3] += a.w;
+        }
+      }
+      if (m_shared > 0) {
+        // pooling's adjoint: token (y, x) lies in landmark windows
+        // iy in [floor(y lh / gh), ceil((y + 1) lh / gh) - 1] (likewise x),
+        // window iy spanning [floor(iy gh / lh), ceil((iy + 1) gh / lh))
+        const long long y = qn[b] / gw, x = qn[b] % gw;
+        const int ylo = (int)(y * lh / gh), yhi = min(lh - 1, (int)(((y + 1) * lh + gh - 1) / gh) - 1);
+        const int xlo = (int)(x * lw / gw), xhi = min(lw - 1, (int)(((x + 1) * lw + gw - 1) / gw) - 1);
+        for (int iy = ylo; iy <= yhi; ++iy) {
+          const long long hy = ((long long)(iy + 1) * gh + lh - 1) / lh - (long long)iy * gh / lh;
+          for (int ix = xlo; ix <= xhi; ++ix) {
+            const long long hx = ((long long)(ix + 1) * gw + lw - 1) / lw - (long long)ix * gw / lw;
+            const float w = 1.0f / (float)(hy * hx);
+            const float* g = dqt + ((size_t)bh * m + (size_t)iy * lw + ix) * D;
+#pragma unroll
+            for (int cb = 0; cb < D / 16; ++cb) {
+              const float4 a = *(const float4*)(g + cb * 16 + 4 * lg);
+              v[cb][0] += w * a.x; v[cb][1] += w * a.y; v[cb][2] += w * a.z; v[cb][3] += w * a.w;
+            }
+          }
+        }
+      }
+      T* dst = dQ + qrow * D;
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[cb * 16 + 4 * lg + r] = from_f32<T>(v[cb][r]);
+    }
+  }
+  (void)aw;
+}
+
+// ---------------------------------------------------------------------------
+// small passes
+
+// delta_n = dO_n . o_n (fp32) with o_n the forward's output before rounding,
+// so that delta equals sum_t P_t dP_t up to fp32 rounding even where one
+// entry dominates and dP_t - delta cancels.  CPR lanes per row.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_bwd_dot(const float* __restrict__ O32, const T* __restrict__ dO,
+                                                 float* __restrict__ Dn, long long rows) {
+  constexpr int EPC = 16 / (int)sizeof(T), CPR = D / EPC;
+  const long long g = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = g / CPR;
+  const int c = (int)(g % CPR);
+  float acc = 0.f;
+  if (row < rows) {
+    const uint4 b = *(const uint4*)(dO + row * D + c * EPC);
+    const T* pb = (const T*)&b;
+    const float4* pa = (const float4*)(O32 + row * D + c * EPC);
+#pragma unroll
+    for (int q = 0; q < EPC / 4; ++q) {
+      const float4 a = pa[q];
+      acc = __builtin_fmaf(a.x, to_f32(pb[4 * q]), acc);
+      acc = __builtin_fmaf(a.y, to_f32(pb[4 * q + 1]), acc);
+      acc = __builtin_fmaf(a.z, to_f32(pb[4 * q + 2]), acc);
+      acc = __builtin_fmaf(a.w, to_f32(pb[4 * q + 3]), acc);
+    }
+  }
+#pragma unroll
+  for (int off = CPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && c == 0) Dn[row] = acc;
+}
+
+// v~ in the input dtype, rounded as the forward rounded it for step 6.
+template <typename T>
+__global__ __launch_bounds__(256) void k_bwd_cvt(const float* __restrict__ x, T* __restrict__ y, long long n) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) y[i] = from_f32<T>(x[i]);
+}
+
+// Per-(slot, head, expert) query counts from the saved routes, which are
+// copied (clamped into [0, m)) for the grouping kernels.
+constexpr int CNT_PER_WG = 4096;
+__global__ __launch_bounds__(256) void k_bwd_count(const int32_t* __restrict__ route_in, int32_t* __restrict__ route,
+                                                   int* __restrict__ counts, int N, int m, int s, int BH, int hist_lds) {
+  extern __shared__ int hist[];
+  const int bh = blockIdx.y;
+  if (hist_lds) {
+    for (int x = threadIdx.x; x < s * m; x += 256) hist[x] = 0;
+    __syncthreads();
+  }
+  const long long tot = (long long)N * s;
+  const long long base = (long long)bh * tot;
+  const long long e0 = (long long)blockIdx.x * CNT_PER_WG;
+  for (int u = threadIdx.x; u < CNT_PER_WG; u += 256) {
+    const long long x = e0 + u;
+    if (x < tot) {
+      const int e = min(max(route_in[base + x], 0), m - 1);
+      route[base + x] = e;
+      const int t = (int)(x % s);
+      if (hist_lds) atomicAdd(hist + t * m + e, 1);
+      else atomicAdd(counts + ((size_t)t * BH + bh) * m + e, 1);
+    }
+  }
+  if (hist_lds) {
+    __syncthreads();
+    for (int x = threadIdx.x; x < s * m; x += 256) {
+      const int c = hist[x];
+      if (c) atomicAdd(counts + ((size_t)(x / m) * BH + bh) * m + (x % m), c);
+    }
+  }
+}
+
+// Sum of the joint pass's chunk partials per landmark row: dq~ (joint part),
+// dv~ (fp32 and input dtype) and delta = dv~ . v~, taken with the rounded
+// dv~ the matrix cores use for dA = dv~ . v_j and the fp32 v~, so that
+// dA_j - delta = dv~ . (v_j - v~) holds without bf16 cancellation error.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void k_bwd_red1(const float* __restrict__ part, const float* __restrict__ vt32,
+                                                 float* __restrict__ dqt, float* __restrict__ dvt,
+                                                 T* __restrict__ dvtT, float* __restrict__ delta, int m, int C) {
+  const size_t row = blockIdx.x;
+  const size_t bh = row / m, i = row % m;
+  const int c = threadIdx.x;
+  float q = 0.f, v = 0.f;
+  if (c < D) {
+    const float* p = part + ((bh * C) * m + i) * 2 * D;
+    for (int ch = 0; ch < C; ++ch, p += (size_t)m * 2 * D) {
+      q += p[c];
+      v += p[D + c];
+    }
+  }
+  const T vr = from_f32<T>(v);
+  float dd = c < D ? to_f32(vr) * vt32[row * D + c] : 0.f;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) dd += __shfl_xor(dd, off);
+  if (c < D) {
+    dqt[row * D + c] = q;
+    dvt[row * D + c] = v;
+    dvtT[row * D + c] = vr;
+  }
+  if (c == 0) delta[row] = dd;
+}
+
+// dq~ += the shared-value pass's chunk partials.
+template <int D>
+__global__ __launch_bounds__(64) void k_bwd_red4(const float* __restrict__ part, float* __restrict__ dqt, int m,
+                                                 int C) {
+  const size_t row = blockIdx.x;
+  const size_t bh = row / m, i = row % m;
+  const int c = threadIdx.x;
+  if (c >= D) return;
+  float q = 0.f;
+  const float* p = part + ((bh * C) * m + i) * D;
+  for (int ch = 0; ch < C; ++ch, p += (size_t)m * D) q += p[c];
+  dqt[row * D + c] += q;
+}
+
+__global__ __launch_bounds__(256) void k_bwd_zero(uint4* __restrict__ p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+template <class F>
+static void allow_lds(F fn, size_t lds) {
+  if (lds > 65536)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
+template <typename T, int D, int NW, int IB>
+static void launch_backward_t(const BPlan& p) {
+  constexpr int R = NW * 16 * IB;
+  const size_t lds = 2 * GradLds<T, D>::STEP_BYTES;
+  const hipStream_t st = p.stream;
+  const int BH = p.BH, N = p.N, m = p.m, k = p.k, s = p.s;
+
+  const size_t n16 = p.zero_bytes / 16;
+  if (n16) {
+    const int blocks = (int)((n16 + 255) / 256 < 4096 ? (n16 + 255) / 256 : 4096);
+    hipLaunchKernelGGL(k_bwd_zero, dim3(blocks), dim3(256), 0, st, (uint4*)p.zero_begin, n16);
+  }
+  {
+    constexpr int CPR = D * (int)sizeof(T) / 16;
+    const long long rows = (long long)BH * N;
+    const long long blocks = (rows * CPR + 255) / 256;
+    hipLaunchKernelGGL((k_bwd_dot<T, D>), dim3((unsigned)blocks), dim3(256), 0, st, p.o32, (const T*)p.dO,
+                       p.Dn, rows);
+  }
+  if (p.shared) {
+    const long long n = (long long)BH * m * D;
+    hipLaunchKernelGGL((k_bwd_cvt<T>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p.vt32, (T*)p.vt, n);
+  }
+  {
+    const int hist_lds = s * m <= 8192 ? 1 : 0;
+    dim3 grid((unsigned)(((long long)N * s + CNT_PER_WG - 1) / CNT_PER_WG), (unsigned)BH);
+    hipLaunchKernelGGL(k_bwd_count, grid, dim3(256), hist_lds ? (size_t)s * m * 4 : 0, st, p.route, p.bk.route,
+                       p.bk.counts, N, m, s, BH, hist_lds);
+  }
+  launch_bucket(p.bk);
+
+  // routed keys (atomic adds into the fp32 accumulators)
+  {
+    auto fn = &k_bwd_keys<T, D, NW, IB, true>;
+    allow_lds(fn, lds);
+    dim3 grid((unsigned)((k + R - 1) / R), (unsigned)(s * m), (unsigned)BH);
+    hipLaunchKernelGGL(fn, grid, dim3(NW * 64), lds, st, (const T*)p.K, (const T*)p.V, (const T*)p.Q,
+                       (const T*)p.dO, p.lse, p.Dn, p.topk, p.bk.perm, p.bk.gpre, p.bk.counts, p.dKacc, p.dVacc,
+                       (T*)nullptr, (T*)nullptr, N, m, k, 0, BH, p.cscale, p.cnat);
+  }
+  if (p.shared) {
+    auto fn = &k_bwd_lm<T, D, NW, IB, true>;
+    allow_lds(fn, lds);
+    dim3 grid((unsigned)((m + R - 1) / R), (unsigned)p.C1, (unsigned)BH);
+    hipLaunchKernelGGL(fn, grid, dim3(NW * 64), lds, st, (const T*)p.Q, (const T*)p.dO, (const T*)p.qt,
+                       (const T*)p.vt, p.lse, p.Dn, p.part1, N, m, p.L1, p.C1, p.cscale_sh, p.cnat_sh);
+    hipLaunchKernelGGL((k_bwd_red1<T, D>), dim3((unsigned)(BH * m)), dim3(64), 0, st, p.part1, p.vt32,
+                       p.dqt, p.dvt, (T*)p.dvtT, p.delta, m, p.C1);
+  }
+  // shared-value softmax for the keys, added to the routed part: final dK, dV
+  {
+    auto fn = &k_bwd_keys<T, D, NW, IB, false>;
+    allow_lds(fn, lds);
+    dim3 grid((unsigned)((N + R - 1) / R), (unsigned)BH);
+    hipLaunchKernelGGL(fn, grid, dim3(NW * 64), lds, st, (const T*)p.K, (const T*)p.V, (const T*)p.qt,
+                       (const T*)p.dvtT, p.lse_lm, p.delta, p.topk, p.bk.perm, p.bk.gpre, p.bk.counts, p.dKacc,
+                       p.dVacc, (T*)p.dK, (T*)p.dV, N, m, k, p.shared ? m : 0, BH, p.cscale, p.cnat);
+  }
+  if (p.shared) {
+    auto fn = &k_bwd_lm<T, D, NW, IB, false>;
+    allow_lds(fn, lds);
+    dim3 grid((unsigned)((m + R - 1) / R), (unsigned)p.C4, (unsigned)BH);
+    hipLaunchKernelGGL(fn, grid, dim3(NW * 64), lds, st, (const T*)p.K, (const T*)p.V, (const T*)p.qt,
+                       (const T*)p.dvtT, p.lse_lm, p.delta, p.part4, N, m, p.L4, p.C4, p.cscale, p.cnat);
+    hipLaunchKernelGGL((k_bwd_red4<D>), dim3((unsigned)(BH * m)), dim3(64), 0, st, p.part4, p.dqt, m, p.C4);
+  }
+  // queries: slots s-1 .. 1 store parts, slot 0 finishes dQ
+  {
+    auto f1 = &k_bwd_q<T, D, NW, IB, false>;
+    auto f0 = &k_bwd_q<T, D, NW, IB, true>;
+    allow_lds(f1, lds);
+    allow_lds(f0, lds);
+    for (int t = s - 1; t >= 0; --t) {
+      const int32_t* perm = p.bk.perm + (size_t)t * BH * N;
+      const WorkItem* wl = p.bk.wl + (size_t)t * p.bk.UB;
+      const int* wlc = p.bk.wl_count + t;
+      hipLaunchKernelGGL(t > 0 ? f1 : f0, dim3((unsigned)p.bk.UB), dim3(NW * 64), lds, st, (const T*)p.Q,
+                         (const T*)p.K, (const T*)p.V, (const T*)p.dO, (const T*)p.qt, (const T*)p.vt, p.lse, p.Dn,
+                         p.topk, perm, wl, wlc, p.dqt, p.qpart, (T*)p.dQ, N, m, k, s, t, BH, p.shared ? m : 0,
+                         p.gh, p.gw, p.lh, p.lw, p.cscale, p.cscale_sh, p.cnat, p.cnat_sh);
+    }
+  }
+}
+
+// Rows per workgroup of every backward kernel for a dtype (the plan's R).
+int backward_rows(int dtype) { return dtype == 1 ? 8 * 16 * 2 : 4 * 16 * 1; }
+
+void launch_backward(const BPlan& p) {
+  if (p.dtype == 0) {
+    if (p.d == 32) launch_backward_t<float, 32, 4, 1>(p); else launch_backward_t<float, 64, 4, 1>(p);
+  } else {
+    if (p.d == 32) launch_backward_t<__bf16, 32, 8, 2>(p); else launch_backward_t<__bf16, 64, 8, 2>(p);
+  }
+}
+
+}  // namespace mita

@@ -28,6 +28,12 @@ struct WorkItem {
   int pad;
 };
 
+// Outputs the forward keeps for the backward pass (each nullptr: not written).
+struct TrainOut {
+  float* lse;  // [BH, N] log2-sum-exp of each query's joint softmax
+  float* o32;  // [BH, N, d] output before rounding to the input dtype
+};
+
 struct Plan {
   // arguments
   int dtype;  // 0 f32, 1 bf16
@@ -83,6 +89,11 @@ struct Plan {
   size_t zero_bytes;
   size_t total_bytes;
 
+  // optional outputs kept for the backward pass (nullptr: not written)
+  float* lse_out;   // [BH, N] log2-sum-exp of each query's joint softmax
+  float* lse_lm;    // [BH, m] log2-sum-exp of each landmark row over all N keys
+  float* o32;       // [BH, N, d] the output before rounding to the input dtype
+
   // call
   const void* Q;
   const void* K;
@@ -106,6 +117,51 @@ void launch_expert(const Plan& p);
 void launch_dense(const void* Q, const void* K, const void* V, void* O, int dtype, int BH, int N, int d,
                   hipStream_t stream);
 size_t resident_bytes(int dtype, int d, int E);
+
+// Host-side plan of one backward call (mita_backward): sizes, launch shapes
+// and workspace regions, derived from the arguments alone.
+struct BPlan {
+  int dtype, esize, BH, N, d, gh, gw, lh, lw, m, k, s;
+  int shared;            // 1: shared entries in the joint softmax (not the routing-only variant)
+  float cscale, cscale_sh;  // log2(e) x logit scale (routed / shared logits)
+  float cnat, cnat_sh;      // the logit scales themselves
+  int R;                 // stationary rows per workgroup
+  int L1, C1;            // joint pass over queries: entries per chunk, chunks
+  int L4, C4;            // shared-value pass over keys: entries per chunk, chunks
+  Plan bk;               // query grouping by expert (counts, prefix, permutation, work list)
+
+  // workspace
+  float* Dn;      // [BH, N] dO . O per query
+  float* dKacc;   // [BH, N, d] routed key gradients (zeroed each call)
+  float* dVacc;   // [BH, N, d]
+  float* part1;   // [BH, C1, m, 2d] per-chunk dq~ and dv~ of the joint softmax
+  float* part4;   // [BH, C4, m, d] per-chunk dq~ of the shared-value softmax
+  float* dqt;     // [BH, m, d] dq~
+  float* dvt;     // [BH, m, d] dv~
+  void* dvtT;     // [BH, m, d] dv~ in the input dtype (matrix-core operand)
+  float* delta;   // [BH, m] dv~ . v~
+  float* qpart;   // [s - 1, BH, N, d] dQ of slots 1 .. s-1
+  // (vt, the input-dtype copy of the saved v~, is also a workspace region)
+  void* zero_begin;
+  size_t zero_bytes;
+  size_t total_bytes;
+
+  // call
+  const void *Q, *K, *V, *O, *dO;
+  void *dQ, *dK, *dV;
+  const void* qt;         // saved q~ [BH, m, d]
+  const float* vt32;      // saved v~ [BH, m, d] (fp32)
+  void* vt;               // v~ rounded to the input dtype as the forward used it (workspace)
+  const float* o32;       // saved output before rounding [BH, N, d]
+  const int32_t* topk;    // saved experts [BH, m, k]
+  const int32_t* route;   // saved routes [BH, N, s]
+  const float* lse;       // saved [BH, N]
+  const float* lse_lm;    // saved [BH, m]
+  hipStream_t stream;
+};
+void launch_backward(const BPlan& p);
+// stationary rows per workgroup of the backward kernels (dtype 0 f32, 1 bf16)
+int backward_rows(int dtype);
 // LDS a resident entry set may take (of 160 KB per compute unit).
 constexpr size_t RES_MAX = 150 * 1024;
 

@@ -308,7 +308,7 @@ template <int IB, typename T, int D>
 __device__ __forceinline__ void expert_group(const Frag<T> (&qf)[IB][D / 32], const int (&qn)[IB], const T* Ks,
                                              const T* Vs, int Kp, int k, const Frag<T>& one, size_t row0,
                                              float* __restrict__ plse, typename PartT<T>::type* __restrict__ po,
-                                             T* __restrict__ O, int merge_in, int last, float cscale, int li,
+                                             T* __restrict__ O, TrainOut tr, int merge_in, int last, float cscale, int li,
                                              int lg) {
   using RL = Resident<T, D>;
   using P = typename PartT<T>::type;
@@ -359,6 +359,7 @@ __device__ __forceinline__ void expert_group(const Frag<T> (&qf)[IB][D / 32], co
         T* dst = O + qrow * D + cb * 16 + 4 * lg;
 #pragma unroll
         for (int r = 0; r < 4; ++r) dst[r] = from_f32<T>(v[r]);
+        if (tr.o32) *(float4*)(tr.o32 + qrow * D + cb * 16 + 4 * lg) = make_float4(v[0], v[1], v[2], v[3]);
       } else {
         PV w;
 #pragma unroll
@@ -366,28 +367,35 @@ __device__ __forceinline__ void expert_group(const Frag<T> (&qf)[IB][D / 32], co
         *(PV*)(o + part_pos<D>(lg, cb)) = w;
       }
     }
-    if (!last && lg == 0) plse[qrow] = mx + __builtin_amdgcn_logf(den);
+    if (lg == 0) {
+      // the log2-sum-exp of everything merged so far: the next slot's input,
+      // or after the last slot the query's whole normaliser (kept for the
+      // backward pass when requested)
+      const float lse = mx + __builtin_amdgcn_logf(den);
+      if (!last) plse[qrow] = lse;
+      else if (tr.lse) tr.lse[qrow] = lse;
+    }
   }
 }
 
 template <int IBX, typename T, int D, class QR>
 __device__ __forceinline__ void expert_blocks(const T* Qh, QR qrow, const T* Ks, const T* Vs, int Kp, int k,
                                               const Frag<T>& one, size_t row0, float* plse,
-                                              typename PartT<T>::type* po, T* O, int merge_in, int last,
+                                              typename PartT<T>::type* po, T* O, TrainOut tr, int merge_in, int last,
                                               float cscale, int li, int lg) {
   Frag<T> qf[IBX][D / 32];
   int qn[IBX];
   load_queries<T, D, IBX>(qf, Qh, lg, qrow);
 #pragma unroll
   for (int b = 0; b < IBX; ++b) qn[b] = (int)qrow(b);
-  expert_group<IBX, T, D>(qf, qn, Ks, Vs, Kp, k, one, row0, plse, po, O, merge_in, last, cscale, li, lg);
+  expert_group<IBX, T, D>(qf, qn, Ks, Vs, Kp, k, one, row0, plse, po, O, tr, merge_in, last, cscale, li, lg);
 }
 
 template <typename T, int D, int NW, int IB>
 __global__ __launch_bounds__(NW * 64, 2) void k_expert(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const int32_t* __restrict__ topk,
     const int32_t* __restrict__ perm, const WorkItem* __restrict__ wl, const int* __restrict__ wl_count,
-    float* __restrict__ plse, typename PartT<T>::type* __restrict__ po, T* __restrict__ O, int N, int m, int k,
+    float* __restrict__ plse, typename PartT<T>::type* __restrict__ po, T* __restrict__ O, TrainOut tr, int N, int m, int k,
     int merge_in, int last, float cscale) {
   using RL = Resident<T, D>;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -435,7 +443,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_expert(
       qn[b] = s_q[gi * GQ + b * 16 + li];
     }
     if (gi + NW < nfull) load_queries<T, D, IB>(qnx, Qh, lg, group_rows(gi + NW));
-    expert_group<IB, T, D>(qf, qn, Ks, Vs, Kp, k, one, row0, plse, po, O, merge_in, last, cscale, li, lg);
+    expert_group<IB, T, D>(qf, qn, Ks, Vs, Kp, k, one, row0, plse, po, O, tr, merge_in, last, cscale, li, lg);
   }
   // ... then the rest in blocks of 16 queries dealt to the waves in turn, so
   // a short remainder keeps every wave busy on narrower groups
@@ -447,13 +455,13 @@ __global__ __launch_bounds__(NW * 64, 2) void k_expert(
     return l < it.count ? s_q[l] : -1;
   };
   if constexpr (IB >= 4) {
-    if (mine == 4) expert_blocks<4, T, D>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, merge_in, last, cscale, li, lg);
-    if (mine == 3) expert_blocks<3, T, D>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, merge_in, last, cscale, li, lg);
+    if (mine == 4) expert_blocks<4, T, D>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, tr, merge_in, last, cscale, li, lg);
+    if (mine == 3) expert_blocks<3, T, D>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, tr, merge_in, last, cscale, li, lg);
   }
   if constexpr (IB >= 2) {
-    if (mine == 2) expert_blocks<2, T, D>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, merge_in, last, cscale, li, lg);
+    if (mine == 2) expert_blocks<2, T, D>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, tr, merge_in, last, cscale, li, lg);
   }
-  if (mine == 1) expert_blocks<1, T, D>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, merge_in, last, cscale, li, lg);
+  if (mine == 1) expert_blocks<1, T, D>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, tr, merge_in, last, cscale, li, lg);
 }
 
 // ---------------------------------------------------------------------------
@@ -505,7 +513,7 @@ static void launch_expert_t(const Plan& p) {
     const int32_t* perm = p.perm + (size_t)t * p.BH * p.N;
     const WorkItem* wl = p.wl + (size_t)t * p.UB;
     hipLaunchKernelGGL(fn, dim3((unsigned)(p.UB + 8)), dim3(NW * 64), lds, p.stream, (const T*)p.Q, (const T*)p.K,
-                       (const T*)p.V, p.topk, perm, wl, p.wl_count + t, p.plse, (typename PartT<T>::type*)p.po, (T*)p.O, p.N, p.m, p.k,
+                       (const T*)p.V, p.topk, perm, wl, p.wl_count + t, p.plse, (typename PartT<T>::type*)p.po, (T*)p.O, TrainOut{p.lse_out, p.o32}, p.N, p.m, p.k,
                        (t > 0 || p.shared) ? 1 : 0, t == p.s - 1 ? 1 : 0, p.cscale);
   }
 }

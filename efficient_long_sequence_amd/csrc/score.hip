@@ -324,7 +324,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void k_final(const float* __restrict__ vpart, const uint64_t* __restrict__ cand,
                                                const int* __restrict__ cand_cnt, int32_t* __restrict__ topk,
                                                float* __restrict__ vt32, T* __restrict__ vtT, int* __restrict__ fail,
-                                               int N, int k, int C, int capg, int dense, int shared) {
+                                               float* __restrict__ lse_lm, int N, int k, int C, int capg, int dense,
+                                               int shared) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint64_t* a = (uint64_t*)smem;
   __shared__ float red[256];
@@ -362,6 +363,8 @@ __global__ __launch_bounds__(256) void k_final(const float* __restrict__ vpart, 
       float sv = 0.f, zs = 0.f;
       for (int g = 0; g < NG; ++g) { sv += red[g * D + tid]; zs += zred[g]; }
       const float v = sv / zs;
+      // the row's log2-sum-exp, kept for the backward pass when requested
+      if (lse_lm && tid == 0) lse_lm[r] = Mx + __builtin_amdgcn_logf(zs);
       vt32[r * D + tid] = v;
       vtT[r * D + tid] = from_f32<T>(v);
     }
@@ -526,7 +529,7 @@ static void launch_final_t(const Plan& p) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_final<T, D>), hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)lds);
   hipLaunchKernelGGL((k_final<T, D>), dim3((unsigned)(p.BH * p.m)), dim3(256), lds, p.stream, p.vpart, p.cand,
-                     p.cand_cnt, p.topk, p.vt32, (T*)p.vtT, p.fail, p.N, p.k, p.C, p.capg, p.dense, p.shared);
+                     p.cand_cnt, p.topk, p.vt32, (T*)p.vtT, p.fail, p.lse_lm, p.N, p.k, p.C, p.capg, p.dense, p.shared);
   if (!p.dense) {
     const size_t lds2 = (size_t)next_pow2(2 * p.k + 256) * 8;
     hipLaunchKernelGGL((k_fallback<T, D>), dim3((unsigned)(p.BH * p.m)), dim3(256), lds2, p.stream,

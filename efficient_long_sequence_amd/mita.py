@@ -26,7 +26,7 @@ STATUS = {
 EXPORTS = [
     "mita_workspace_bytes", "mita_forward", "mita_forward_timed", "mita_forward_variant", "mita_dense_attention", "mita_num_stages",
     "mita_stage_name", "mita_events_create", "mita_events_destroy", "mita_events_elapsed",
-    "mita_status_str", "mita_version",
+    "mita_status_str", "mita_version", "mita_forward_train", "mita_backward_workspace_bytes", "mita_backward",
 ]
 
 
@@ -38,6 +38,12 @@ class Pool(ctypes.Structure):
 class Debug(ctypes.Structure):
     _fields_ = [("topk", ctypes.c_void_p), ("route", ctypes.c_void_p),
                 ("vtilde", ctypes.c_void_p), ("qtilde", ctypes.c_void_p)]
+
+
+class Saved(ctypes.Structure):
+    _fields_ = [("qtilde", ctypes.c_void_p), ("vtilde", ctypes.c_void_p), ("topk", ctypes.c_void_p),
+                ("route", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("lse_landmark", ctypes.c_void_p),
+                ("out_f32", ctypes.c_void_p)]
 
 
 class MitaError(RuntimeError):
@@ -80,6 +86,13 @@ def lib() -> ctypes.CDLL:
     L.mita_events_destroy.argtypes = [ctypes.POINTER(vp), c_int]
     L.mita_events_elapsed.restype = c_int
     L.mita_events_elapsed.argtypes = [ctypes.POINTER(vp), c_int, ctypes.POINTER(ctypes.c_float)]
+    L.mita_forward_train.restype = c_int
+    L.mita_forward_train.argtypes = fwd[:13] + [c_int, ctypes.POINTER(Saved), vp, c_size, vp]
+    L.mita_backward_workspace_bytes.restype = c_size
+    L.mita_backward_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int, Pool, c_int, c_int, c_int]
+    L.mita_backward.restype = c_int
+    L.mita_backward.argtypes = [vp] * 8 + [c_int, c_int, c_int, c_int, c_int, Pool, c_int, c_int, c_int, c_int,
+                                           ctypes.POINTER(Saved), vp, c_size, vp]
     L.mita_status_str.restype = ctypes.c_char_p
     L.mita_status_str.argtypes = [c_int]
     L.mita_version.restype = ctypes.c_char_p
@@ -217,3 +230,116 @@ def forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, pool, k: int, s: 
         code = L.mita_forward_timed(*args, events.arr)
     _check(code)
     return (O, dbg) if debug else O
+
+
+# ---------------------------------------------------------------------------
+# training: forward that keeps what the backward needs, and the backward
+@dataclass
+class SavedOut:
+    """What mita_forward_train keeps for mita_backward (device tensors)."""
+    qtilde: torch.Tensor        # dtype [B, H, m, d]
+    vtilde: torch.Tensor        # float32 [B, H, m, d] (unused by the routing-only variant)
+    topk: torch.Tensor          # int32 [B, H, m, k]
+    route: torch.Tensor         # int32 [B, H, N, s]
+    lse: torch.Tensor           # float32 [B, H, N]: log2 of each query's joint normaliser
+    lse_landmark: torch.Tensor  # float32 [B, H, m]: log2 of each landmark row's normaliser
+    out_f32: torch.Tensor       # float32 [B, H, N, d]: the output before rounding
+
+    def struct(self) -> Saved:
+        return Saved(self.qtilde.data_ptr(), self.vtilde.data_ptr(), self.topk.data_ptr(),
+                     self.route.data_ptr(), self.lse.data_ptr(), self.lse_landmark.data_ptr(),
+                     self.out_f32.data_ptr())
+
+
+def _check_qkv(*ts):
+    Q = ts[0]
+    for t in ts:
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != Q.dtype or t.shape != Q.shape:
+            raise MitaError(2, "tensors must be contiguous device tensors of one shape and dtype")
+
+
+def forward_train(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, pool, k: int, s: int,
+                  variant: str = "paper", workspace: torch.Tensor | None = None):
+    """Forward pass that also keeps the tensors the backward pass needs.
+    Returns (O, SavedOut)."""
+    L = lib()
+    _check_qkv(Q, K, V)
+    if variant not in VARIANTS:
+        raise MitaError(3, f"unknown variant {variant!r}")
+    B, H, N, d = Q.shape
+    gh, gw, lh, lw = pool
+    m = lh * lw
+    dt = _dtype_code(Q.dtype)
+    P = Pool(gh, gw, lh, lw)
+    if workspace is None:
+        workspace = torch.empty(max(int(L.mita_workspace_bytes(dt, B, H, N, d, P, m, k, s)), 16),
+                                dtype=torch.uint8, device=Q.device)
+    dev = Q.device
+    sv = SavedOut(
+        qtilde=torch.empty((B, H, m, d), dtype=Q.dtype, device=dev),
+        vtilde=torch.empty((B, H, m, d), dtype=torch.float32, device=dev),
+        topk=torch.empty((B, H, m, k), dtype=torch.int32, device=dev),
+        route=torch.empty((B, H, N, s), dtype=torch.int32, device=dev),
+        lse=torch.empty((B, H, N), dtype=torch.float32, device=dev),
+        lse_landmark=torch.empty((B, H, m), dtype=torch.float32, device=dev),
+        out_f32=torch.empty((B, H, N, d), dtype=torch.float32, device=dev),
+    )
+    O = torch.empty_like(Q)
+    st = sv.struct()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(L.mita_forward_train(Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), dt, B, H, N, d, P, m, k, s,
+                                VARIANTS[variant], ctypes.byref(st), workspace.data_ptr(), workspace.numel(),
+                                stream))
+    return O, sv
+
+
+def backward_workspace_bytes(dtype: torch.dtype, B: int, H: int, N: int, d: int, pool, k: int, s: int) -> int:
+    gh, gw, lh, lw = pool
+    return int(lib().mita_backward_workspace_bytes(_dtype_code(dtype), B, H, N, d, Pool(gh, gw, lh, lw),
+                                                   lh * lw, k, s))
+
+
+def backward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, O: torch.Tensor, dO: torch.Tensor, pool,
+             k: int, s: int, saved: SavedOut, variant: str = "paper", workspace: torch.Tensor | None = None):
+    """Gradients (dQ, dK, dV) of sum(O * dO), experts and routes held fixed."""
+    L = lib()
+    _check_qkv(Q, K, V, O, dO)
+    if variant not in VARIANTS:
+        raise MitaError(3, f"unknown variant {variant!r}")
+    B, H, N, d = Q.shape
+    gh, gw, lh, lw = pool
+    m = lh * lw
+    dt = _dtype_code(Q.dtype)
+    P = Pool(gh, gw, lh, lw)
+    if workspace is None:
+        workspace = torch.empty(max(int(L.mita_backward_workspace_bytes(dt, B, H, N, d, P, m, k, s)), 16),
+                                dtype=torch.uint8, device=Q.device)
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(Q), torch.empty_like(Q)
+    st = saved.struct()
+    stream = torch.cuda.current_stream(Q.device).cuda_stream
+    _check(L.mita_backward(Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), dO.data_ptr(), dQ.data_ptr(),
+                           dK.data_ptr(), dV.data_ptr(), dt, B, H, N, d, P, m, k, s, VARIANTS[variant],
+                           ctypes.byref(st), workspace.data_ptr(), workspace.numel(), stream))
+    return dQ, dK, dV
+
+
+class MitaFunction(torch.autograd.Function):
+    """MiTA attention as an autograd function: forward_train / backward.
+
+    ``MitaFunction.apply(Q, K, V, pool, k, s, variant)``; gradients flow to
+    Q, K and V (experts and routes held fixed)."""
+
+    @staticmethod
+    def forward(ctx, Q, K, V, pool, k, s, variant="paper"):
+        Q, K, V = Q.contiguous(), K.contiguous(), V.contiguous()
+        O, sv = forward_train(Q, K, V, pool, k, s, variant=variant)
+        ctx.save_for_backward(Q, K, V, O)
+        ctx.sv, ctx.cfg = sv, (pool, k, s, variant)
+        return O
+
+    @staticmethod
+    def backward(ctx, dO):
+        Q, K, V, O = ctx.saved_tensors
+        pool, k, s, variant = ctx.cfg
+        dQ, dK, dV = backward(Q, K, V, O, dO.contiguous(), pool, k, s, ctx.sv, variant=variant)
+        return dQ, dK, dV, None, None, None, None

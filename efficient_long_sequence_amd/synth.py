@@ -15,6 +15,8 @@ Value recipes (all drawn in float64 from NumPy's PCG64, then rounded once):
 * ``runs``       as ``clustered`` but the cluster ids come in runs: the
                  sequence is cut into runs of length U{1..256}, each run
                  drawing one cluster id ~ U{0..G-1}.
+* upstream gradients (``make_grad``) for the backward pass: dO ~ N(0, 1)
+  independently, from their own seed.
 
 The three shapes stand in for the workloads the MiTA pages evaluate on:
 ImageNet-1K DeiT-S patches (14x14), ADE20K segmentation patches (32x32 and
@@ -129,3 +131,9 @@ def make_one_head(B: int, H: int, N: int, d: int, kind: str, n_clusters: int, dt
 
 def make_from_workload(w, seed_offset: int = 0):
     return make(w.B, w.H, w.N, w.d, w.kind, w.n_clusters, w.dtype, w.seed + seed_offset)
+
+
+def make_grad(B: int, H: int, N: int, d: int, dtype: str, seed: int) -> np.ndarray:
+    """Upstream gradient dO [B, H, N, d] ~ N(0, 1) (float32, dtype-exact)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0x6772])))
+    return _round(rng.standard_normal((B, H, N, d)), dtype).astype(np.float32)

@@ -151,6 +151,83 @@ mita_status mita_forward_variant(const void* Q, const void* K, const void* V, vo
 mita_status mita_dense_attention(const void* Q, const void* K, const void* V, void* O,
                                  mita_dtype dtype, int B, int H, int N, int d, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Training: the forward pass that keeps what the backward pass needs, and the
+ * backward pass.  The pages train MiTA models end to end (MiTA tutorial,
+ * chapter 7: LRA training time) without writing a backward pass; the one here
+ * differentiates steps 1-6 with the top-k experts (step 3) and the top-s
+ * routes (step 5) held fixed -- choices are constant wherever they are
+ * unique, so they pass no gradient -- and takes q~'s rounding to the input
+ * dtype as the identity (pooling's adjoint spreads d q~_i / |W_i| over window
+ * W_i).  Every other step is differentiated exactly, a key chosen by two of a
+ * query's experts counting twice as in the forward.
+ * ------------------------------------------------------------------------ */
+
+/* Tensors kept by mita_forward_train for mita_backward: device buffers owned
+ * by the caller, written by mita_forward_train, read by mita_backward.
+ *   qtilde       dtype [B, H, m, d]  landmark queries q~ (step 1)
+ *   vtilde       float [B, H, m, d]  shared values v~ (step 4) before the
+ *                step-6 softmax rounded them to the input dtype
+ *   topk         int32 [B, H, m, k]  experts (step 3)
+ *   route        int32 [B, H, N, s]  routes (step 5)
+ *   lse          float [B, H, N]     log2 of each query's step-6 normaliser,
+ *                log2(sum_t exp(z_t)) over its logits z_t
+ *   lse_landmark float [B, H, m]     log2(sum_j exp(q~_i . k_j / sqrt(d))),
+ *                the normaliser of step 4
+ *   out_f32      float [B, H, N, d]  the output before rounding to the input
+ *                dtype (the backward's dO . o is taken from it: where one
+ *                entry dominates a softmax, dP_t - dO . o cancels and the
+ *                rounded output would leave a 2^-8 relative error in it)
+ * qtilde, vtilde and out_f32 must be 16-byte aligned.  In MITA_VARIANT_ROUTED there is
+ * no step 4: vtilde and lse_landmark are not written or read and may be
+ * NULL.  mita_backward needs the contents written by mita_forward_train for
+ * the same inputs and arguments; other contents give unspecified results (all
+ * indices are clamped, so memory accesses stay in bounds). */
+typedef struct {
+  void* qtilde;
+  float* vtilde;
+  int32_t* topk;
+  int32_t* route;
+  float* lse;
+  float* lse_landmark;
+  float* out_f32;
+} mita_saved;
+
+/* mita_forward_variant (same arguments, same workspace size, same errors)
+ * that also fills `saved` (MITA_ERR_NULL if saved or a required member is
+ * NULL; MITA_ERR_PARAM if qtilde, vtilde or out_f32 is misaligned). */
+mita_status mita_forward_train(const void* Q, const void* K, const void* V, void* O,
+                               mita_dtype dtype, int B, int H, int N, int d, mita_pool pool,
+                               int m, int k, int s, mita_variant variant, const mita_saved* saved,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace mita_backward needs (0 if the arguments are
+ * invalid).  Host-only; no HIP call. */
+size_t mita_backward_workspace_bytes(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool,
+                                     int m, int k, int s);
+
+/* Gradients of sum(O * dO) with respect to Q, K and V.
+ *   Q, K, V, O  the forward's inputs and output (device, dtype, [B, H, N, d];
+ *               O is validated like the others but not read: saved->out_f32
+ *               stands in for it)
+ *   dO          device, dtype, [B, H, N, d]: the upstream gradient
+ *   dQ, dK, dV  device, dtype, [B, H, N, d], written (accumulated in fp32,
+ *               rounded once)
+ *   variant     the variant the forward ran with
+ *   saved       the tensors mita_forward_train kept
+ *   workspace   device, >= mita_backward_workspace_bytes(...), 16-byte
+ *               aligned, caller-owned, need not be initialised
+ * All pointers 16-byte aligned.  Same shape limits and errors as
+ * mita_forward (MITA_ERR_NULL also for a NULL dO, dQ, dK, dV or saved
+ * member); nothing is launched on a validation error.  Key gradients of the
+ * routed experts are summed with fp32 atomic adds, so dK and dV may differ
+ * in the last bits from call to call; dQ is deterministic. */
+mita_status mita_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                          void* dQ, void* dK, void* dV, mita_dtype dtype, int B, int H, int N, int d,
+                          mita_pool pool, int m, int k, int s, mita_variant variant,
+                          const mita_saved* saved, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* Number of timed stages and their names ("pool", "estimate", "score", ...). */
 int mita_num_stages(void);
 const char* mita_stage_name(int stage);

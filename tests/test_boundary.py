@@ -116,3 +116,61 @@ def test_dense_attention_rejects_invalid_arguments(kw, code):
     got = mita.lib().mita_dense_attention(a["Q"], a["K"], a["V"], a["O"], a["dt"], a["B"], a["H"], a["N"],
                                           a["d"], None)
     assert got == code
+
+
+def _saved(**kw):
+    a = dict(qtilde=A, vtilde=A, topk=A, route=A, lse=A, lse_landmark=A, out_f32=A)
+    a.update(kw)
+    return mita.Saved(a["qtilde"], a["vtilde"], a["topk"], a["route"], a["lse"], a["lse_landmark"], a["out_f32"])
+
+
+@pytest.mark.parametrize("variant,kw,code", [
+    (0, dict(qtilde=0), 1), (0, dict(lse=0), 1), (0, dict(lse_landmark=0), 1), (1, dict(vtilde=0), 1),
+    (0, dict(qtilde=A + 2), 3), (0, dict(vtilde=A + 8), 3), (5, {}, 3), (0, dict(out_f32=0), 1),
+    (2, dict(out_f32=A + 4), 3),
+    # the routing-only variant neither writes nor reads v~ and its normaliser
+    (2, dict(vtilde=0, lse_landmark=0), 5),
+    (0, {}, 5),  # valid saved set, undersized workspace
+])
+def test_forward_train_rejects_invalid_saved_tensors(variant, kw, code):
+    L = mita.lib()
+    P = mita.Pool(1, 4096, 1, 64)
+    sv = _saved(**kw)
+    got = L.mita_forward_train(A, A, A, A, mita.BF16, 1, 2, 4096, 64, P, 64, 64, 1, variant, ctypes.byref(sv),
+                               A, 16, None)
+    assert got == code
+    assert L.mita_forward_train(A, A, A, A, mita.BF16, 1, 2, 4096, 64, P, 64, 64, 1, 0, None, A, 1 << 40,
+                                None) == 1
+
+
+def _bwd(variant=0, sv=None, **kw):
+    a = dict(Q=A, K=A, V=A, O=A, dO=A, dQ=A, dK=A, dV=A, dt=mita.BF16, B=1, H=2, N=4096, d=64,
+             pool=(1, 4096, 1, 64), m=64, k=64, s=1, ws=A, wsb=16)
+    a.update(kw)
+    sv = _saved() if sv is None else sv
+    return mita.lib().mita_backward(a["Q"], a["K"], a["V"], a["O"], a["dO"], a["dQ"], a["dK"], a["dV"], a["dt"],
+                                    a["B"], a["H"], a["N"], a["d"], mita.Pool(*a["pool"]), a["m"], a["k"], a["s"],
+                                    variant, ctypes.byref(sv), a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=0), 1), (dict(dO=0), 1), (dict(dQ=0), 1), (dict(dV=0), 1), (dict(ws=0), 1),
+    (dict(N=4095), 2), (dict(k=0), 3), (dict(dK=A + 4), 3), (dict(dO=A + 2), 3), (dict(ws=A + 4), 3),
+    (dict(variant=9), 3), (dict(sv=_saved(topk=0)), 1), (dict(sv=_saved(route=0)), 1),
+    (dict(d=48), 4), (dict(s=9, m=64), 4), (dict(B=64, H=512, N=1 << 16, pool=(1, 1 << 16, 1, 64)), 4),
+    ({}, 5), (dict(variant=2, sv=_saved(vtilde=0, lse_landmark=0)), 5),
+])
+def test_backward_rejects_invalid_arguments(kw, code):
+    assert _bwd(**kw) == code
+
+
+def test_backward_workspace_bytes():
+    L = mita.lib()
+    P = mita.Pool(1, 1 << 20, 1, 512)
+    big = L.mita_backward_workspace_bytes(mita.BF16, 1, 2, 1 << 20, 64, P, 512, 512, 1)
+    # the fp32 key-gradient accumulators alone take 2 * B*H*N*d*4 bytes
+    assert 2 * 2 * (1 << 20) * 64 * 4 < big < 4 << 30
+    assert L.mita_backward_workspace_bytes(mita.BF16, 1, 2, 1 << 20, 64, P, 511, 512, 1) == 0
+    s2 = L.mita_backward_workspace_bytes(mita.BF16, 1, 2, 4096, 64, mita.Pool(1, 4096, 1, 64), 64, 64, 2)
+    s1 = L.mita_backward_workspace_bytes(mita.BF16, 1, 2, 4096, 64, mita.Pool(1, 4096, 1, 64), 64, 64, 1)
+    assert s2 > s1

@@ -1,0 +1,174 @@
+"""GPU parity of the backward pass (mita_forward_train + mita_backward) through the C ABI.
+
+The oracle (oracle/mita_backward.py, fp64 autograd pinned by central
+differences) differentiates the forward with the experts and routes held
+fixed; here it is given the GPU's own experts and routes (from the saved
+tensors), so both sides differentiate the same function.  The saved
+log-sum-exps are checked against their definitions first.
+
+Tolerance (bf16): the kernels round each probability and each softmax
+gradient to bf16 before the matrix cores (relative error <= 2^-8), accumulate
+in fp32 and round each gradient once to bf16 (<= 2^-8), and take dO . O from
+the bf16 output; every gradient element is a sum of such terms, so its error
+is a small multiple of 2^-8 of the largest terms.  The bar is relative to the
+tensor's largest reference entry: max error <= 2.5e-2, mean <= 2.5e-3 of it
+(fp32 inputs: 2e-4 and 2e-5, the fp32 matrix-core path rounds nothing to
+bf16).  Full-size (N = 1M) runs are checked by properties that hold at any
+size: value-shift invariance sum_j dV_j = sum_n dO_n and, for the
+routing-only variant, sum_j dK_j = 0 plus sampled query rows of dQ that the
+oracle computes one by one.
+"""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from efficient_long_sequence_amd import mita, synth
+from efficient_long_sequence_amd.configs import WORKLOADS
+from oracle import mita_backward as mb
+from oracle import mita_oracle as mo
+from tests import gpu_harness as gh_
+
+pytestmark = pytest.mark.gpu
+
+BTOL = {"bf16": dict(max=2.5e-2, mean=2.5e-3), "f32": dict(max=2e-4, mean=2e-5)}
+LOG2E = 1.0 / math.log(2.0)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+CASES = {
+    # label: (B, H, grid_h, grid_w, d, land_h, land_w, k, s, kind, clusters, dtype, variant)
+    "ade_2d": (1, 2, 16, 16, 64, 4, 4, 32, 1, "clustered", 8, "bf16", "paper"),
+    "long_s2": (1, 1, 1, 4096, 64, 1, 32, 64, 2, "runs", 16, "bf16", "paper"),
+    "ragged_d32": (1, 2, 1, 777, 32, 1, 13, 50, 1, "clustered", 8, "bf16", "paper"),
+    "overlap_s3": (2, 1, 7, 9, 64, 2, 3, 13, 3, "iid", 0, "bf16", "paper"),
+    "f32_d64_s2": (2, 1, 12, 20, 64, 4, 5, 20, 2, "iid", 0, "f32", "paper"),
+    "f32_d32": (1, 2, 9, 11, 32, 3, 2, 17, 1, "clustered", 4, "f32", "paper"),
+    "streaming_m600": (1, 1, 1, 12000, 64, 1, 600, 24, 2, "runs", 32, "bf16", "paper"),
+    "sparse_16k": (1, 1, 1, 16384, 64, 1, 64, 64, 1, "runs", 64, "bf16", "paper"),
+    "official_s2": (1, 2, 1, 3000, 64, 1, 24, 40, 2, "clustered", 8, "bf16", "official"),
+    "routed_s2": (1, 2, 1, 3000, 64, 1, 24, 64, 2, "clustered", 8, "bf16", "routed"),
+    "routed_f32": (1, 1, 6, 10, 32, 2, 2, 9, 1, "iid", 0, "f32", "routed"),
+}
+
+
+def _run(Q, K, V, dO, pool, k, s, dtype, variant):
+    q, kk, v, g = (gh_.to_device(x, dtype) for x in (Q, K, V, dO))
+    O, sv = mita.forward_train(q, kk, v, pool, k, s, variant=variant)
+    dQ, dK, dV = mita.backward(q, kk, v, O, g, pool, k, s, sv, variant=variant)
+    torch.cuda.synchronize()
+    host = {n: gh_.to_host(t) for n, t in (("O", O), ("dQ", dQ), ("dK", dK), ("dV", dV), ("qt", sv.qtilde),
+                                          ("lse", sv.lse), ("lse_lm", sv.lse_landmark))}
+    host["topk"] = sv.topk.cpu().numpy().astype(np.int64)
+    host["route"] = sv.route.cpu().numpy().astype(np.int64)
+    return host
+
+
+def _compare(name, got, ref, dtype):
+    scale = max(float(np.abs(ref).max()), 1e-30)
+    err = np.abs(got - ref)
+    mx, mean = float(err.max()) / scale, float(err.mean()) / scale
+    gh_.say(f"[gpu]   {name}: max {mx:.2e} mean {mean:.2e} (of max |ref| {scale:.3e})")
+    assert mx <= BTOL[dtype]["max"], name
+    assert mean <= BTOL[dtype]["mean"], name
+
+
+@pytest.mark.parametrize("label", list(CASES))
+def test_backward_parity(label):
+    B, H, gh, gw, d, lh, lw, k, s, kind, nc, dtype, variant = CASES[label]
+    N = gh * gw
+    seed = zlib.crc32(label.encode()) % 1000
+    Q, K, V = synth.make(B, H, N, d, kind, nc, dtype, seed)
+    dO = synth.make_grad(B, H, N, d, dtype, seed)
+    gh_.say(f"[gpu] backward {label} B={B} H={H} N={N} d={d} m={lh * lw} k={k} s={s} {dtype} {variant}")
+    r = _run(Q, K, V, dO, (gh, gw, lh, lw), k, s, dtype, variant)
+    for b in range(B):
+        for h in range(H):
+            I, e = r["topk"][b, h], r["route"][b, h]
+            Qh, Kh, Vh = (x[b, h].astype(np.float64) for x in (Q, K, V))
+            Qt = mo.landmarks(Qh, gh, gw, lh, lw, dtype)
+            np.testing.assert_array_equal(r["qt"][b, h], Qt)
+            # saved log-sum-exps (log2 units) against their definitions
+            L = mb.joint_lse(Qh, Kh, Qt, I, e, variant=variant) * LOG2E
+            assert np.abs(r["lse"][b, h] - L).max() <= 2e-3 * max(1.0, np.abs(L).max())
+            if variant != "routed":
+                Lm = mb.landmark_lse(Qt, Kh) * LOG2E
+                assert np.abs(r["lse_lm"][b, h] - Lm).max() <= 2e-3 * max(1.0, np.abs(Lm).max())
+            ref = mb.backward(Qh, Kh, Vh, dO[b, h], gh, gw, lh, lw, I, e, dtype=dtype, variant=variant)
+            for name, g, rf in zip(("dQ", "dK", "dV"), (r["dQ"][b, h], r["dK"][b, h], r["dV"][b, h]), ref):
+                _compare(f"{label} ({b},{h}) {name}", g, rf, dtype)
+
+
+def test_autograd_function_matches_the_entry_points():
+    """MitaFunction (torch.autograd) runs forward_train and backward."""
+    B, H, N, d = 1, 2, 512, 64
+    Q, K, V = synth.make(B, H, N, d, "clustered", 8, "bf16", 5)
+    dO = gh_.to_device(synth.make_grad(B, H, N, d, "bf16", 5), "bf16")
+    q, kk, v = (gh_.to_device(x, "bf16").requires_grad_() for x in (Q, K, V))
+    pool = (1, N, 1, 16)
+    O = mita.MitaFunction.apply(q, kk, v, pool, 32, 1)
+    O.backward(dO)
+    O2, sv = mita.forward_train(q.detach(), kk.detach(), v.detach(), pool, 32, 1)
+    g = mita.backward(q.detach(), kk.detach(), v.detach(), O2, dO, pool, 32, 1, sv)
+    torch.cuda.synchronize()
+    assert torch.equal(O.detach(), O2)
+    assert torch.equal(q.grad, g[0])
+    for a, b in ((kk.grad, g[1]), (v.grad, g[2])):  # fp32 atomics: last-bit differences
+        assert float((a.float() - b.float()).abs().max()) <= 1e-2 * float(b.float().abs().max())
+
+
+def _shift_invariance(dV, dO):
+    a = dV.double().sum(dim=2)
+    b = dO.double().sum(dim=2)
+    return float((a - b).abs().max() / b.abs().max())
+
+
+@pytest.mark.parametrize("variant", ["paper", "routed"])
+def test_backward_long_1m_properties(variant):
+    """The benchmark's N = 1M shape: sum_j dV_j = sum_n dO_n (every softmax
+    sums to one); routing-only: sum_j dK_j = 0 and sampled dQ rows, each from
+    the oracle's single-query softmax gradient."""
+    w = WORKLOADS["long_n1m"]
+    Q, K, V = synth.make_from_workload(w)
+    pool = (w.grid_h, w.grid_w, w.land_h, w.land_w)
+    k = w.k if variant == "paper" else w.k + w.m
+    gh_.say(f"[gpu] backward long_n1m {variant} k={k}")
+    q, kk, v = (gh_.to_device(x, w.dtype) for x in (Q, K, V))
+    dO = gh_.to_device(synth.make_grad(w.B, w.H, w.N, w.d, w.dtype, 77), w.dtype)
+    O, sv = mita.forward_train(q, kk, v, pool, k, w.s, variant=variant)
+    dQ, dK, dV = mita.backward(q, kk, v, O, dO, pool, k, w.s, sv, variant=variant)
+    torch.cuda.synchronize()
+    rel = _shift_invariance(dV.float(), dO.float())
+    gh_.say(f"[gpu]   sum dV - sum dO: {rel:.2e} of max |sum dO|")
+    assert rel <= 1e-2
+    if variant != "routed":
+        return
+    ks = dK.double().sum(dim=2).abs().max() / dK.double().abs().sum(dim=2).max()
+    gh_.say(f"[gpu]   |sum dK| / sum |dK|: {float(ks):.2e}")
+    assert float(ks) <= 1e-2
+    bh = (0, 1)
+    I = sv.topk[bh].cpu().numpy().astype(np.int64)
+    e = sv.route[bh].cpu().numpy().astype(np.int64)
+    Qh, Kh, Vh = (x[bh].astype(np.float64) for x in (Q, K, V))
+    g = gh_.to_host(dO[bh])
+    got = gh_.to_host(dQ[bh])
+    worst, scale = 0.0, 0.0
+    for n in np.sort(np.random.default_rng(9).choice(w.N, 256, replace=False)):
+        sel = np.concatenate([I[x] for x in e[n]])
+        z = Kh[sel] @ Qh[n] / math.sqrt(w.d)
+        P = np.exp(z - z.max())
+        P /= P.sum()
+        dP = Vh[sel] @ g[n]
+        dS = P * (dP - P @ dP)
+        ref = (dS @ Kh[sel]) / math.sqrt(w.d)
+        worst = max(worst, float(np.abs(got[n] - ref).max()))
+        scale = max(scale, float(np.abs(ref).max()))
+    gh_.say(f"[gpu]   sampled dQ rows: max {worst / scale:.2e} of max |ref|")
+    assert worst <= BTOL["bf16"]["max"] * scale
