@@ -373,6 +373,51 @@ def ablation(steps: int, warmup: int):
     return out
 
 
+def backward_flops(w, k: int | None = None) -> float:
+    """Matrix-core flops of one backward pass (2 flops per multiply-add):
+    joint softmax at the landmarks (S, dP, dq~, dv~ over m N pairs), routed
+    keys (S, dP, dk, dv over N s k pairs), shared-value keys (the same four
+    over N m pairs), shared-value landmarks (S, dP, dq~ over m N) and queries
+    (S, dP, dq over N (m + s k)): d N (28 m + 14 s k) per head."""
+    k = w.k if k is None else k
+    return 2.0 * w.B * w.H * w.d * w.N * (14 * w.m + 7 * w.s * k)
+
+
+def time_backward(w, steps: int, warmup: int, variant: str = "paper"):
+    """forward_train and backward of one workload, timed with torch events on
+    the launch stream (the library enqueues on torch's current stream)."""
+    import torch
+    from efficient_long_sequence_amd import mita, synth
+    _, (q, kk, v) = make_device_inputs(w)
+    pool = (w.grid_h, w.grid_w, w.land_h, w.land_w)
+    g = torch.from_numpy(synth.make_grad(w.B, w.H, w.N, w.d, w.dtype, w.seed)).cuda().to(q.dtype)
+    ws_f = torch.empty(mita.workspace_bytes(q.dtype, w.B, w.H, w.N, w.d, pool, w.k, w.s), dtype=torch.uint8,
+                       device="cuda")
+    ws_b = torch.empty(mita.backward_workspace_bytes(q.dtype, w.B, w.H, w.N, w.d, pool, w.k, w.s),
+                       dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        O, sv = mita.forward_train(q, kk, v, pool, w.k, w.s, variant=variant, workspace=ws_f)
+        mita.backward(q, kk, v, O, g, pool, w.k, w.s, sv, variant=variant, workspace=ws_b)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record()
+        O, sv = mita.forward_train(q, kk, v, pool, w.k, w.s, variant=variant, workspace=ws_f)
+        e[1].record()
+        mita.backward(q, kk, v, O, g, pool, w.k, w.s, sv, variant=variant, workspace=ws_b)
+        e[2].record()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    fwd = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    bwd = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    fl = backward_flops(w)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    return dict(workload=w.name, variant=variant, train_step_tokens_per_s=w.tokens * steps / dt,
+                ms_per_step=1e3 * dt / steps, forward_train_ms=fwd, backward_ms=bwd,
+                backward_tflops=fl / (bwd * 1e-3) * 1e-12, backward_frac_of_mfma_peak=fl / (bwd * 1e-3) * 1e-12 / peak)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -389,6 +434,8 @@ def main():
     ap.add_argument("--e2e", action="store_true",
                     help="instead: the three-layer, width-128 model with MiTA vs dense attention at 16K-1M")
     ap.add_argument("--e2e-max-n", type=int, default=1 << 20, help="largest sequence length of --e2e")
+    ap.add_argument("--backward", action="store_true",
+                    help="instead: training step (forward_train + backward) of --workload (all long ones unless --only)")
     ap.add_argument("--ablation", action="store_true",
                     help="instead: MiTA against the routing-only variant with matched entries per query")
     args = ap.parse_args()
@@ -404,6 +451,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(2)
+    if args.backward:
+        names = [args.workload] if args.only else LONG
+        pts = []
+        for name in names:
+            pts.append(time_backward(WORKLOADS[name], args.steps, args.warmup))
+            print(json.dumps(pts[-1]), file=sys.stderr, flush=True)
+            torch.cuda.empty_cache()
+        print(json.dumps(dict(metric="MiTA training step (forward_train + backward) tokens/s", unit="tokens/s",
+                              n_gpus=1, dtype="bf16", data="synthetic", points=pts)), flush=True)
+        return
     if args.ablation:
         print(json.dumps(dict(metric="MiTA vs routing-only forward tokens/s, entries per query matched",
                               unit="tokens/s", n_gpus=1, dtype="bf16", data="synthetic",

@@ -306,11 +306,19 @@ BPlan make_bplan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, i
   const size_t zoff = off;
   b.counts = (int*)take((size_t)s * Mr * 4);
   b.cursor = (int*)take((size_t)s * Mr * 4);
-  p.dKacc = (float*)take(Nr * d * 4);
-  p.dVacc = (float*)take(Nr * d * 4);
+  p.icnt = (int*)take(Nr * 4);
+  p.icur = (int*)take(Nr * 4);
   p.zero_begin = base ? base + zoff : nullptr;
   p.zero_bytes = off - zoff;
   p.Dn = (float*)take(Nr * 4);
+  p.ipos = (int*)take(Nr * 4);
+  p.bsum = (int*)take(((Nr + 4095) / 4096 + 1) * 4);
+  p.ilist = (int32_t*)take(Mr * k * 4);
+  p.G = (float*)take((size_t)s * Mr * k * 2 * d * 4);
+  p.Qg = take((size_t)s * Nr * d * p.esize);
+  p.dOg = take((size_t)s * Nr * d * p.esize);
+  p.Lg = (float*)take((size_t)s * Nr * 4);
+  p.Dg = (float*)take((size_t)s * Nr * 4);
   b.route = (int32_t*)take(Nr * s * 4);
   b.gpre = (int*)take((size_t)s * Mr * 4);
   b.perm = (int32_t*)take((size_t)s * Nr * 4);
@@ -385,6 +393,7 @@ mita_status mita_forward_train(const void* Q, const void* K, const void* V, void
 size_t mita_backward_workspace_bytes(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int m, int k,
                                      int s) {
   if (validate(nullptr, nullptr, nullptr, nullptr, dtype, B, H, N, d, pool, m, k, s, false) != MITA_OK) return 0;
+  if ((long long)B * H * m * k > 0x7FFFFFFFLL) return 0;
   return make_bplan(dtype, B, H, N, d, pool, m, k, s, nullptr).total_bytes;
 }
 
@@ -398,6 +407,8 @@ mita_status mita_backward(const void* Q, const void* K, const void* V, const voi
   if (((uintptr_t)dO | (uintptr_t)dQ | (uintptr_t)dK | (uintptr_t)dV) & 15u) return MITA_ERR_PARAM;
   if (!valid_variant((int)variant)) return MITA_ERR_PARAM;
   if ((st = check_saved(saved, (int)variant)) != MITA_OK) return st;
+  // positions in the keys' inverse lists are 32-bit
+  if ((long long)B * H * m * k > 0x7FFFFFFFLL) return MITA_ERR_UNSUPPORTED;
   if (!workspace) return MITA_ERR_NULL;
   if ((uintptr_t)workspace & 15u) return MITA_ERR_PARAM;
   BPlan p = make_bplan(dtype, B, H, N, d, pool, m, k, s, (char*)workspace);

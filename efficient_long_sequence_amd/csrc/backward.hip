@@ -24,8 +24,12 @@
 // layout cancels in every contraction.  The passes:
 //
 //   joint softmax, landmark rows over all queries    X q~, W v~,  Y q,  Z dO   -> dq~, dv~  (chunk partials)
-//   joint softmax, expert key rows over its queries  X k,  W v,   Y q,  Z dO   -> dk, dv    (atomic adds)
+//   joint softmax, expert key rows over its queries  X k,  W v,   Y q,  Z dO   -> dk, dv    (per expert row)
 //   shared values, key rows over all landmarks       X k,  W v,   Y q~, Z dv~  -> dk, dv    (+ the above, final)
+//
+// A key can sit in several experts; its routed parts are gathered by the
+// key's owner through the inverse of the expert lists (a counting sort), so
+// every output row has exactly one writer and no atomics touch HBM.
 //   shared values, landmark rows over all keys       X q~, W dv~, Y k,  Z v    -> dq~       (chunk partials)
 //   joint softmax, query rows over [q~; expert keys] X q,  W dO,  Y,    Z      -> dq        (+ pooling's adjoint)
 //
@@ -201,45 +205,6 @@ struct SrcRows {
   __device__ float cnat(int) const { return cn; }
 };
 
-// Entries = the rows idx[0 .. cnt) of Y and Z (queries of one expert).
-template <typename T, int D>
-struct SrcPerm {
-  const T* Y;
-  const T* Z;
-  const float* Lv;
-  const float* Dv;
-  const int32_t* idx;
-  int cnt;
-  float cs, cn;
-  __device__ auto ry(int st) const {
-    const T* b = Y;
-    const int32_t* ix = idx;
-    const int a = st * 32, e = cnt;
-    return [=](int r) -> const T* { const int x = a + r; return x < e ? b + (size_t)ix[x] * D : nullptr; };
-  }
-  __device__ auto rz(int st) const {
-    const T* b = Z;
-    const int32_t* ix = idx;
-    const int a = st * 32, e = cnt;
-    return [=](int r) -> const T* { const int x = a + r; return x < e ? b + (size_t)ix[x] * D : nullptr; };
-  }
-  __device__ auto re(int st) const {
-    const float* l = Lv;
-    const float* d = Dv;
-    const int32_t* ix = idx;
-    const int a = st * 32, e = cnt;
-    return [=](int r) -> float2 {
-      const int x = a + r;
-      if (x >= e) return make_float2(0.f, 0.f);
-      const int n = ix[x];
-      return make_float2(l[n], d[n]);
-    };
-  }
-  __device__ int nv(int st) const { return min(32, cnt - st * 32); }
-  __device__ float cscale(int) const { return cs; }
-  __device__ float cnat(int) const { return cn; }
-};
-
 // Entries of one query tile: the m0 shared entries (q~, v~; padded to whole
 // steps, so each step has one logit scale), then the expert's k keys.
 template <typename T, int D>
@@ -345,17 +310,21 @@ __global__ __launch_bounds__(NW * 64, 2) void k_bwd_lm(const T* __restrict__ Y, 
 }
 
 // Key rows.  ROUTED: the k keys of expert e (grid y = slot * m + e) over the
-// queries routed to it in that slot; adds dk, dv to the fp32 accumulators.
-// Otherwise: every key over the nent landmark rows of the shared-value
-// softmax (nent = 0 in the routing-only variant); writes dK, dV = the
-// accumulators plus this part, in the input dtype.
+// queries routed to it in that slot (read from the copies gathered in expert
+// order, so every step streams contiguous rows); writes the expert rows' dk, dv parts to
+// G [s, BH, m, k, 2d] (zeros for an expert no query chose).  Otherwise:
+// every key over the nent landmark rows of the shared-value softmax (nent = 0
+// in the routing-only variant), plus the G parts of every (slot, expert, row)
+// holding the key (its inverse list ilist[ipos[key] .. + icnt[key])); writes
+// dK, dV in the input dtype.  No atomics: every output row has one writer.
 template <typename T, int D, int NW, int IB, bool ROUTED>
 __global__ __launch_bounds__(NW * 64, 2) void k_bwd_keys(
     const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ Ysrc, const T* __restrict__ Zsrc,
     const float* __restrict__ Lv, const float* __restrict__ Dv, const int32_t* __restrict__ topk,
     const int32_t* __restrict__ perm, const int* __restrict__ gpre, const int* __restrict__ counts,
-    float* __restrict__ dKacc, float* __restrict__ dVacc, T* __restrict__ dK, T* __restrict__ dV, int N, int m,
-    int k, int nent, int BH, float cscale, float cnat) {
+    float* __restrict__ G, const int* __restrict__ icnt, const int* __restrict__ ipos,
+    const int32_t* __restrict__ ilist, T* __restrict__ dK, T* __restrict__ dV, int N, int m, int k, int s,
+    int nent, int BH, float cscale, float cnat) {
   constexpr int NT = NW * 64;
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, li = lane % 16, lg = lane / 16;
@@ -367,12 +336,10 @@ __global__ __launch_bounds__(NW * 64, 2) void k_bwd_keys(
     e = blockIdx.y % m;
     const size_t x = ((size_t)slot * BH + bh) * m + e;
     cnt = counts[x];
-    if (cnt == 0) return;  // uniform over the block
     start = gpre[x];
   } else {
     bh = blockIdx.y;
   }
-  const int nrows = ROUTED ? k : N;
   int jr[IB];
 #pragma unroll
   for (int b = 0; b < IB; ++b) {
@@ -380,7 +347,6 @@ __global__ __launch_bounds__(NW * 64, 2) void k_bwd_keys(
     if constexpr (ROUTED) jr[b] = r < k ? min(max(topk[((size_t)bh * m + e) * k + r], 0), N - 1) : -1;
     else jr[b] = r < N ? r : -1;
   }
-  (void)nrows;
   Frag<T> xf[IB][D / 32], wf[IB][D / 32];
   load_rows<T, D, IB>(xf, lg, [&](int b) -> const T* { return jr[b] >= 0 ? K + ((size_t)bh * N + jr[b]) * D : nullptr; });
   load_rows<T, D, IB>(wf, lg, [&](int b) -> const T* { return jr[b] >= 0 ? V + ((size_t)bh * N + jr[b]) * D : nullptr; });
@@ -389,39 +355,163 @@ __global__ __launch_bounds__(NW * 64, 2) void k_bwd_keys(
   zero_acc<IB, D>(ax);
   zero_acc<IB, D>(aw);
   if constexpr (ROUTED) {
-    const SrcPerm<T, D> src{Ysrc + (size_t)bh * N * D, Zsrc + (size_t)bh * N * D, Lv + (size_t)bh * N,
-                            Dv + (size_t)bh * N, perm + (size_t)slot * BH * N + start, cnt, cscale, cnat};
+    // the slot's queries gathered in expert order (q, dO, lse, dO . o)
+    const size_t so = (size_t)slot * BH * N;
+    const SrcRows<T, D> src{Ysrc + so * D, Zsrc + so * D, Lv + so, Dv + so, start, start + cnt, cscale, cnat};
     grad_stream<IB, false, true, true, NT, T, D>(smem, (cnt + 31) / 32, src, xf, wf, Lr, Dr, ax, aw, li, lg);
+#pragma unroll
+    for (int b = 0; b < IB; ++b) {
+      const int r = r0 + b * 16 + li;
+      if (r >= k) continue;
+      float* dst = G + ((((size_t)slot * BH + bh) * m + e) * k + r) * (2 * D);
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb) {
+        *(float4*)(dst + cb * 16 + 4 * lg) = make_float4(ax[b][cb][0], ax[b][cb][1], ax[b][cb][2], ax[b][cb][3]);
+        *(float4*)(dst + D + cb * 16 + 4 * lg) = make_float4(aw[b][cb][0], aw[b][cb][1], aw[b][cb][2], aw[b][cb][3]);
+      }
+    }
   } else {
     const SrcRows<T, D> src{Ysrc + (size_t)bh * m * D, Zsrc + (size_t)bh * m * D, Lv + (size_t)bh * m,
                             Dv + (size_t)bh * m, 0, nent, cscale, cnat};
     grad_stream<IB, false, true, true, NT, T, D>(smem, (nent + 31) / 32, src, xf, wf, Lr, Dr, ax, aw, li, lg);
-  }
+    const size_t mk = (size_t)m * k;
 #pragma unroll
-  for (int b = 0; b < IB; ++b) {
-    if (jr[b] < 0) continue;
-    const size_t o = ((size_t)bh * N + jr[b]) * D;
+    for (int b = 0; b < IB; ++b) {
+      if (jr[b] < 0) continue;
+      const size_t key = (size_t)bh * N + jr[b];
+      const int p0 = ipos[key], n = icnt[key];
+      for (int x = 0; x < n; ++x) {
+        const size_t er = (size_t)ilist[p0 + x];
+        for (int t = 0; t < s; ++t) {
+          const float* g = G + (((size_t)t * BH + bh) * mk + er) * (2 * D);
 #pragma unroll
-    for (int cb = 0; cb < D / 16; ++cb) {
-      const int c0 = cb * 16 + 4 * lg;
-      if constexpr (ROUTED) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          unsafeAtomicAdd(dKacc + o + c0 + r, ax[b][cb][r]);
-          unsafeAtomicAdd(dVacc + o + c0 + r, aw[b][cb][r]);
-        }
-      } else {
-        const float4 gk = *(const float4*)(dKacc + o + c0);
-        const float4 gv = *(const float4*)(dVacc + o + c0);
-        const float vk[4] = {gk.x, gk.y, gk.z, gk.w}, vv[4] = {gv.x, gv.y, gv.z, gv.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          dK[o + c0 + r] = from_f32<T>(vk[r] + ax[b][cb][r]);
-          dV[o + c0 + r] = from_f32<T>(vv[r] + aw[b][cb][r]);
+          for (int cb = 0; cb < D / 16; ++cb) {
+            const float4 a = *(const float4*)(g + cb * 16 + 4 * lg);
+            const float4 c = *(const float4*)(g + D + cb * 16 + 4 * lg);
+            ax[b][cb][0] += a.x; ax[b][cb][1] += a.y; ax[b][cb][2] += a.z; ax[b][cb][3] += a.w;
+            aw[b][cb][0] += c.x; aw[b][cb][1] += c.y; aw[b][cb][2] += c.z; aw[b][cb][3] += c.w;
+          }
         }
       }
+      const size_t o = key * D;
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          dK[o + cb * 16 + 4 * lg + r] = from_f32<T>(ax[b][cb][r]);
+          dV[o + cb * 16 + 4 * lg + r] = from_f32<T>(aw[b][cb][r]);
+        }
     }
   }
+}
+
+// Copies of q, dO, lse and dO . o in each slot's expert order: position
+// t * BH * N + x holds query perm_t[x] of head x / N (each head fills N
+// consecutive positions of a slot).  CPR lanes per row.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_bwd_gather(const T* __restrict__ Q, const T* __restrict__ dO,
+                                                    const float* __restrict__ lse, const float* __restrict__ Dn,
+                                                    const int32_t* __restrict__ perm, T* __restrict__ Qg,
+                                                    T* __restrict__ dOg, float* __restrict__ Lg,
+                                                    float* __restrict__ Dg, int N, long long BHN, long long rows) {
+  constexpr int EPC = 16 / (int)sizeof(T), CPR = D / EPC;
+  const long long g = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long pos = g / CPR;  // over s * BH * N
+  const int c = (int)(g % CPR);
+  if (pos >= rows) return;
+  const long long x = pos % BHN;
+  const long long src = (x / N) * N + min(max(perm[pos], 0), N - 1);
+  *(uint4*)(Qg + pos * D + c * EPC) = *(const uint4*)(Q + src * D + c * EPC);
+  *(uint4*)(dOg + pos * D + c * EPC) = *(const uint4*)(dO + src * D + c * EPC);
+  if (c == 0) {
+    Lg[pos] = lse[src];
+    Dg[pos] = Dn[src];
+  }
+}
+
+// Inverse of the experts: for every key, the (expert, row) slots holding it,
+// by a counting sort (count, exclusive prefix over all keys, fill).
+__global__ __launch_bounds__(256) void k_bwd_inv_count(const int32_t* __restrict__ topk, int* __restrict__ icnt,
+                                                       int N, long long mk, long long total) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const long long bh = i / mk;
+  const int j = min(max(topk[i], 0), N - 1);
+  atomicAdd(icnt + bh * N + j, 1);
+}
+
+__global__ __launch_bounds__(256) void k_bwd_inv_fill(const int32_t* __restrict__ topk, const int* __restrict__ ipos,
+                                                      int* __restrict__ icur, int32_t* __restrict__ ilist, int N,
+                                                      long long mk, long long total) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const long long bh = i / mk;
+  const int j = min(max(topk[i], 0), N - 1);
+  const long long key = bh * N + j;
+  ilist[ipos[key] + atomicAdd(icur + key, 1)] = (int32_t)(i - bh * mk);
+}
+
+// Exclusive prefix sum of n ints in three passes: per-block scans of
+// SCAN_PER_BLOCK elements with block totals, a one-workgroup scan of the
+// totals, and the block offsets added.
+constexpr int SCAN_EPT = 16;
+constexpr int SCAN_PER_BLOCK = 256 * SCAN_EPT;
+
+__device__ __forceinline__ int block_exclusive_scan256(int v, int* sh, int& total) {
+  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  int wbase = 0;
+  for (int w = 0; w < wave; ++w) wbase += sh[w];
+  total = sh[0] + sh[1] + sh[2] + sh[3];
+  __syncthreads();
+  return wbase + x - v;
+}
+
+__global__ __launch_bounds__(256) void k_scan_local(const int* __restrict__ in, int* __restrict__ out,
+                                                    int* __restrict__ bsum, long long n) {
+  __shared__ int sh[4];
+  const long long base = (long long)blockIdx.x * SCAN_PER_BLOCK + (long long)threadIdx.x * SCAN_EPT;
+  int v[SCAN_EPT], sum = 0;
+#pragma unroll
+  for (int u = 0; u < SCAN_EPT; ++u) {
+    v[u] = base + u < n ? in[base + u] : 0;
+    sum += v[u];
+  }
+  int total;
+  int run = block_exclusive_scan256(sum, sh, total);
+#pragma unroll
+  for (int u = 0; u < SCAN_EPT; ++u) {
+    if (base + u < n) out[base + u] = run;
+    run += v[u];
+  }
+  if (threadIdx.x == 0) bsum[blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(256) void k_scan_top(int* __restrict__ bsum, int nb) {
+  __shared__ int sh[4];
+  int carry = 0;
+  for (int c0 = 0; c0 < nb; c0 += 256) {
+    const int i = c0 + threadIdx.x;
+    const int v = i < nb ? bsum[i] : 0;
+    int total;
+    const int ex = block_exclusive_scan256(v, sh, total);
+    if (i < nb) bsum[i] = carry + ex;
+    carry += total;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_scan_add(int* __restrict__ out, const int* __restrict__ bsum, long long n) {
+  const long long base = (long long)blockIdx.x * SCAN_PER_BLOCK;
+  const int add = bsum[blockIdx.x];
+  for (int u = threadIdx.x; u < SCAN_PER_BLOCK; u += 256)
+    if (base + u < n) out[base + u] += add;
 }
 
 // Query rows of one work item (expert e, a tile of the queries routed to it
@@ -680,14 +770,29 @@ static void launch_backward_t(const BPlan& p) {
   }
   launch_bucket(p.bk);
 
-  // routed keys (atomic adds into the fp32 accumulators)
+  // routed keys: per-(slot, expert, row) parts, and the inverse of the experts
   {
+    constexpr int CPR = D * (int)sizeof(T) / 16;
+    const long long BHN = (long long)BH * N, rows = (long long)s * BHN;
+    hipLaunchKernelGGL((k_bwd_gather<T, D>), dim3((unsigned)((rows * CPR + 255) / 256)), dim3(256), 0, st,
+                       (const T*)p.Q, (const T*)p.dO, p.lse, (const float*)p.Dn, (const int32_t*)p.bk.perm, (T*)p.Qg,
+                       (T*)p.dOg, p.Lg, p.Dg, N, BHN, rows);
     auto fn = &k_bwd_keys<T, D, NW, IB, true>;
     allow_lds(fn, lds);
     dim3 grid((unsigned)((k + R - 1) / R), (unsigned)(s * m), (unsigned)BH);
-    hipLaunchKernelGGL(fn, grid, dim3(NW * 64), lds, st, (const T*)p.K, (const T*)p.V, (const T*)p.Q,
-                       (const T*)p.dO, p.lse, p.Dn, p.topk, p.bk.perm, p.bk.gpre, p.bk.counts, p.dKacc, p.dVacc,
-                       (T*)nullptr, (T*)nullptr, N, m, k, 0, BH, p.cscale, p.cnat);
+    hipLaunchKernelGGL(fn, grid, dim3(NW * 64), lds, st, (const T*)p.K, (const T*)p.V, (const T*)p.Qg,
+                       (const T*)p.dOg, p.Lg, p.Dg, p.topk, p.bk.perm, p.bk.gpre, p.bk.counts, p.G,
+                       (const int*)nullptr, (const int*)nullptr, (const int32_t*)nullptr, (T*)nullptr, (T*)nullptr,
+                       N, m, k, s, 0, BH, p.cscale, p.cnat);
+    const long long mk = (long long)m * k, total = (long long)BH * mk, keys = (long long)BH * N;
+    const unsigned gb = (unsigned)((total + 255) / 256);
+    hipLaunchKernelGGL(k_bwd_inv_count, dim3(gb), dim3(256), 0, st, p.topk, p.icnt, N, mk, total);
+    const int nb = (int)((keys + SCAN_PER_BLOCK - 1) / SCAN_PER_BLOCK);
+    hipLaunchKernelGGL(k_scan_local, dim3((unsigned)nb), dim3(256), 0, st, (const int*)p.icnt, p.ipos, p.bsum, keys);
+    hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(256), 0, st, p.bsum, nb);
+    hipLaunchKernelGGL(k_scan_add, dim3((unsigned)nb), dim3(256), 0, st, p.ipos, (const int*)p.bsum, keys);
+    hipLaunchKernelGGL(k_bwd_inv_fill, dim3(gb), dim3(256), 0, st, p.topk, (const int*)p.ipos, p.icur, p.ilist, N,
+                       mk, total);
   }
   if (p.shared) {
     auto fn = &k_bwd_lm<T, D, NW, IB, true>;
@@ -698,14 +803,18 @@ static void launch_backward_t(const BPlan& p) {
     hipLaunchKernelGGL((k_bwd_red1<T, D>), dim3((unsigned)(BH * m)), dim3(64), 0, st, p.part1, p.vt32,
                        p.dqt, p.dvt, (T*)p.dvtT, p.delta, m, p.C1);
   }
-  // shared-value softmax for the keys, added to the routed part: final dK, dV
+  // shared-value softmax for the keys plus their routed parts: final dK, dV
+  // (one 16-row block per wave: with two, the gather of the routed parts
+  // leaves too few registers)
   {
-    auto fn = &k_bwd_keys<T, D, NW, IB, false>;
+    constexpr int IB3 = 1, R3 = NW * 16 * IB3;
+    auto fn = &k_bwd_keys<T, D, NW, IB3, false>;
     allow_lds(fn, lds);
-    dim3 grid((unsigned)((N + R - 1) / R), (unsigned)BH);
+    dim3 grid((unsigned)((N + R3 - 1) / R3), (unsigned)BH);
     hipLaunchKernelGGL(fn, grid, dim3(NW * 64), lds, st, (const T*)p.K, (const T*)p.V, (const T*)p.qt,
-                       (const T*)p.dvtT, p.lse_lm, p.delta, p.topk, p.bk.perm, p.bk.gpre, p.bk.counts, p.dKacc,
-                       p.dVacc, (T*)p.dK, (T*)p.dV, N, m, k, p.shared ? m : 0, BH, p.cscale, p.cnat);
+                       (const T*)p.dvtT, p.lse_lm, p.delta, p.topk, p.bk.perm, p.bk.gpre, p.bk.counts, p.G,
+                       (const int*)p.icnt, (const int*)p.ipos, (const int32_t*)p.ilist, (T*)p.dK, (T*)p.dV, N, m,
+                       k, s, p.shared ? m : 0, BH, p.cscale, p.cnat);
   }
   if (p.shared) {
     auto fn = &k_bwd_lm<T, D, NW, IB, false>;

@@ -132,8 +132,16 @@ struct BPlan {
 
   // workspace
   float* Dn;      // [BH, N] dO . O per query
-  float* dKacc;   // [BH, N, d] routed key gradients (zeroed each call)
-  float* dVacc;   // [BH, N, d]
+  float* G;       // [s, BH, m, k, 2d] routed dk, dv per (slot, expert, row)
+  void* Qg;       // [s, BH * N, d] q in each slot's expert order
+  void* dOg;      // [s, BH * N, d] dO likewise
+  float* Lg;      // [s, BH * N] lse likewise
+  float* Dg;      // [s, BH * N] dO . o likewise
+  int* icnt;      // [BH * N] expert rows holding each key (zeroed each call)
+  int* icur;      // [BH * N] fill cursors (zeroed each call)
+  int* ipos;      // [BH * N] exclusive prefix of icnt
+  int* bsum;      // per-block totals of the prefix
+  int32_t* ilist; // [BH * m * k] (expert * k + row) of each key, grouped by key
   float* part1;   // [BH, C1, m, 2d] per-chunk dq~ and dv~ of the joint softmax
   float* part4;   // [BH, C4, m, d] per-chunk dq~ of the shared-value softmax
   float* dqt;     // [BH, m, d] dq~

@@ -202,7 +202,9 @@ mita_status mita_forward_train(const void* Q, const void* K, const void* V, void
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace mita_backward needs (0 if the arguments are
- * invalid).  Host-only; no HIP call. */
+ * invalid).  Host-only; no HIP call.  It holds, besides O(B*H*N) index and
+ * scalar arrays, the routed key parts (s*B*H*m*k*2d fp32) and the
+ * landmark-row partials of the two chunked passes. */
 size_t mita_backward_workspace_bytes(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool,
                                      int m, int k, int s);
 
@@ -219,9 +221,10 @@ size_t mita_backward_workspace_bytes(mita_dtype dtype, int B, int H, int N, int 
  *               aligned, caller-owned, need not be initialised
  * All pointers 16-byte aligned.  Same shape limits and errors as
  * mita_forward (MITA_ERR_NULL also for a NULL dO, dQ, dK, dV or saved
- * member); nothing is launched on a validation error.  Key gradients of the
- * routed experts are summed with fp32 atomic adds, so dK and dV may differ
- * in the last bits from call to call; dQ is deterministic. */
+ * member), and MITA_ERR_UNSUPPORTED when B*H*m*k > 2^31 - 1; nothing is
+ * launched on a validation error.  A key held by several experts receives
+ * their parts in an order that may change from call to call, so dK and dV
+ * may differ in the last bits between calls; dQ is deterministic. */
 mita_status mita_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                           void* dQ, void* dK, void* dV, mita_dtype dtype, int B, int H, int N, int d,
                           mita_pool pool, int m, int k, int s, mita_variant variant,

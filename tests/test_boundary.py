@@ -159,6 +159,8 @@ def _bwd(variant=0, sv=None, **kw):
     (dict(variant=9), 3), (dict(sv=_saved(topk=0)), 1), (dict(sv=_saved(route=0)), 1),
     (dict(d=48), 4), (dict(s=9, m=64), 4), (dict(B=64, H=512, N=1 << 16, pool=(1, 1 << 16, 1, 64)), 4),
     ({}, 5), (dict(variant=2, sv=_saved(vtilde=0, lse_landmark=0)), 5),
+    # a valid forward whose backward inverse lists would need 64-bit positions
+    (dict(B=128, H=1, N=8192, pool=(1, 8192, 1, 4096), m=4096, k=8192), 4),
 ])
 def test_backward_rejects_invalid_arguments(kw, code):
     assert _bwd(**kw) == code
@@ -168,9 +170,11 @@ def test_backward_workspace_bytes():
     L = mita.lib()
     P = mita.Pool(1, 1 << 20, 1, 512)
     big = L.mita_backward_workspace_bytes(mita.BF16, 1, 2, 1 << 20, 64, P, 512, 512, 1)
-    # the fp32 key-gradient accumulators alone take 2 * B*H*N*d*4 bytes
-    assert 2 * 2 * (1 << 20) * 64 * 4 < big < 4 << 30
+    # the routed key parts alone take s * B*H*m*k * 2d * 4 bytes
+    assert 2 * 512 * 512 * 128 * 4 < big < 4 << 30
     assert L.mita_backward_workspace_bytes(mita.BF16, 1, 2, 1 << 20, 64, P, 511, 512, 1) == 0
+    assert L.mita_backward_workspace_bytes(mita.BF16, 128, 1, 8192, 64, mita.Pool(1, 8192, 1, 4096), 4096, 8192,
+                                           1) == 0
     s2 = L.mita_backward_workspace_bytes(mita.BF16, 1, 2, 4096, 64, mita.Pool(1, 4096, 1, 64), 64, 64, 2)
     s1 = L.mita_backward_workspace_bytes(mita.BF16, 1, 2, 4096, 64, mita.Pool(1, 4096, 1, 64), 64, 64, 1)
     assert s2 > s1
