@@ -314,7 +314,15 @@ BPlan make_bplan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, i
   p.ipos = (int*)take(Nr * 4);
   p.bsum = (int*)take(((Nr + 4095) / 4096 + 1) * 4);
   p.ilist = (int32_t*)take(Mr * k * 4);
-  p.G = (float*)take((size_t)s * Mr * k * 2 * d * 4);
+  // routed-key pass: items of at most CH queries (large experts split)
+  p.CH = 2048;
+  p.UB2 = (int)((long long)p.BH * (ceil_div(N, p.CH) + m));
+  p.wl2 = (WorkItem*)take((size_t)s * p.UB2 * sizeof(WorkItem));
+  p.wl2_count = (int*)take(MAX_S * 4);
+  p.efirst = (int*)take((size_t)s * Mr * 4);
+  p.epart = (int*)take((size_t)s * Mr * 4);
+  p.G = (float*)take((size_t)s * p.UB2 * k * 2 * d * 4);
+  p.Gs = (float*)take(Mr * k * 2 * d * 4);
   p.Qg = take((size_t)s * Nr * d * p.esize);
   p.dOg = take((size_t)s * Nr * d * p.esize);
   p.Lg = (float*)take((size_t)s * Nr * 4);

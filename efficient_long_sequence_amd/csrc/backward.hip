@@ -206,7 +206,8 @@ struct SrcRows {
 };
 
 // Entries of one query tile: the m0 shared entries (q~, v~; padded to whole
-// steps, so each step has one logit scale), then the expert's k keys.
+// steps, so each step has one logit scale), then the expert's k keys (Ie:
+// their indices, staged in LDS and already clamped into [0, N)).
 template <typename T, int D>
 struct SrcJoint {
   const T* qt;
@@ -220,15 +221,14 @@ struct SrcJoint {
   __device__ auto rz(int st) const { return rows(st, vt, V); }
   __device__ auto rows(int st, const T* shared, const T* raw) const {
     const int32_t* I = Ie;
-    const int ns_ = ns, m0_ = m0, k_ = k, n1 = N - 1;
+    const int ns_ = ns, m0_ = m0, k_ = k;
     return [=](int r) -> const T* {
       if (st < ns_) {
         const int x = st * 32 + r;
         return x < m0_ ? shared + (size_t)x * D : nullptr;
       }
       const int x = (st - ns_) * 32 + r;
-      // indices come from the forward; the clamp only keeps other contents in bounds
-      return x < k_ ? raw + (size_t)min(max(I[x], 0), n1) * D : nullptr;
+      return x < k_ ? raw + (size_t)I[x] * D : nullptr;
     };
   }
   __device__ auto re(int) const { return [](int) -> float2 { return make_float2(0.f, 0.f); }; }
@@ -309,37 +309,44 @@ __global__ __launch_bounds__(NW * 64, 2) void k_bwd_lm(const T* __restrict__ Y, 
   }
 }
 
-// Key rows.  ROUTED: the k keys of expert e (grid y = slot * m + e) over the
-// queries routed to it in that slot (read from the copies gathered in expert
-// order, so every step streams contiguous rows); writes the expert rows' dk, dv parts to
-// G [s, BH, m, k, 2d] (zeros for an expert no query chose).  Otherwise:
+// Key rows.  ROUTED: the k keys of expert e over one item (up to CH of the
+// queries routed to e in a slot; a large expert is split into several items
+// so no workgroup carries its whole list), read from the copies gathered in
+// expert order so every step streams contiguous rows; writes the item's
+// dk, dv parts of the expert rows to G [s, UB2, k, 2d].  Otherwise:
 // every key over the nent landmark rows of the shared-value softmax (nent = 0
-// in the routing-only variant), plus the G parts of every (slot, expert, row)
-// holding the key (its inverse list ilist[ipos[key] .. + icnt[key])); writes
-// dK, dV in the input dtype.  No atomics: every output row has one writer.
+// in the routing-only variant), plus the sum of its routed parts (G here is
+// the compact per-key sum k_bwd_route_sum wrote at ipos[key], present when
+// icnt[key] > 0); writes dK, dV in the input dtype.  No atomics: every output
+// row has one writer.
 template <typename T, int D, int NW, int IB, bool ROUTED>
 __global__ __launch_bounds__(NW * 64, 2) void k_bwd_keys(
     const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ Ysrc, const T* __restrict__ Zsrc,
     const float* __restrict__ Lv, const float* __restrict__ Dv, const int32_t* __restrict__ topk,
-    const int32_t* __restrict__ perm, const int* __restrict__ gpre, const int* __restrict__ counts,
-    float* __restrict__ G, const int* __restrict__ icnt, const int* __restrict__ ipos,
-    const int32_t* __restrict__ ilist, T* __restrict__ dK, T* __restrict__ dV, int N, int m, int k, int s,
-    int nent, int BH, float cscale, float cnat) {
+    const WorkItem* __restrict__ wl2, const int* __restrict__ wl2_count, const int* __restrict__ counts,
+    const int* __restrict__ efirst, const int* __restrict__ epart, float* __restrict__ G,
+    const int* __restrict__ icnt, const int* __restrict__ ipos, const int32_t* __restrict__ ilist,
+    T* __restrict__ dK, T* __restrict__ dV, int N, int m, int k, int s, int nent, int BH, int CH, int UB2,
+    float cscale, float cnat) {
   constexpr int NT = NW * 64;
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, li = lane % 16, lg = lane / 16;
-  const int r0 = blockIdx.x * (NW * 16 * IB) + wave * 16 * IB;
-  int bh, cnt = 0, start = 0, slot = 0, e = 0;
+  int bh, cnt = 0, start = 0, slot = 0, e = 0, rt;
   if constexpr (ROUTED) {
-    bh = blockIdx.z;
-    slot = blockIdx.y / m;
-    e = blockIdx.y % m;
-    const size_t x = ((size_t)slot * BH + bh) * m + e;
-    cnt = counts[x];
-    start = gpre[x];
+    // grid x: (slot, item) of the slot's list, y: 16*IB*NW-row tiles of the expert
+    slot = blockIdx.x / UB2;
+    if ((int)(blockIdx.x % UB2) >= wl2_count[slot]) return;  // uniform over the block
+    const WorkItem it = wl2[blockIdx.x];
+    bh = it.be / m;
+    e = it.be % m;
+    start = it.start;
+    cnt = it.count;
+    rt = blockIdx.y;
   } else {
     bh = blockIdx.y;
+    rt = blockIdx.x;
   }
+  const int r0 = rt * (NW * 16 * IB) + wave * 16 * IB;
   int jr[IB];
 #pragma unroll
   for (int b = 0; b < IB; ++b) {
@@ -363,7 +370,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_bwd_keys(
     for (int b = 0; b < IB; ++b) {
       const int r = r0 + b * 16 + li;
       if (r >= k) continue;
-      float* dst = G + ((((size_t)slot * BH + bh) * m + e) * k + r) * (2 * D);
+      float* dst = G + ((size_t)blockIdx.x * k + r) * (2 * D);
 #pragma unroll
       for (int cb = 0; cb < D / 16; ++cb) {
         *(float4*)(dst + cb * 16 + 4 * lg) = make_float4(ax[b][cb][0], ax[b][cb][1], ax[b][cb][2], ax[b][cb][3]);
@@ -374,23 +381,18 @@ __global__ __launch_bounds__(NW * 64, 2) void k_bwd_keys(
     const SrcRows<T, D> src{Ysrc + (size_t)bh * m * D, Zsrc + (size_t)bh * m * D, Lv + (size_t)bh * m,
                             Dv + (size_t)bh * m, 0, nent, cscale, cnat};
     grad_stream<IB, false, true, true, NT, T, D>(smem, (nent + 31) / 32, src, xf, wf, Lr, Dr, ax, aw, li, lg);
-    const size_t mk = (size_t)m * k;
 #pragma unroll
     for (int b = 0; b < IB; ++b) {
       if (jr[b] < 0) continue;
       const size_t key = (size_t)bh * N + jr[b];
-      const int p0 = ipos[key], n = icnt[key];
-      for (int x = 0; x < n; ++x) {
-        const size_t er = (size_t)ilist[p0 + x];
-        for (int t = 0; t < s; ++t) {
-          const float* g = G + (((size_t)t * BH + bh) * mk + er) * (2 * D);
+      if (icnt[key] > 0) {  // the key's routed parts, summed by k_bwd_route_sum
+        const float* g = G + (size_t)ipos[key] * (2 * D);
 #pragma unroll
-          for (int cb = 0; cb < D / 16; ++cb) {
-            const float4 a = *(const float4*)(g + cb * 16 + 4 * lg);
-            const float4 c = *(const float4*)(g + D + cb * 16 + 4 * lg);
-            ax[b][cb][0] += a.x; ax[b][cb][1] += a.y; ax[b][cb][2] += a.z; ax[b][cb][3] += a.w;
-            aw[b][cb][0] += c.x; aw[b][cb][1] += c.y; aw[b][cb][2] += c.z; aw[b][cb][3] += c.w;
-          }
+        for (int cb = 0; cb < D / 16; ++cb) {
+          const float4 a = *(const float4*)(g + cb * 16 + 4 * lg);
+          const float4 c = *(const float4*)(g + D + cb * 16 + 4 * lg);
+          ax[b][cb][0] += a.x; ax[b][cb][1] += a.y; ax[b][cb][2] += a.z; ax[b][cb][3] += a.w;
+          aw[b][cb][0] += c.x; aw[b][cb][1] += c.y; aw[b][cb][2] += c.z; aw[b][cb][3] += c.w;
         }
       }
       const size_t o = key * D;
@@ -427,6 +429,42 @@ __global__ __launch_bounds__(256) void k_bwd_gather(const T* __restrict__ Q, con
     Lg[pos] = lse[src];
     Dg[pos] = Dn[src];
   }
+}
+
+// Sum of every routed part of a key (over its expert rows, slots and items)
+// into Gs[ipos[key]] (a compact row per key that some expert holds).  Each
+// key's 2d values are spread over 2d/4 lanes with float4 loads.
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_route_sum(const float* __restrict__ G, const int* __restrict__ counts,
+                                                       const int* __restrict__ efirst, const int* __restrict__ epart,
+                                                       const int* __restrict__ icnt, const int* __restrict__ ipos,
+                                                       const int32_t* __restrict__ ilist, float* __restrict__ Gs,
+                                                       int N, int m, int k, int s, int BH, int CH, int UB2) {
+  constexpr int LPK = 2 * D / 4;  // lanes per key
+  const long long g = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long key = g / LPK;
+  const int c = (int)(g % LPK) * 4;
+  if (key >= (long long)BH * N) return;
+  const int n = icnt[key];
+  if (n == 0) return;
+  const int bh = (int)(key / N);
+  const int p0 = ipos[key];
+  const size_t E = (size_t)BH * m;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int x = 0; x < n; ++x) {
+    const int er = ilist[p0 + x];
+    const int ee = er / k, r = er % k;
+    for (int t = 0; t < s; ++t) {
+      const size_t xe = (size_t)t * E + (size_t)bh * m + ee;
+      const int f0 = efirst[xe], nf = counts[xe] / CH, pi = epart[xe];
+      for (int q = f0; q < f0 + nf + (pi >= 0 ? 1 : 0); ++q) {
+        const int item = q < f0 + nf ? q : pi;
+        const float4 v = *(const float4*)(G + (((size_t)t * UB2 + item) * k + r) * (2 * D) + c);
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      }
+    }
+  }
+  *(float4*)(Gs + (size_t)p0 * (2 * D) + c) = acc;
 }
 
 // Inverse of the experts: for every key, the (expert, row) slots holding it,
@@ -552,8 +590,14 @@ __global__ __launch_bounds__(NW * 64, 2) void k_bwd_q(
   zero_acc<IB, D>(ax);
   const int m0 = SLOT0 ? m_shared : 0;
   const int ns = (m0 + 31) / 32;
+  // the expert's key indices (from the forward; the clamp only keeps other
+  // contents in bounds), staged after the two step buffers
+  int32_t* s_idx = (int32_t*)(smem + 2 * GradLds<T, D>::STEP_BYTES);
+  const int32_t* Ie = topk + (size_t)it.be * k;
+  for (int x = tid; x < k; x += NT) s_idx[x] = min(max(Ie[x], 0), N - 1);
+  __syncthreads();
   const SrcJoint<T, D> src{qt + (size_t)bh * m * D, vt + (size_t)bh * m * D, K + row0 * D, V + row0 * D,
-                           topk + (size_t)it.be * k, m0, ns, k, N, cscale, cnat, cscale_sh, cnat_sh};
+                           s_idx, m0, ns, k, N, cscale, cnat, cscale_sh, cnat_sh};
   grad_stream<IB, true, false, false, NT, T, D>(smem, ns + (k + 31) / 32, src, xf, wf, Lr, Dr, ax, aw, li, lg);
 
 #pragma unroll
@@ -777,13 +821,14 @@ static void launch_backward_t(const BPlan& p) {
     hipLaunchKernelGGL((k_bwd_gather<T, D>), dim3((unsigned)((rows * CPR + 255) / 256)), dim3(256), 0, st,
                        (const T*)p.Q, (const T*)p.dO, p.lse, (const float*)p.Dn, (const int32_t*)p.bk.perm, (T*)p.Qg,
                        (T*)p.dOg, p.Lg, p.Dg, N, BHN, rows);
+    launch_items(p.bk, p.CH, p.UB2, p.wl2, p.wl2_count, p.efirst, p.epart);
     auto fn = &k_bwd_keys<T, D, NW, IB, true>;
     allow_lds(fn, lds);
-    dim3 grid((unsigned)((k + R - 1) / R), (unsigned)(s * m), (unsigned)BH);
+    dim3 grid((unsigned)(s * p.UB2), (unsigned)((k + R - 1) / R));
     hipLaunchKernelGGL(fn, grid, dim3(NW * 64), lds, st, (const T*)p.K, (const T*)p.V, (const T*)p.Qg,
-                       (const T*)p.dOg, p.Lg, p.Dg, p.topk, p.bk.perm, p.bk.gpre, p.bk.counts, p.G,
+                       (const T*)p.dOg, p.Lg, p.Dg, p.topk, p.wl2, p.wl2_count, p.bk.counts, p.efirst, p.epart, p.G,
                        (const int*)nullptr, (const int*)nullptr, (const int32_t*)nullptr, (T*)nullptr, (T*)nullptr,
-                       N, m, k, s, 0, BH, p.cscale, p.cnat);
+                       N, m, k, s, 0, BH, p.CH, p.UB2, p.cscale, p.cnat);
     const long long mk = (long long)m * k, total = (long long)BH * mk, keys = (long long)BH * N;
     const unsigned gb = (unsigned)((total + 255) / 256);
     hipLaunchKernelGGL(k_bwd_inv_count, dim3(gb), dim3(256), 0, st, p.topk, p.icnt, N, mk, total);
@@ -803,18 +848,23 @@ static void launch_backward_t(const BPlan& p) {
     hipLaunchKernelGGL((k_bwd_red1<T, D>), dim3((unsigned)(BH * m)), dim3(64), 0, st, p.part1, p.vt32,
                        p.dqt, p.dvt, (T*)p.dvtT, p.delta, m, p.C1);
   }
+  {
+    const long long thr = (long long)BH * N * (2 * D / 4);
+    hipLaunchKernelGGL((k_bwd_route_sum<D>), dim3((unsigned)((thr + 255) / 256)), dim3(256), 0, st, (const float*)p.G,
+                       (const int*)p.bk.counts, (const int*)p.efirst, (const int*)p.epart, (const int*)p.icnt,
+                       (const int*)p.ipos, (const int32_t*)p.ilist, p.Gs, N, m, k, s, BH, p.CH, p.UB2);
+  }
   // shared-value softmax for the keys plus their routed parts: final dK, dV
-  // (one 16-row block per wave: with two, the gather of the routed parts
-  // leaves too few registers)
+  // (one 16-row block per wave: with two this pass spills registers)
   {
     constexpr int IB3 = 1, R3 = NW * 16 * IB3;
     auto fn = &k_bwd_keys<T, D, NW, IB3, false>;
     allow_lds(fn, lds);
     dim3 grid((unsigned)((N + R3 - 1) / R3), (unsigned)BH);
     hipLaunchKernelGGL(fn, grid, dim3(NW * 64), lds, st, (const T*)p.K, (const T*)p.V, (const T*)p.qt,
-                       (const T*)p.dvtT, p.lse_lm, p.delta, p.topk, p.bk.perm, p.bk.gpre, p.bk.counts, p.G,
-                       (const int*)p.icnt, (const int*)p.ipos, (const int32_t*)p.ilist, (T*)p.dK, (T*)p.dV, N, m,
-                       k, s, p.shared ? m : 0, BH, p.cscale, p.cnat);
+                       (const T*)p.dvtT, p.lse_lm, p.delta, p.topk, p.wl2, p.wl2_count, p.bk.counts, p.efirst,
+                       p.epart, p.Gs, (const int*)p.icnt, (const int*)p.ipos, (const int32_t*)p.ilist, (T*)p.dK,
+                       (T*)p.dV, N, m, k, s, p.shared ? m : 0, BH, p.CH, p.UB2, p.cscale, p.cnat);
   }
   if (p.shared) {
     auto fn = &k_bwd_lm<T, D, NW, IB, false>;
@@ -828,13 +878,14 @@ static void launch_backward_t(const BPlan& p) {
   {
     auto f1 = &k_bwd_q<T, D, NW, IB, false>;
     auto f0 = &k_bwd_q<T, D, NW, IB, true>;
-    allow_lds(f1, lds);
-    allow_lds(f0, lds);
+    const size_t lq = lds + (size_t)k * 4;
+    allow_lds(f1, lq);
+    allow_lds(f0, lq);
     for (int t = s - 1; t >= 0; --t) {
       const int32_t* perm = p.bk.perm + (size_t)t * BH * N;
       const WorkItem* wl = p.bk.wl + (size_t)t * p.bk.UB;
       const int* wlc = p.bk.wl_count + t;
-      hipLaunchKernelGGL(t > 0 ? f1 : f0, dim3((unsigned)p.bk.UB), dim3(NW * 64), lds, st, (const T*)p.Q,
+      hipLaunchKernelGGL(t > 0 ? f1 : f0, dim3((unsigned)p.bk.UB), dim3(NW * 64), lq, st, (const T*)p.Q,
                          (const T*)p.K, (const T*)p.V, (const T*)p.dO, (const T*)p.qt, (const T*)p.vt, p.lse, p.Dn,
                          p.topk, perm, wl, wlc, p.dqt, p.qpart, (T*)p.dQ, N, m, k, s, t, BH, p.shared ? m : 0,
                          p.gh, p.gw, p.lh, p.lw, p.cscale, p.cscale_sh, p.cnat, p.cnat_sh);

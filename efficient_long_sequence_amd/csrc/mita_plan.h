@@ -110,6 +110,9 @@ void launch_score(const Plan& p);
 void launch_final(const Plan& p);
 void launch_route(const Plan& p);
 void launch_bucket(const Plan& p);
+// another work list over the same counts with items of at most T queries,
+// recording each expert's full items (efirst) and partial item (epart)
+void launch_items(const Plan& p, int T, int UB, WorkItem* wl, int* wl_count, int* efirst, int* epart);
 void launch_attend(const Plan& p);
 void launch_route_shared(const Plan& p);
 void launch_expert(const Plan& p);
@@ -132,7 +135,14 @@ struct BPlan {
 
   // workspace
   float* Dn;      // [BH, N] dO . O per query
-  float* G;       // [s, BH, m, k, 2d] routed dk, dv per (slot, expert, row)
+  int CH;         // queries per item of the routed-key pass
+  int UB2;        // upper bound on its items per slot
+  WorkItem* wl2;  // [s, UB2] its items
+  int* wl2_count; // [s]
+  int* efirst;    // [s, BH, m] first full item of each expert
+  int* epart;     // [s, BH, m] partial item of each expert (-1: none)
+  float* G;       // [s, UB2, k, 2d] routed dk, dv per (slot, item, expert row)
+  float* Gs;      // [BH * m * k, 2d] each key's summed routed parts, at its first list position
   void* Qg;       // [s, BH * N, d] q in each slot's expert order
   void* dOg;      // [s, BH * N, d] dO likewise
   float* Lg;      // [s, BH * N] lse likewise

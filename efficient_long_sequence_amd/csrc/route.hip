@@ -148,6 +148,9 @@ __global__ __launch_bounds__(NW * 64) void k_route(const T* __restrict__ Q, cons
 
 // Exclusive prefix of the expert counts and the work list, for every slot.
 // One workgroup of 1024 threads; each thread owns a contiguous segment.
+// Optionally (efirst, epart not null) records where each expert's items
+// went: its full items at efirst .. efirst + count / T - 1 and its partial
+// item at epart (-1 if none).
 // Work list order: first every item of a full T queries (experts in index
 // order, so an expert's items stay adjacent), then each expert's partial
 // item, larger ones first (a counting sort on the number of 16-query
@@ -156,7 +159,8 @@ constexpr int SCAN_BUCKETS = 128;  // T <= 2048 queries per item
 
 __global__ __launch_bounds__(1024) void k_scan(const int* __restrict__ counts, int* __restrict__ gpre,
                                                WorkItem* __restrict__ wl, int* __restrict__ wl_count,
-                                               int E, int m, int s, int T, int UB) {
+                                               int E, int m, int s, int T, int UB, int* __restrict__ efirst,
+                                               int* __restrict__ epart) {
   __shared__ int sn[1024], stl[1024];
   __shared__ int bcnt[SCAN_BUCKETS];
   const int tid = threadIdx.x;
@@ -201,8 +205,14 @@ __global__ __launch_bounds__(1024) void k_scan(const int* __restrict__ counts, i
       const int n = c[x];
       gpre[(size_t)t * E + x] = nb;
       const int nf = n / T;
+      if (efirst) efirst[(size_t)t * E + x] = tb;
       for (int q = 0; q < nf; ++q) w[tb++] = WorkItem{nb + q * T, T, x, 0};
-      if (n % T) w[atomicAdd(bcnt + bucket(n % T), 1)] = WorkItem{nb + nf * T, n % T, x, 0};
+      int pi = -1;
+      if (n % T) {
+        pi = atomicAdd(bcnt + bucket(n % T), 1);
+        w[pi] = WorkItem{nb + nf * T, n % T, x, 0};
+      }
+      if (epart) epart[(size_t)t * E + x] = pi;
       nb += n;
     }
     __syncthreads();
@@ -278,10 +288,17 @@ void launch_route(const Plan& p) {
 void launch_bucket(const Plan& p) {
   const int E = p.BH * p.m;
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, p.stream, p.counts, p.gpre, p.wl, p.wl_count, E, p.m, p.s,
-                     p.T, p.UB);
+                     p.T, p.UB, (int*)nullptr, (int*)nullptr);
   dim3 grid((unsigned)((p.N + SC_QPW - 1) / SC_QPW), (unsigned)p.BH);
   hipLaunchKernelGGL(k_scatter, grid, dim3(256), (size_t)2 * p.m * sizeof(int), p.stream, p.route, p.gpre, p.cursor,
                      p.perm, p.N, p.m, p.s, p.BH);
 }
 
+}  // namespace mita
+
+namespace mita {
+void launch_items(const Plan& p, int T, int UB, WorkItem* wl, int* wl_count, int* efirst, int* epart) {
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, p.stream, p.counts, p.gpre, wl, wl_count, p.BH * p.m, p.m,
+                     p.s, T, UB, efirst, epart);
+}
 }  // namespace mita
