@@ -8,8 +8,8 @@ log-sum-exps are checked against their definitions first.
 
 Tolerance (bf16): the kernels round each probability and each softmax
 gradient to bf16 before the matrix cores (relative error <= 2^-8), accumulate
-in fp32 and round each gradient once to bf16 (<= 2^-8), and take dO . O from
-the bf16 output; every gradient element is a sum of such terms, so its error
+in fp32 and round each gradient once to bf16 (<= 2^-8); dO . o and dv~ . v~
+come from the forward's fp32 output and v~; every gradient element is a sum of such terms, so its error
 is a small multiple of 2^-8 of the largest terms.  The bar is relative to the
 tensor's largest reference entry: max error <= 2.5e-2, mean <= 2.5e-3 of it
 (fp32 inputs: 2e-4 and 2e-5, the fp32 matrix-core path rounds nothing to
@@ -56,6 +56,12 @@ CASES = {
     "official_s2": (1, 2, 1, 3000, 64, 1, 24, 40, 2, "clustered", 8, "bf16", "official"),
     "routed_s2": (1, 2, 1, 3000, 64, 1, 24, 64, 2, "clustered", 8, "bf16", "routed"),
     "routed_f32": (1, 1, 6, 10, 32, 2, 2, 9, 1, "iid", 0, "f32", "routed"),
+    # edge cases: one token; s = m with two tokens; k = N; a single landmark
+    "tiny_n1": (1, 1, 1, 1, 64, 1, 1, 1, 1, "iid", 0, "bf16", "paper"),
+    "tiny_n2_s_eq_m_f32": (1, 1, 1, 2, 32, 1, 2, 2, 2, "iid", 0, "f32", "paper"),
+    "k_eq_n_routed": (1, 1, 1, 300, 64, 1, 4, 300, 1, "clustered", 4, "bf16", "routed"),
+    "k_eq_n_f32": (1, 1, 8, 8, 32, 2, 2, 64, 1, "iid", 0, "f32", "official"),
+    "m1": (1, 2, 1, 500, 64, 1, 1, 40, 1, "clustered", 4, "bf16", "paper"),
 }
 
 
@@ -72,7 +78,10 @@ def _run(Q, K, V, dO, pool, k, s, dtype, variant):
 
 
 def _compare(name, got, ref, dtype):
-    scale = max(float(np.abs(ref).max()), 1e-30)
+    if float(np.abs(ref).max()) < 1e-6:  # a gradient that vanishes identically
+        assert float(np.abs(got).max()) <= 1e-3, name
+        return
+    scale = float(np.abs(ref).max())
     err = np.abs(got - ref)
     mx, mean = float(err.max()) / scale, float(err.mean()) / scale
     gh_.say(f"[gpu]   {name}: max {mx:.2e} mean {mean:.2e} (of max |ref| {scale:.3e})")
@@ -120,7 +129,8 @@ def test_autograd_function_matches_the_entry_points():
     torch.cuda.synchronize()
     assert torch.equal(O.detach(), O2)
     assert torch.equal(q.grad, g[0])
-    for a, b in ((kk.grad, g[1]), (v.grad, g[2])):  # fp32 atomics: last-bit differences
+    # a key's routed parts are summed in an order that may change: last bits
+    for a, b in ((kk.grad, g[1]), (v.grad, g[2])):
         assert float((a.float() - b.float()).abs().max()) <= 1e-2 * float(b.float().abs().max())
 
 
