@@ -6,7 +6,9 @@ One step is one full mita_forward call (pool, landmark scoring with shared
 values and top-k, routing, bucketing, joint-softmax attention) over one batch
 of synthetic inputs already resident in HBM.  The headline workload is the
 N = 1M long sequence (B=1, H=2, d=64, m=k=512, s=1); the N = 64K and 256K
-shapes are timed the same way and reported beside it.  Prints one JSON line.
+shapes are timed the same way and reported beside it, and so is the
+training step (forward_train + backward) of the headline workload.  Prints
+one JSON line.
 
 The roofline of the dominant kernel uses the per-stage durations measured
 with HIP events on the launch stream during the timed steps; its HBM traffic
@@ -498,6 +500,14 @@ def main():
                                stages_ms=r["stages"], roofline=roofline(wo, r["stages"])))
             del r
             torch.cuda.empty_cache()
+    train = None
+    if not args.only:
+        # the backward pass of the same workload (forward_train + backward), reported beside the forward
+        try:
+            train = time_backward(w, 5, 2)
+        except Exception as exc:  # keep the forward line even if this extra measurement fails
+            train = dict(error=f"{type(exc).__name__}: {exc}")
+        torch.cuda.empty_cache()
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, run)
     line = dict(
         metric=METRIC, value=run["tokens_per_s"], unit="tokens/s", n_gpus=1, steps=args.steps,
@@ -507,7 +517,7 @@ def main():
                     pool=f"{w.grid_h}x{w.grid_w} tokens -> {w.land_h}x{w.land_w} landmarks",
                     values=f"{w.kind}, {w.n_clusters} clusters, seed {w.seed}"),
         roofline=roofline(w, run["stages"]), cpu_baseline=cpu, stages_ms=run["stages"],
-        other_workloads=others,
+        other_workloads=others, training_step=train,
     )
     print(json.dumps(line), flush=True)
 
