@@ -11,7 +11,9 @@ training step (forward_train + backward) of the headline workload.  Prints
 one JSON line.
 
 The roofline of the dominant kernel uses the per-stage durations measured
-with HIP events on the launch stream during the timed steps; its HBM traffic
+with HIP events on the launch stream during the timed steps, against the
+spec-sheet peak and against the peak this GPU sustains on a pure
+matrix-core loop or a plain copy (measured at the start of the run); its HBM traffic
 comes from committed rocprofv3 counter summaries (profiles/) when they were
 taken on the current kernel sources, else null.  The CPU baseline times the
 fp64 oracle on a bounded sample of the same workload on the host cores.
@@ -135,6 +137,9 @@ def time_workload(w, steps: int, warmup: int, variant: str = "paper", k: int | N
 STAGE_KERNEL = {"score": "k_score", "route": "k_route_shared", "attend": "k_expert"}
 
 
+MEASURED_PEAKS = {}  # filled once per run by mita.probe_peaks()
+
+
 def roofline_of(w, stages: dict, stage: str, traffic):
     flops, byts = algorithmic(w, stage)
     sec = stages[stage] * 1e-3
@@ -146,6 +151,12 @@ def roofline_of(w, stages: dict, stage: str, traffic):
         r = dict(bound="hbm", achieved=byts / sec / 1e9, peak=PEAK_HBM_GBS, unit="GB/s")
     r["frac"] = r["achieved"] / r["peak"]
     r["traffic"] = traffic
+    # the same against what this GPU sustains on a pure matrix-core loop or a
+    # plain copy (bf16 only: the probe runs bf16 MFMA)
+    pm = MEASURED_PEAKS.get("mfma_bf16_tflops" if r["bound"] == "mfma" else "hbm_copy_gbs")
+    if pm and (r["bound"] == "hbm" or w.dtype == "bf16"):
+        r["peak_measured"] = pm
+        r["frac_measured"] = r["achieved"] / pm
     r.update(kernel=STAGE_KERNEL[stage], kernel_ms=stages[stage], alg_flops=flops, alg_bytes=byts,
              hbm_gbs_alg=byts / sec / 1e9, mfma_tflops_alg=flops / sec / 1e12)
     return r
@@ -485,6 +496,9 @@ def main():
                               points=e2e(pts))), flush=True)
         return
     w = WORKLOADS[args.workload]
+    from efficient_long_sequence_amd import mita as _mita
+    MEASURED_PEAKS.update(_mita.probe_peaks())
+    torch.cuda.empty_cache()
     if args.copy_calib_mib:
         n = args.copy_calib_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
@@ -525,6 +539,7 @@ def main():
                     values=f"{w.kind}, {w.n_clusters} clusters, seed {w.seed}"),
         roofline=roofline(w, run["stages"]), cpu_baseline=cpu, stages_ms=run["stages"],
         call_ms=run["call_ms"], tokens_per_s_median_call=run["tokens_per_s_median_call"],
+        measured_peaks=dict(MEASURED_PEAKS),
         other_workloads=others, training_step=train,
     )
     print(json.dumps(line), flush=True)

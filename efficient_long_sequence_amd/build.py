@@ -20,7 +20,7 @@ OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmita.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "pool.hip", "score.hip", "route.hip", "attend.hip", "resident.hip", "dense.hip", "backward.hip"]
+SOURCES = ["api.cpp", "pool.hip", "score.hip", "route.hip", "attend.hip", "resident.hip", "dense.hip", "backward.hip", "probe.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

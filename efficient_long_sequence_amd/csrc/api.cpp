@@ -442,6 +442,22 @@ mita_status mita_backward(const void* Q, const void* K, const void* V, const voi
   return hipGetLastError() == hipSuccess ? MITA_OK : MITA_ERR_HIP;
 }
 
+mita_status mita_probe_mfma(float* out, int blocks, int iters, void* stream) {
+  if (!out) return MITA_ERR_NULL;
+  if (blocks <= 0 || iters <= 0 || ((uintptr_t)out & 15u)) return MITA_ERR_PARAM;
+  (void)hipGetLastError();
+  launch_probe_mfma(out, blocks, iters, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? MITA_OK : MITA_ERR_HIP;
+}
+
+mita_status mita_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (!src || !dst) return MITA_ERR_NULL;
+  if (bytes % 16 || (((uintptr_t)src | (uintptr_t)dst) & 15u)) return MITA_ERR_PARAM;
+  (void)hipGetLastError();
+  launch_probe_copy(src, dst, bytes, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? MITA_OK : MITA_ERR_HIP;
+}
+
 int mita_num_stages(void) { return ST_COUNT; }
 
 const char* mita_stage_name(int stage) { return (stage >= 0 && stage < ST_COUNT) ? kStageNames[stage] : "?"; }

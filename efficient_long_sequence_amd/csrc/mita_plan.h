@@ -178,6 +178,9 @@ struct BPlan {
   hipStream_t stream;
 };
 void launch_backward(const BPlan& p);
+// peak probes (measurement only)
+void launch_probe_mfma(float* out, int blocks, int iters, hipStream_t stream);
+void launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 // stationary rows per workgroup of the backward kernels (dtype 0 f32, 1 bf16)
 int backward_rows(int dtype);
 // LDS a resident entry set may take (of 160 KB per compute unit).

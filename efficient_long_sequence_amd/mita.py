@@ -27,6 +27,7 @@ EXPORTS = [
     "mita_workspace_bytes", "mita_forward", "mita_forward_timed", "mita_forward_variant", "mita_dense_attention", "mita_num_stages",
     "mita_stage_name", "mita_events_create", "mita_events_destroy", "mita_events_elapsed",
     "mita_status_str", "mita_version", "mita_forward_train", "mita_backward_workspace_bytes", "mita_backward",
+    "mita_probe_mfma", "mita_probe_copy",
 ]
 
 
@@ -93,6 +94,10 @@ def lib() -> ctypes.CDLL:
     L.mita_backward.restype = c_int
     L.mita_backward.argtypes = [vp] * 8 + [c_int, c_int, c_int, c_int, c_int, Pool, c_int, c_int, c_int, c_int,
                                            ctypes.POINTER(Saved), vp, c_size, vp]
+    L.mita_probe_mfma.restype = c_int
+    L.mita_probe_mfma.argtypes = [vp, c_int, c_int, vp]
+    L.mita_probe_copy.restype = c_int
+    L.mita_probe_copy.argtypes = [vp, vp, c_size, vp]
     L.mita_status_str.restype = ctypes.c_char_p
     L.mita_status_str.argtypes = [c_int]
     L.mita_version.restype = ctypes.c_char_p
@@ -343,3 +348,34 @@ class MitaFunction(torch.autograd.Function):
         pool, k, s, variant = ctx.cfg
         dQ, dK, dV = backward(Q, K, V, O, dO.contiguous(), pool, k, s, ctx.sv, variant=variant)
         return dQ, dK, dV, None, None, None, None
+
+
+def probe_peaks(mfma_blocks: int = 2048, mfma_iters: int = 16384, copy_mib: int = 1024, reps: int = 3) -> dict:
+    """Measured peaks of this GPU: bf16 matrix-core TFLOP/s (mita_probe_mfma)
+    and device-copy HBM GB/s (bytes read + written, mita_probe_copy); the
+    best of `reps` timed launches after one warm-up."""
+    L = lib()
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    out = torch.empty(mfma_blocks * 256, dtype=torch.float32, device=dev)
+    src = torch.ones(copy_mib << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+
+    def best(fn):
+        fn()
+        ms = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ms.append(a.elapsed_time(b))
+        return min(ms)
+
+    t_mfma = best(lambda: _check(L.mita_probe_mfma(out.data_ptr(), mfma_blocks, mfma_iters, stream)))
+    t_copy = best(lambda: _check(L.mita_probe_copy(src.data_ptr(), dst.data_ptr(), src.numel(), stream)))
+    flops = mfma_blocks * 4 * mfma_iters * 8 * 16384.0
+    return dict(mfma_bf16_tflops=flops / (t_mfma * 1e-3) * 1e-12, hbm_copy_gbs=2.0 * src.numel() / (t_copy * 1e-3) * 1e-9,
+                probe="mita_probe_mfma (eight independent 16x16x32 bf16 MFMA chains on varied operands), "
+                      "mita_probe_copy (16-byte copy, four loads in flight per thread)")

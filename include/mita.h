@@ -231,6 +231,19 @@ mita_status mita_backward(const void* Q, const void* K, const void* V, const voi
                           const mita_saved* saved, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* Peak probes for the roofline (measurement only; no part of the forward or
+ * backward pass uses them).  Each enqueues one kernel on `stream`.
+ *   mita_probe_mfma  `blocks` workgroups of 256 threads; every wave runs
+ *                    `iters` rounds of eight independent 16x16x32 bf16
+ *                    matrix operations, blocks * 4 * iters * 8 * 16384 flops
+ *                    in all; writes blocks * 256 floats to `out` (device).
+ *   mita_probe_copy  copies `bytes` (a multiple of 16) from src to dst
+ *                    (device, 16-byte aligned, not overlapping).
+ * Errors: MITA_ERR_NULL (NULL pointer), MITA_ERR_PARAM (blocks or iters
+ * <= 0, bytes not a multiple of 16, misaligned pointer), MITA_ERR_HIP. */
+mita_status mita_probe_mfma(float* out, int blocks, int iters, void* stream);
+mita_status mita_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
+
 /* Number of timed stages and their names ("pool", "estimate", "score", ...). */
 int mita_num_stages(void);
 const char* mita_stage_name(int stage);

@@ -178,3 +178,14 @@ def test_backward_workspace_bytes():
     s2 = L.mita_backward_workspace_bytes(mita.BF16, 1, 2, 4096, 64, mita.Pool(1, 4096, 1, 64), 64, 64, 2)
     s1 = L.mita_backward_workspace_bytes(mita.BF16, 1, 2, 4096, 64, mita.Pool(1, 4096, 1, 64), 64, 64, 1)
     assert s2 > s1
+
+
+def test_probes_reject_invalid_arguments():
+    L = mita.lib()
+    assert L.mita_probe_mfma(None, 1, 1, None) == 1
+    assert L.mita_probe_mfma(A, 0, 1, None) == 3
+    assert L.mita_probe_mfma(A, 1, 0, None) == 3
+    assert L.mita_probe_mfma(A + 4, 1, 1, None) == 3
+    assert L.mita_probe_copy(None, A, 16, None) == 1
+    assert L.mita_probe_copy(A, A, 17, None) == 3
+    assert L.mita_probe_copy(A + 8, A, 16, None) == 3
