@@ -396,6 +396,34 @@ def ablation(steps: int, warmup: int):
     return out
 
 
+def time_graph(w, run, steps: int) -> float:
+    """Tokens/s of the same forward captured once in a HIP graph
+    (torch.cuda.CUDAGraph) and replayed `steps` times: the launch cost
+    removed, which is what bounds the small shapes."""
+    import torch
+    from efficient_long_sequence_amd import mita
+    q, kk, v, pool, ws = run["q"], run["k"], run["v"], run["pool"], run["ws"]
+    out = torch.empty_like(q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mita.forward(q, kk, v, pool, w.k, w.s, workspace=ws, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mita.forward(q, kk, v, pool, w.k, w.s, workspace=ws, out=out)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    del g
+    return w.tokens * steps / dt
+
+
 def backward_flops(w, k: int | None = None) -> float:
     """Matrix-core flops of one backward pass (2 flops per multiply-add):
     joint softmax at the landmarks (S, dP, dq~, dv~ over m N pairs), routed
@@ -518,9 +546,12 @@ def main():
             wo = WORKLOADS[name]
             r = time_workload(wo, args.steps, args.warmup)
             others.append(dict(workload=name, tokens_per_s=r["tokens_per_s"], ms_per_step=r["ms_per_step"],
-                               call_ms=r["call_ms"], stages_ms=r["stages"], roofline=roofline(wo, r["stages"])))
+                               call_ms=r["call_ms"], stages_ms=r["stages"], roofline=roofline(wo, r["stages"]),
+                               tokens_per_s_graph=time_graph(wo, r, args.steps)))
             del r
             torch.cuda.empty_cache()
+    # the same calls replayed from one captured HIP graph (launch cost removed)
+    graph_value = time_graph(w, run, args.steps)
     train = None
     if not args.only:
         # the backward pass of the same workload (forward_train + backward), reported beside the forward
@@ -539,6 +570,7 @@ def main():
                     values=f"{w.kind}, {w.n_clusters} clusters, seed {w.seed}"),
         roofline=roofline(w, run["stages"]), cpu_baseline=cpu, stages_ms=run["stages"],
         call_ms=run["call_ms"], tokens_per_s_median_call=run["tokens_per_s_median_call"],
+        tokens_per_s_graph=graph_value,
         measured_peaks=dict(MEASURED_PEAKS),
         other_workloads=others, training_step=train,
     )
