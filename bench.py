@@ -485,6 +485,8 @@ def main():
     ap.add_argument("--e2e", action="store_true",
                     help="instead: the three-layer, width-128 model with MiTA vs dense attention at 16K-1M")
     ap.add_argument("--e2e-max-n", type=int, default=1 << 20, help="largest sequence length of --e2e")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the measured-peak probes (profiling runs: keeps their kernels out of the trace)")
     ap.add_argument("--backward", action="store_true",
                     help="instead: training step (forward_train + backward) of --workload (all long ones unless --only)")
     ap.add_argument("--ablation", action="store_true",
@@ -524,9 +526,10 @@ def main():
                               points=e2e(pts))), flush=True)
         return
     w = WORKLOADS[args.workload]
-    from efficient_long_sequence_amd import mita as _mita
-    MEASURED_PEAKS.update(_mita.probe_peaks())
-    torch.cuda.empty_cache()
+    if not args.no_probe:
+        from efficient_long_sequence_amd import mita as _mita
+        MEASURED_PEAKS.update(_mita.probe_peaks())
+        torch.cuda.empty_cache()
     if args.copy_calib_mib:
         n = args.copy_calib_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
