@@ -323,11 +323,9 @@ template <typename T, int D, int NW, int IB, bool ROUTED>
 __global__ __launch_bounds__(NW * 64, 2) void k_bwd_keys(
     const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ Ysrc, const T* __restrict__ Zsrc,
     const float* __restrict__ Lv, const float* __restrict__ Dv, const int32_t* __restrict__ topk,
-    const WorkItem* __restrict__ wl2, const int* __restrict__ wl2_count, const int* __restrict__ counts,
-    const int* __restrict__ efirst, const int* __restrict__ epart, float* __restrict__ G,
-    const int* __restrict__ icnt, const int* __restrict__ ipos, const int32_t* __restrict__ ilist,
-    T* __restrict__ dK, T* __restrict__ dV, int N, int m, int k, int s, int nent, int BH, int CH, int UB2,
-    float cscale, float cnat) {
+    const WorkItem* __restrict__ wl2, const int* __restrict__ wl2_count, float* __restrict__ G,
+    const int* __restrict__ icnt, const int* __restrict__ ipos, T* __restrict__ dK, T* __restrict__ dV, int N,
+    int m, int k, int nent, int BH, int UB2, float cscale, float cnat) {
   constexpr int NT = NW * 64;
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, li = lane % 16, lg = lane / 16;
@@ -826,9 +824,8 @@ static void launch_backward_t(const BPlan& p) {
     allow_lds(fn, lds);
     dim3 grid((unsigned)(s * p.UB2), (unsigned)((k + R - 1) / R));
     hipLaunchKernelGGL(fn, grid, dim3(NW * 64), lds, st, (const T*)p.K, (const T*)p.V, (const T*)p.Qg,
-                       (const T*)p.dOg, p.Lg, p.Dg, p.topk, p.wl2, p.wl2_count, p.bk.counts, p.efirst, p.epart, p.G,
-                       (const int*)nullptr, (const int*)nullptr, (const int32_t*)nullptr, (T*)nullptr, (T*)nullptr,
-                       N, m, k, s, 0, BH, p.CH, p.UB2, p.cscale, p.cnat);
+                       (const T*)p.dOg, p.Lg, p.Dg, p.topk, p.wl2, p.wl2_count, p.G, (const int*)nullptr,
+                       (const int*)nullptr, (T*)nullptr, (T*)nullptr, N, m, k, 0, BH, p.UB2, p.cscale, p.cnat);
     const long long mk = (long long)m * k, total = (long long)BH * mk, keys = (long long)BH * N;
     const unsigned gb = (unsigned)((total + 255) / 256);
     hipLaunchKernelGGL(k_bwd_inv_count, dim3(gb), dim3(256), 0, st, p.topk, p.icnt, N, mk, total);
@@ -862,9 +859,9 @@ static void launch_backward_t(const BPlan& p) {
     allow_lds(fn, lds);
     dim3 grid((unsigned)((N + R3 - 1) / R3), (unsigned)BH);
     hipLaunchKernelGGL(fn, grid, dim3(NW * 64), lds, st, (const T*)p.K, (const T*)p.V, (const T*)p.qt,
-                       (const T*)p.dvtT, p.lse_lm, p.delta, p.topk, p.wl2, p.wl2_count, p.bk.counts, p.efirst,
-                       p.epart, p.Gs, (const int*)p.icnt, (const int*)p.ipos, (const int32_t*)p.ilist, (T*)p.dK,
-                       (T*)p.dV, N, m, k, s, p.shared ? m : 0, BH, p.CH, p.UB2, p.cscale, p.cnat);
+                       (const T*)p.dvtT, p.lse_lm, p.delta, p.topk, (const WorkItem*)nullptr, (const int*)nullptr,
+                       p.Gs, (const int*)p.icnt, (const int*)p.ipos, (T*)p.dK, (T*)p.dV, N, m, k,
+                       p.shared ? m : 0, BH, p.UB2, p.cscale, p.cnat);
   }
   if (p.shared) {
     auto fn = &k_bwd_lm<T, D, NW, IB, false>;

@@ -1,5 +1,8 @@
 /*
- * mita.h - C ABI of the MI355X (gfx950) MiTA forward-pass library (libmita.so).
+ * mita.h - C ABI of the MI355X (gfx950) MiTA library (libmita.so): the forward
+ * pass (mita_forward and its variants), its backward pass for training
+ * (mita_forward_train, mita_backward), the dense-attention baseline the pages
+ * compare against (mita_dense_attention) and peak probes for the roofline.
  *
  * MiTA (Mixture-of-Top-k Attention; Wen et al., arXiv 2602.01219 v6) replaces
  * each query's scan over N keys by m + s*k entries.  Per (b, h) head the
@@ -56,7 +59,7 @@ typedef enum {
   MITA_ERR_PARAM = 3,       /* k not in [1, N]; s not in [1, m]; pointer not 16-byte aligned */
   MITA_ERR_UNSUPPORTED = 4, /* d not in {32, 64}; unknown dtype; s > 8; m > 4096;
                                N > 2^26; k > 2048 when N > 8192; B*H > 65535;
-                               B*H*N > 2^31 - 1 */
+                               B*H*N > 2^31 - 1; (backward only) B*H*m*k > 2^31 - 1 */
   MITA_ERR_WORKSPACE = 5,   /* workspace smaller than mita_workspace_bytes() */
   MITA_ERR_HIP = 6          /* the HIP runtime reported an error while enqueueing */
 } mita_status;
