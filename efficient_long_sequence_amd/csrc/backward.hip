@@ -405,6 +405,121 @@ __global__ __launch_bounds__(NW * 64, 2) void k_bwd_keys(
   }
 }
 
+// The shared-value key pass with the landmarks resident in LDS (bf16): q~
+// and dv~ are staged once per workgroup, row-major, and the workgroup loops
+// over key tiles with no staging and no barrier in its inner loop.  The
+// transposed operands (q~^T, dv~^T for dk += dS q~, dv += P dv~) come from
+// the same row-major rows through the LDS transpose read: in each 16-lane
+// group, lane i receives element i mod 4 of the 8-byte words supplied by
+// lanes i/4 + 4t (t = 0..3), so lane j supplying row x0 + 4g + j/4, columns
+// 16 cb + 4 (j mod 4) .. + 3 hands lane (li, g) the values of column 16 cb +
+// li for the four keys of slots t (and a second read for slots 4..7).
+typedef short tr_v4s __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void tr_frag(Frag<__bf16>& f, const __bf16* rows, int KS, int x0, int cb, int lane16,
+                                        int g) {
+  const int r = lane16 / 4, c = cb * 16 + 4 * (lane16 % 4);
+  const tr_v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) tr_v4s*)(rows + (size_t)(x0 + 4 * g + r) * KS + c));
+  const tr_v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) tr_v4s*)(rows + (size_t)(x0 + 16 + 4 * g + r) * KS + c));
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    f.v[t] = __builtin_bit_cast(__bf16, a[t]);
+    f.v[4 + t] = __builtin_bit_cast(__bf16, b[t]);
+  }
+}
+
+template <int D, int NW, int IB>
+__global__ __launch_bounds__(NW * 64, 2) void k_bwd_keys_res(
+    const __bf16* __restrict__ K, const __bf16* __restrict__ V, const __bf16* __restrict__ Qt,
+    const __bf16* __restrict__ dVt, const float* __restrict__ Lm, const float* __restrict__ Dm,
+    const float* __restrict__ Gs, const int* __restrict__ icnt, const int* __restrict__ ipos,
+    __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int m, float cscale, float cnat) {
+  using T = __bf16;
+  constexpr int KS = TileLayout<T, D>::KS;
+  constexpr int R = NW * 16 * IB;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int Mp = (m + 31) / 32 * 32;
+  T* Yr = (T*)smem;
+  T* Zr = Yr + (size_t)Mp * KS;
+  float* Le = (float*)(Zr + (size_t)Mp * KS);
+  float* De = Le + Mp;
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, li = lane % 16, lg = lane / 16;
+  const int bh = blockIdx.y;
+  // stage the head's landmarks once: rows past m are zero and their L, delta
+  // zero (they are masked in the last step)
+  constexpr int CPR = D / 8;
+  for (int i = tid; i < Mp * CPR; i += NW * 64) {
+    const int r = i / CPR, c = (i % CPR) * 8;
+    uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
+    if (r < m) {
+      a = *(const uint4*)(Qt + ((size_t)bh * m + r) * D + c);
+      b = *(const uint4*)(dVt + ((size_t)bh * m + r) * D + c);
+    }
+    *(uint4*)(Yr + (size_t)r * KS + c) = a;
+    *(uint4*)(Zr + (size_t)r * KS + c) = b;
+  }
+  for (int r = tid; r < Mp; r += NW * 64) {
+    Le[r] = r < m ? Lm[(size_t)bh * m + r] : 0.f;
+    De[r] = r < m ? Dm[(size_t)bh * m + r] : 0.f;
+  }
+  __syncthreads();
+  const float Lr[IB] = {}, Dr[IB] = {};
+  const int ntiles = (N + R - 1) / R;
+  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int r0 = tile * R + wave * 16 * IB;
+    int jr[IB];
+#pragma unroll
+    for (int b = 0; b < IB; ++b) {
+      const int r = r0 + b * 16 + li;
+      jr[b] = r < N ? r : -1;
+    }
+    Frag<T> xf[IB][D / 32], wf[IB][D / 32];
+    load_rows<T, D, IB>(xf, lg, [&](int b) -> const T* { return jr[b] >= 0 ? K + ((size_t)bh * N + jr[b]) * D : nullptr; });
+    load_rows<T, D, IB>(wf, lg, [&](int b) -> const T* { return jr[b] >= 0 ? V + ((size_t)bh * N + jr[b]) * D : nullptr; });
+    f32x4 ax[IB][D / 16], aw[IB][D / 16];
+    zero_acc<IB, D>(ax);
+    zero_acc<IB, D>(aw);
+    for (int x0 = 0; x0 < m; x0 += 32) {
+      StepFrags<T, D> fy, fz;
+      fy.load_keys(Yr + (size_t)x0 * KS, li, lg);
+      fz.load_keys(Zr + (size_t)x0 * KS, li, lg);
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb) {
+        tr_frag(fy.va[cb], Yr, KS, x0, cb, li, lg);
+        tr_frag(fz.va[cb], Zr, KS, x0, cb, li, lg);
+      }
+      const int nv = m - x0;
+      if (nv >= 32) grad_step<IB, false, false, true>(fy, fz, xf, wf, nv, lg, cscale, cnat, Lr, Dr, Le + x0, De + x0, ax, aw);
+      else grad_step<IB, true, false, true>(fy, fz, xf, wf, nv, lg, cscale, cnat, Lr, Dr, Le + x0, De + x0, ax, aw);
+    }
+#pragma unroll
+    for (int b = 0; b < IB; ++b) {
+      if (jr[b] < 0) continue;
+      const size_t key = (size_t)bh * N + jr[b];
+      if (icnt[key] > 0) {  // the key's routed parts, summed by k_bwd_route_sum
+        const float* gp = Gs + (size_t)ipos[key] * (2 * D);
+#pragma unroll
+        for (int cb = 0; cb < D / 16; ++cb) {
+          const float4 a = *(const float4*)(gp + cb * 16 + 4 * lg);
+          const float4 c = *(const float4*)(gp + D + cb * 16 + 4 * lg);
+          ax[b][cb][0] += a.x; ax[b][cb][1] += a.y; ax[b][cb][2] += a.z; ax[b][cb][3] += a.w;
+          aw[b][cb][0] += c.x; aw[b][cb][1] += c.y; aw[b][cb][2] += c.z; aw[b][cb][3] += c.w;
+        }
+      }
+      const size_t o = key * D;
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          dK[o + cb * 16 + 4 * lg + r] = from_f32<T>(ax[b][cb][r]);
+          dV[o + cb * 16 + 4 * lg + r] = from_f32<T>(aw[b][cb][r]);
+        }
+    }
+  }
+}
+
 // Copies of q, dO, lse and dO . o in each slot's expert order: position
 // t * BH * N + x holds query perm_t[x] of head x / N (each head fills N
 // consecutive positions of a slot).  CPR lanes per row.
@@ -851,9 +966,26 @@ static void launch_backward_t(const BPlan& p) {
                        (const int*)p.bk.counts, (const int*)p.efirst, (const int*)p.epart, (const int*)p.icnt,
                        (const int*)p.ipos, (const int32_t*)p.ilist, p.Gs, N, m, k, s, BH, p.CH, p.UB2);
   }
-  // shared-value softmax for the keys plus their routed parts: final dK, dV
-  // (one 16-row block per wave: with two this pass spills registers)
-  {
+  // shared-value softmax for the keys plus their routed parts: final dK, dV;
+  // bf16 with the landmarks resident in LDS when they fit
+  const size_t res_lds = 2 * (size_t)((m + 31) / 32 * 32) * (TileLayout<T, D>::KS * sizeof(T) + 4);
+  bool resident = false;
+  if constexpr (sizeof(T) == 2) {
+    if (p.shared && res_lds <= RES_MAX) {
+      resident = true;
+      constexpr int IBR = 1;
+      auto fn = &k_bwd_keys_res<D, NW, IBR>;
+      allow_lds(fn, res_lds);
+      const int tiles = (N + NW * 16 * IBR - 1) / (NW * 16 * IBR);
+      const int per_head = (256 + BH - 1) / BH;  // about one workgroup per compute unit in all
+      dim3 grid((unsigned)(tiles < per_head ? tiles : per_head), (unsigned)BH);
+      hipLaunchKernelGGL(fn, grid, dim3(NW * 64), res_lds, st, (const T*)p.K, (const T*)p.V, (const T*)p.qt,
+                         (const T*)p.dvtT, p.lse_lm, p.delta, (const float*)p.Gs, (const int*)p.icnt,
+                         (const int*)p.ipos, (T*)p.dK, (T*)p.dV, N, m, p.cscale, p.cnat);
+    }
+  }
+  // (otherwise staged per step, one 16-row block per wave: with two this pass spills registers)
+  if (!resident) {
     constexpr int IB3 = 1, R3 = NW * 16 * IB3;
     auto fn = &k_bwd_keys<T, D, NW, IB3, false>;
     allow_lds(fn, lds);
