@@ -19,9 +19,11 @@
 // through double-buffered LDS.  Per step it forms S = X.Y and dP = W.Z (X, W
 // the rows' two vectors; Y, Z the entries'), then P and dS, and accumulates
 // dX += c dS Y and, when asked, dW += P Z, with c the logit scale.  The entry
-// vectors are staged twice, row-major (operands of S and dP) and transposed
-// (operands of the accumulations); the slot permutation of the forward's
-// layout cancels in every contraction.  The passes:
+// vectors are needed in two orders, row-major (operands of S and dP) and
+// transposed (operands of the accumulations): bf16 tiles are staged once,
+// row-major, and read transposed through the LDS transpose read; fp32 tiles
+// are staged twice.  The slot permutation of the forward's layout cancels in
+// every contraction.  The passes:
 //
 //   joint softmax, landmark rows over all queries    X q~, W v~,  Y q,  Z dO   -> dq~, dv~  (chunk partials)
 //   joint softmax, expert key rows over its queries  X k,  W v,   Y q,  Z dO   -> dk, dv    (per expert row)
@@ -44,12 +46,35 @@
 
 namespace mita {
 
+// The V^T-order operand of one 16-column block `cb` for the 32 rows x0 ..
+// x0+31 of a row-major bf16 tile (row stride KS), in the slot permutation of
+// the score layout (slot t < 4: row x0 + 4g + t; t >= 4: row x0 + 16 + 4g +
+// t - 4), read with the LDS transpose read ds_read_b64_tr_b16: in each
+// 16-lane group, lane i receives element i mod 4 of the 8-byte words supplied
+// by lanes i/4 + 4t (t = 0..3); lane j supplies row x0 + 4g + j/4, columns
+// 16 cb + 4 (j mod 4) .. + 3, so lane (li, g) receives column 16 cb + li of
+// the four rows of its slots.  The two results are joined as whole vectors.
+typedef short tr_v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void tr_frag(Frag<__bf16>& f, const __bf16* rows, int KS, int x0, int cb, int lane16,
+                                        int g) {
+  const int r = lane16 / 4, c = cb * 16 + 4 * (lane16 % 4);
+  const tr_v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) tr_v4s*)(rows + (size_t)(x0 + 4 * g + r) * KS + c));
+  const tr_v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) tr_v4s*)(rows + (size_t)(x0 + 16 + 4 * g + r) * KS + c));
+  const bf16x4 a4 = __builtin_bit_cast(bf16x4, a), b4 = __builtin_bit_cast(bf16x4, b);
+  f.v = __builtin_shufflevector(a4, b4, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // LDS of one step: Y (row-major + transposed), Z (likewise), then L and delta
 // of the 32 entries.
 template <typename T, int D>
 struct GradLds {
   using TL = TileLayout<T, D>;
-  static constexpr size_t TILE_BYTES = (size_t)TL::ELEMS * sizeof(T);
+  // bf16: one row-major tile per vector (both operand orders are read from
+  // it, the transposed one with tr_frag); fp32: rows and a transposed copy
+  static constexpr bool ROWS = sizeof(T) == 2;
+  static constexpr size_t TILE_BYTES = (size_t)(ROWS ? TL::K_ELEMS : TL::ELEMS) * sizeof(T);
   static constexpr size_t STEP_BYTES = 2 * TILE_BYTES + 64 * sizeof(float);
   static_assert(TILE_BYTES % 16 == 0, "tiles must stay 16-byte aligned");
   __device__ static T* y(unsigned char* b) { return (T*)b; }
@@ -61,8 +86,9 @@ template <typename T, int D, int NT, bool WANT_W, bool ENT>
 struct GradLoader {
   using GL = GradLds<T, D>;
   using TL = TileLayout<T, D>;
-  TileLoader<T, D, NT, true> ly;
-  TileLoader<T, D, NT, WANT_W> lz;
+  static constexpr bool TWO = !GL::ROWS;  // stage a transposed copy too (fp32)
+  TileLoader<T, D, NT, TWO> ly;
+  TileLoader<T, D, NT, TWO && WANT_W> lz;
   float2 e;
   template <class RY, class RZ, class RE>
   __device__ __forceinline__ void load(RY ry, RZ rz, RE re) {
@@ -161,9 +187,18 @@ __device__ __forceinline__ void grad_stream(unsigned char* smem, int nsteps, con
     const T* y = GL::y(cur);
     const T* z = GL::z(cur);
     fy.load_keys(y, li, lg);
-    fy.load_vals(y + TL::K_ELEMS, li, lg);
     fz.load_keys(z, li, lg);
-    if constexpr (WANT_W) fz.load_vals(z + TL::K_ELEMS, li, lg);
+    if constexpr (GL::ROWS) {
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb) tr_frag(fy.va[cb], y, TL::KS, 0, cb, li, lg);
+      if constexpr (WANT_W) {
+#pragma unroll
+        for (int cb = 0; cb < D / 16; ++cb) tr_frag(fz.va[cb], z, TL::KS, 0, cb, li, lg);
+      }
+    } else {
+      fy.load_vals(y + TL::K_ELEMS, li, lg);
+      if constexpr (WANT_W) fz.load_vals(z + TL::K_ELEMS, li, lg);
+    }
     const float* Le = GL::ent(cur);
     const int nv = src.nv(st);
     const float cs = src.cscale(st), cn = src.cnat(st);
@@ -409,27 +444,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_bwd_keys(
 // and dv~ are staged once per workgroup, row-major, and the workgroup loops
 // over key tiles with no staging and no barrier in its inner loop.  The
 // transposed operands (q~^T, dv~^T for dk += dS q~, dv += P dv~) come from
-// the same row-major rows through the LDS transpose read: in each 16-lane
-// group, lane i receives element i mod 4 of the 8-byte words supplied by
-// lanes i/4 + 4t (t = 0..3), so lane j supplying row x0 + 4g + j/4, columns
-// 16 cb + 4 (j mod 4) .. + 3 hands lane (li, g) the values of column 16 cb +
-// li for the four keys of slots t (and a second read for slots 4..7).
-typedef short tr_v4s __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ void tr_frag(Frag<__bf16>& f, const __bf16* rows, int KS, int x0, int cb, int lane16,
-                                        int g) {
-  const int r = lane16 / 4, c = cb * 16 + 4 * (lane16 % 4);
-  const tr_v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) tr_v4s*)(rows + (size_t)(x0 + 4 * g + r) * KS + c));
-  const tr_v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) tr_v4s*)(rows + (size_t)(x0 + 16 + 4 * g + r) * KS + c));
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    f.v[t] = __builtin_bit_cast(__bf16, a[t]);
-    f.v[4 + t] = __builtin_bit_cast(__bf16, b[t]);
-  }
-}
-
+// the same row-major rows through the LDS transpose read (tr_frag).
 template <int D, int NW, int IB>
 __global__ __launch_bounds__(NW * 64, 2) void k_bwd_keys_res(
     const __bf16* __restrict__ K, const __bf16* __restrict__ V, const __bf16* __restrict__ Qt,
