@@ -276,10 +276,10 @@ BPlan make_bplan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, i
   p.cscale = (float)(1.4426950408889634 / std::sqrt((double)d));
   p.cscale_sh = p.cscale;
   p.R = backward_rows(p.dtype);
-  // landmark-row passes: about 1024 workgroups in all, whole 32-entry steps
+  // landmark-row passes: about 256 workgroups in all (one per compute unit: fewer chunks mean fewer partials to sum), whole 32-entry steps
   auto chunks = [&](int& L, int& C) {
     const long long rt = ceil_div(m, p.R);
-    long long c = ceil_div(1024, rt * p.BH);
+    long long c = ceil_div(256, rt * p.BH);
     c = c < 1 ? 1 : c;
     const long long cmax = ceil_div(N, 32);
     c = c > cmax ? cmax : c;
