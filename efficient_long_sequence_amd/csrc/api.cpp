@@ -277,8 +277,8 @@ BPlan make_bplan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, i
   p.cscale_sh = p.cscale;
   p.R = backward_rows(p.dtype);
   // landmark-row passes: about 256 workgroups in all (one per compute unit: fewer chunks mean fewer partials to sum), whole 32-entry steps
-  auto chunks = [&](int& L, int& C) {
-    const long long rt = ceil_div(m, p.R);
+  auto chunks = [&](int& L, int& C, int rows) {
+    const long long rt = ceil_div(m, rows);
     long long c = ceil_div(256, rt * p.BH);
     c = c < 1 ? 1 : c;
     const long long cmax = ceil_div(N, 32);
@@ -287,13 +287,13 @@ BPlan make_bplan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, i
     L = (L + 31) / 32 * 32;
     C = ceil_div(N, L);
   };
-  chunks(p.L1, p.C1);
-  chunks(p.L4, p.C4);
+  chunks(p.L1, p.C1, p.R);
+  chunks(p.L4, p.C4, backward_lm4_rows(p.dtype));
   // query grouping: tiles of R queries
   Plan& b = p.bk;
   b.dtype = p.dtype; b.esize = p.esize; b.B = B; b.H = H; b.BH = p.BH; b.N = N; b.d = d;
   b.m = m; b.k = k; b.s = s;
-  b.T = p.R;
+  b.T = backward_query_rows(p.dtype);
   b.UB = (int)((long long)p.BH * (ceil_div(N, b.T) + m));
 
   const size_t BH = p.BH, Mr = (size_t)p.BH * m, Nr = (size_t)p.BH * N;

@@ -1011,17 +1011,22 @@ static void launch_backward_t(const BPlan& p) {
                        p.shared ? m : 0, BH, p.UB2, p.cscale, p.cnat);
   }
   if (p.shared) {
-    auto fn = &k_bwd_lm<T, D, NW, IB, false>;
+    // four 16-row blocks per wave for bf16 (one accumulator only in this pass)
+    constexpr int IB4 = sizeof(T) == 2 ? 4 : IB, R4 = NW * 16 * IB4;
+    auto fn = &k_bwd_lm<T, D, NW, IB4, false>;
     allow_lds(fn, lds);
-    dim3 grid((unsigned)((m + R - 1) / R), (unsigned)p.C4, (unsigned)BH);
+    dim3 grid((unsigned)((m + R4 - 1) / R4), (unsigned)p.C4, (unsigned)BH);
     hipLaunchKernelGGL(fn, grid, dim3(NW * 64), lds, st, (const T*)p.K, (const T*)p.V, (const T*)p.qt,
                        (const T*)p.dvtT, p.lse_lm, p.delta, p.part4, N, m, p.L4, p.C4, p.cscale, p.cnat);
     hipLaunchKernelGGL((k_bwd_red4<D>), dim3((unsigned)(BH * m)), dim3(64), 0, st, p.part4, p.dqt, m, p.C4);
   }
   // queries: slots s-1 .. 1 store parts, slot 0 finishes dQ
   {
-    auto f1 = &k_bwd_q<T, D, NW, IB, false>;
-    auto f0 = &k_bwd_q<T, D, NW, IB, true>;
+    // three 16-query blocks per wave for bf16 (no transposed values or
+    // second accumulator in this pass leaves the registers for it)
+    constexpr int IBQ = sizeof(T) == 2 ? 3 : IB;
+    auto f1 = &k_bwd_q<T, D, NW, IBQ, false>;
+    auto f0 = &k_bwd_q<T, D, NW, IBQ, true>;
     const size_t lq = lds + (size_t)k * 4;
     allow_lds(f1, lq);
     allow_lds(f0, lq);
@@ -1039,6 +1044,8 @@ static void launch_backward_t(const BPlan& p) {
 
 // Rows per workgroup of every backward kernel for a dtype (the plan's R).
 int backward_rows(int dtype) { return dtype == 1 ? 8 * 16 * 2 : 4 * 16 * 1; }
+int backward_query_rows(int dtype) { return dtype == 1 ? 8 * 16 * 3 : 4 * 16 * 1; }
+int backward_lm4_rows(int dtype) { return dtype == 1 ? 8 * 16 * 4 : 4 * 16 * 1; }
 
 void launch_backward(const BPlan& p) {
   if (p.dtype == 0) {
