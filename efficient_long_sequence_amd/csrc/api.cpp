@@ -314,6 +314,7 @@ BPlan make_bplan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, i
   p.ipos = (int*)take(Nr * 4);
   p.bsum = (int*)take(((Nr + 4095) / 4096 + 1) * 4);
   p.ilist = (int32_t*)take(Mr * k * 4);
+  p.ikey = (int32_t*)take(Mr * k * 4);
   // routed-key pass: items of at most CH queries (large experts split)
   p.CH = 2048;
   p.UB2 = (int)((long long)p.BH * (ceil_div(N, p.CH) + m));

@@ -560,23 +560,26 @@ __global__ __launch_bounds__(256) void k_bwd_gather(const T* __restrict__ Q, con
 }
 
 // Sum of every routed part of a key (over its expert rows, slots and items)
-// into Gs[ipos[key]] (a compact row per key that some expert holds).  Each
-// key's 2d values are spread over 2d/4 lanes with float4 loads.
+// into Gs[ipos[key]] (a compact row per key that some expert holds).  The
+// grid runs over positions of the inverse lists, which are grouped by key;
+// the first position of each key sums its parts.  Each key's 2d values are
+// spread over 2d/4 lanes with float4 loads.
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_route_sum(const float* __restrict__ G, const int* __restrict__ counts,
                                                        const int* __restrict__ efirst, const int* __restrict__ epart,
-                                                       const int* __restrict__ icnt, const int* __restrict__ ipos,
+                                                       const int* __restrict__ icnt, const int32_t* __restrict__ ikey,
                                                        const int32_t* __restrict__ ilist, float* __restrict__ Gs,
-                                                       int N, int m, int k, int s, int BH, int CH, int UB2) {
+                                                       long long total, int N, int m, int k, int s, int BH, int CH,
+                                                       int UB2) {
   constexpr int LPK = 2 * D / 4;  // lanes per key
   const long long g = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long key = g / LPK;
+  const long long p0 = g / LPK;
   const int c = (int)(g % LPK) * 4;
-  if (key >= (long long)BH * N) return;
+  if (p0 >= total) return;
+  const int key = ikey[p0];
+  if (p0 > 0 && ikey[p0 - 1] == key) return;  // not the key's first position
   const int n = icnt[key];
-  if (n == 0) return;
-  const int bh = (int)(key / N);
-  const int p0 = ipos[key];
+  const int bh = key / N;
   const size_t E = (size_t)BH * m;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int x = 0; x < n; ++x) {
@@ -607,14 +610,17 @@ __global__ __launch_bounds__(256) void k_bwd_inv_count(const int32_t* __restrict
 }
 
 __global__ __launch_bounds__(256) void k_bwd_inv_fill(const int32_t* __restrict__ topk, const int* __restrict__ ipos,
-                                                      int* __restrict__ icur, int32_t* __restrict__ ilist, int N,
-                                                      long long mk, long long total) {
+                                                      int* __restrict__ icur, int32_t* __restrict__ ilist,
+                                                      int32_t* __restrict__ ikey, int N, long long mk,
+                                                      long long total) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   if (i >= total) return;
   const long long bh = i / mk;
   const int j = min(max(topk[i], 0), N - 1);
   const long long key = bh * N + j;
-  ilist[ipos[key] + atomicAdd(icur + key, 1)] = (int32_t)(i - bh * mk);
+  const long long at = ipos[key] + atomicAdd(icur + key, 1);
+  ilist[at] = (int32_t)(i - bh * mk);
+  ikey[at] = (int32_t)key;
 }
 
 // Exclusive prefix sum of n ints in three passes: per-block scans of
@@ -963,8 +969,8 @@ static void launch_backward_t(const BPlan& p) {
     hipLaunchKernelGGL(k_scan_local, dim3((unsigned)nb), dim3(256), 0, st, (const int*)p.icnt, p.ipos, p.bsum, keys);
     hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(256), 0, st, p.bsum, nb);
     hipLaunchKernelGGL(k_scan_add, dim3((unsigned)nb), dim3(256), 0, st, p.ipos, (const int*)p.bsum, keys);
-    hipLaunchKernelGGL(k_bwd_inv_fill, dim3(gb), dim3(256), 0, st, p.topk, (const int*)p.ipos, p.icur, p.ilist, N,
-                       mk, total);
+    hipLaunchKernelGGL(k_bwd_inv_fill, dim3(gb), dim3(256), 0, st, p.topk, (const int*)p.ipos, p.icur, p.ilist,
+                       p.ikey, N, mk, total);
   }
   if (p.shared) {
     auto fn = &k_bwd_lm<T, D, NW, IB, true>;
@@ -976,10 +982,10 @@ static void launch_backward_t(const BPlan& p) {
                        p.dqt, p.dvt, (T*)p.dvtT, p.delta, m, p.C1);
   }
   {
-    const long long thr = (long long)BH * N * (2 * D / 4);
+    const long long total = (long long)BH * m * k, thr = total * (2 * D / 4);
     hipLaunchKernelGGL((k_bwd_route_sum<D>), dim3((unsigned)((thr + 255) / 256)), dim3(256), 0, st, (const float*)p.G,
                        (const int*)p.bk.counts, (const int*)p.efirst, (const int*)p.epart, (const int*)p.icnt,
-                       (const int*)p.ipos, (const int32_t*)p.ilist, p.Gs, N, m, k, s, BH, p.CH, p.UB2);
+                       (const int32_t*)p.ikey, (const int32_t*)p.ilist, p.Gs, total, N, m, k, s, BH, p.CH, p.UB2);
   }
   // shared-value softmax for the keys plus their routed parts: final dK, dV;
   // bf16 with the landmarks resident in LDS when they fit

@@ -152,6 +152,7 @@ struct BPlan {
   int* ipos;      // [BH * N] exclusive prefix of icnt
   int* bsum;      // per-block totals of the prefix
   int32_t* ilist; // [BH * m * k] (expert * k + row) of each key, grouped by key
+  int32_t* ikey;  // [BH * m * k] the key (bh * N + j) of each list position
   float* part1;   // [BH, C1, m, 2d] per-chunk dq~ and dv~ of the joint softmax
   float* part4;   // [BH, C4, m, d] per-chunk dq~ of the shared-value softmax
   float* dqt;     // [BH, m, d] dq~
