@@ -535,27 +535,49 @@ __global__ __launch_bounds__(NW * 64, 2) void k_bwd_keys_res(
   }
 }
 
-// Copies of q, dO, lse and dO . o in each slot's expert order: position
-// t * BH * N + x holds query perm_t[x] of head x / N (each head fills N
-// consecutive positions of a slot).  CPR lanes per row.
+// Copies of q, dO, lse and delta = dO . o in each slot's expert order:
+// position t * BH * N + x holds query perm_t[x] of head x / N (each head
+// fills N consecutive positions of a slot).  delta is formed here from the
+// forward's fp32 output (so that it equals sum_t P_t dP_t up to fp32 rounding
+// even where one entry dominates and dP_t - delta cancels) and also written
+// in query order (slot 0).  CPR lanes per row.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_bwd_gather(const T* __restrict__ Q, const T* __restrict__ dO,
-                                                    const float* __restrict__ lse, const float* __restrict__ Dn,
+                                                    const float* __restrict__ O32, const float* __restrict__ lse,
                                                     const int32_t* __restrict__ perm, T* __restrict__ Qg,
                                                     T* __restrict__ dOg, float* __restrict__ Lg,
-                                                    float* __restrict__ Dg, int N, long long BHN, long long rows) {
+                                                    float* __restrict__ Dg, float* __restrict__ Dn, int N,
+                                                    long long BHN, long long rows) {
   constexpr int EPC = 16 / (int)sizeof(T), CPR = D / EPC;
   const long long g = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long pos = g / CPR;  // over s * BH * N
   const int c = (int)(g % CPR);
-  if (pos >= rows) return;
-  const long long x = pos % BHN;
-  const long long src = (x / N) * N + min(max(perm[pos], 0), N - 1);
-  *(uint4*)(Qg + pos * D + c * EPC) = *(const uint4*)(Q + src * D + c * EPC);
-  *(uint4*)(dOg + pos * D + c * EPC) = *(const uint4*)(dO + src * D + c * EPC);
-  if (c == 0) {
+  float acc = 0.f;
+  long long src = 0;
+  if (pos < rows) {
+    const long long x = pos % BHN;
+    src = (x / N) * N + min(max(perm[pos], 0), N - 1);
+    const uint4 qv = *(const uint4*)(Q + src * D + c * EPC);
+    const uint4 gv = *(const uint4*)(dO + src * D + c * EPC);
+    *(uint4*)(Qg + pos * D + c * EPC) = qv;
+    *(uint4*)(dOg + pos * D + c * EPC) = gv;
+    const T* pg = (const T*)&gv;
+    const float4* po = (const float4*)(O32 + src * D + c * EPC);
+#pragma unroll
+    for (int q = 0; q < EPC / 4; ++q) {
+      const float4 o = po[q];
+      acc = __builtin_fmaf(o.x, to_f32(pg[4 * q]), acc);
+      acc = __builtin_fmaf(o.y, to_f32(pg[4 * q + 1]), acc);
+      acc = __builtin_fmaf(o.z, to_f32(pg[4 * q + 2]), acc);
+      acc = __builtin_fmaf(o.w, to_f32(pg[4 * q + 3]), acc);
+    }
+  }
+#pragma unroll
+  for (int off = CPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (pos < rows && c == 0) {
     Lg[pos] = lse[src];
-    Dg[pos] = Dn[src];
+    Dg[pos] = acc;
+    if (pos < BHN) Dn[src] = acc;
   }
 }
 
@@ -791,35 +813,6 @@ __global__ __launch_bounds__(NW * 64, 2) void k_bwd_q(
 // ---------------------------------------------------------------------------
 // small passes
 
-// delta_n = dO_n . o_n (fp32) with o_n the forward's output before rounding,
-// so that delta equals sum_t P_t dP_t up to fp32 rounding even where one
-// entry dominates and dP_t - delta cancels.  CPR lanes per row.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void k_bwd_dot(const float* __restrict__ O32, const T* __restrict__ dO,
-                                                 float* __restrict__ Dn, long long rows) {
-  constexpr int EPC = 16 / (int)sizeof(T), CPR = D / EPC;
-  const long long g = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long row = g / CPR;
-  const int c = (int)(g % CPR);
-  float acc = 0.f;
-  if (row < rows) {
-    const uint4 b = *(const uint4*)(dO + row * D + c * EPC);
-    const T* pb = (const T*)&b;
-    const float4* pa = (const float4*)(O32 + row * D + c * EPC);
-#pragma unroll
-    for (int q = 0; q < EPC / 4; ++q) {
-      const float4 a = pa[q];
-      acc = __builtin_fmaf(a.x, to_f32(pb[4 * q]), acc);
-      acc = __builtin_fmaf(a.y, to_f32(pb[4 * q + 1]), acc);
-      acc = __builtin_fmaf(a.z, to_f32(pb[4 * q + 2]), acc);
-      acc = __builtin_fmaf(a.w, to_f32(pb[4 * q + 3]), acc);
-    }
-  }
-#pragma unroll
-  for (int off = CPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && c == 0) Dn[row] = acc;
-}
-
 // v~ in the input dtype, rounded as the forward rounded it for step 6.
 template <typename T>
 __global__ __launch_bounds__(256) void k_bwd_cvt(const float* __restrict__ x, T* __restrict__ y, long long n) {
@@ -929,13 +922,6 @@ static void launch_backward_t(const BPlan& p) {
     const int blocks = (int)((n16 + 255) / 256 < 4096 ? (n16 + 255) / 256 : 4096);
     hipLaunchKernelGGL(k_bwd_zero, dim3(blocks), dim3(256), 0, st, (uint4*)p.zero_begin, n16);
   }
-  {
-    constexpr int CPR = D * (int)sizeof(T) / 16;
-    const long long rows = (long long)BH * N;
-    const long long blocks = (rows * CPR + 255) / 256;
-    hipLaunchKernelGGL((k_bwd_dot<T, D>), dim3((unsigned)blocks), dim3(256), 0, st, p.o32, (const T*)p.dO,
-                       p.Dn, rows);
-  }
   if (p.shared) {
     const long long n = (long long)BH * m * D;
     hipLaunchKernelGGL((k_bwd_cvt<T>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p.vt32, (T*)p.vt, n);
@@ -953,8 +939,8 @@ static void launch_backward_t(const BPlan& p) {
     constexpr int CPR = D * (int)sizeof(T) / 16;
     const long long BHN = (long long)BH * N, rows = (long long)s * BHN;
     hipLaunchKernelGGL((k_bwd_gather<T, D>), dim3((unsigned)((rows * CPR + 255) / 256)), dim3(256), 0, st,
-                       (const T*)p.Q, (const T*)p.dO, p.lse, (const float*)p.Dn, (const int32_t*)p.bk.perm, (T*)p.Qg,
-                       (T*)p.dOg, p.Lg, p.Dg, N, BHN, rows);
+                       (const T*)p.Q, (const T*)p.dO, p.o32, p.lse, (const int32_t*)p.bk.perm, (T*)p.Qg, (T*)p.dOg,
+                       p.Lg, p.Dg, p.Dn, N, BHN, rows);
     launch_items(p.bk, p.CH, p.UB2, p.wl2, p.wl2_count, p.efirst, p.epart);
     auto fn = &k_bwd_keys<T, D, NW, IB, true>;
     allow_lds(fn, lds);
