@@ -62,7 +62,13 @@ CASES = {
     "k_eq_n_routed": (1, 1, 1, 300, 64, 1, 4, 300, 1, "clustered", 4, "bf16", "routed"),
     "k_eq_n_f32": (1, 1, 8, 8, 32, 2, 2, 64, 1, "iid", 0, "f32", "official"),
     "m1": (1, 2, 1, 500, 64, 1, 1, 40, 1, "clustered", 4, "bf16", "paper"),
+    # experts larger than one work item (2048 queries): their queries are
+    # split over several items whose key parts are summed afterwards
+    "split_m2": (1, 1, 1, 8192, 64, 1, 2, 64, 1, "iid", 0, "bf16", "paper"),
+    "split_routed_s2": (1, 2, 1, 6000, 64, 1, 3, 48, 2, "clustered", 4, "bf16", "routed"),
+    "split_official_f32": (1, 1, 1, 5000, 32, 1, 2, 32, 1, "iid", 0, "f32", "official"),
 }
+SPLIT_ITEM = 2048  # queries per work item of the routed passes
 
 
 def _run(Q, K, V, dO, pool, k, s, dtype, variant):
@@ -101,6 +107,8 @@ def test_backward_parity(label):
     for b in range(B):
         for h in range(H):
             I, e = r["topk"][b, h], r["route"][b, h]
+            if label.startswith("split"):
+                assert np.bincount(e.ravel(), minlength=lh * lw).max() > SPLIT_ITEM
             Qh, Kh, Vh = (x[b, h].astype(np.float64) for x in (Q, K, V))
             Qt = mo.landmarks(Qh, gh, gw, lh, lw, dtype)
             np.testing.assert_array_equal(r["qt"][b, h], Qt)
