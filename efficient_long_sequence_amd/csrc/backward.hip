@@ -162,12 +162,14 @@ __device__ __forceinline__ void grad_step(const StepFrags<T, D>& fy, const StepF
 // Streams nsteps steps of entries from `src` through LDS and applies
 // grad_step to the wave's blocks.  src.ry(st) / src.rz(st): row pointer
 // functions of step st (nullptr past the end); src.re(st): (L, delta) of an
-// entry; src.nv(st), src.cscale(st), src.cnat(st).  Ends with a barrier.
+// entry; src.nv(st), src.cscale(st), src.cnat(st).  A wave with `active`
+// false (none of its rows exists) only helps stage.  Ends with a barrier.
 template <int IB, bool ROWL, bool WANT_W, bool ENT, int NT, typename T, int D, class Src>
 __device__ __forceinline__ void grad_stream(unsigned char* smem, int nsteps, const Src& src,
                                             const Frag<T> (&xf)[IB][D / 32], const Frag<T> (&wf)[IB][D / 32],
                                             const float (&Lr)[IB], const float (&Dr)[IB],
-                                            f32x4 (&ax)[IB][D / 16], f32x4 (&aw)[IB][D / 16], int li, int lg) {
+                                            f32x4 (&ax)[IB][D / 16], f32x4 (&aw)[IB][D / 16], int li, int lg,
+                                            bool active = true) {
   using GL = GradLds<T, D>;
   using TL = TileLayout<T, D>;
   GradLoader<T, D, NT, WANT_W, ENT> ld;
@@ -183,27 +185,29 @@ __device__ __forceinline__ void grad_stream(unsigned char* smem, int nsteps, con
     unsigned char* nxt = (st & 1) ? b0 : b1;
     const bool more = st + 1 < nsteps;
     if (more) ld.load(src.ry(st + 1), src.rz(st + 1), src.re(st + 1));
-    StepFrags<T, D> fy, fz;
-    const T* y = GL::y(cur);
-    const T* z = GL::z(cur);
-    fy.load_keys(y, li, lg);
-    fz.load_keys(z, li, lg);
-    if constexpr (GL::ROWS) {
+    if (active) {
+      StepFrags<T, D> fy, fz;
+      const T* y = GL::y(cur);
+      const T* z = GL::z(cur);
+      fy.load_keys(y, li, lg);
+      fz.load_keys(z, li, lg);
+      if constexpr (GL::ROWS) {
 #pragma unroll
-      for (int cb = 0; cb < D / 16; ++cb) tr_frag(fy.va[cb], y, TL::KS, 0, cb, li, lg);
-      if constexpr (WANT_W) {
+        for (int cb = 0; cb < D / 16; ++cb) tr_frag(fy.va[cb], y, TL::KS, 0, cb, li, lg);
+        if constexpr (WANT_W) {
 #pragma unroll
-        for (int cb = 0; cb < D / 16; ++cb) tr_frag(fz.va[cb], z, TL::KS, 0, cb, li, lg);
+          for (int cb = 0; cb < D / 16; ++cb) tr_frag(fz.va[cb], z, TL::KS, 0, cb, li, lg);
+        }
+      } else {
+        fy.load_vals(y + TL::K_ELEMS, li, lg);
+        if constexpr (WANT_W) fz.load_vals(z + TL::K_ELEMS, li, lg);
       }
-    } else {
-      fy.load_vals(y + TL::K_ELEMS, li, lg);
-      if constexpr (WANT_W) fz.load_vals(z + TL::K_ELEMS, li, lg);
+      const float* Le = GL::ent(cur);
+      const int nv = src.nv(st);
+      const float cs = src.cscale(st), cn = src.cnat(st);
+      if (nv >= 32) grad_step<IB, false, ROWL, WANT_W>(fy, fz, xf, wf, nv, lg, cs, cn, Lr, Dr, Le, Le + 32, ax, aw);
+      else grad_step<IB, true, ROWL, WANT_W>(fy, fz, xf, wf, nv, lg, cs, cn, Lr, Dr, Le, Le + 32, ax, aw);
     }
-    const float* Le = GL::ent(cur);
-    const int nv = src.nv(st);
-    const float cs = src.cscale(st), cn = src.cnat(st);
-    if (nv >= 32) grad_step<IB, false, ROWL, WANT_W>(fy, fz, xf, wf, nv, lg, cs, cn, Lr, Dr, Le, Le + 32, ax, aw);
-    else grad_step<IB, true, ROWL, WANT_W>(fy, fz, xf, wf, nv, lg, cs, cn, Lr, Dr, Le, Le + 32, ax, aw);
     if (more) ld.store(nxt);
     __syncthreads();
   }
@@ -754,7 +758,11 @@ __global__ __launch_bounds__(NW * 64, 2) void k_bwd_q(
   __syncthreads();
   const SrcJoint<T, D> src{qt + (size_t)bh * m * D, vt + (size_t)bh * m * D, K + row0 * D, V + row0 * D,
                            s_idx, m0, ns, k, N, cscale, cnat, cscale_sh, cnat_sh};
-  grad_stream<IB, true, false, false, NT, T, D>(smem, ns + (k + 31) / 32, src, xf, wf, Lr, Dr, ax, aw, li, lg);
+  // the last tile of an expert is partly empty: waves with no query skip
+  // the arithmetic
+  const bool active = __builtin_amdgcn_readfirstlane(wave * 16 * IB) < it.count;
+  grad_stream<IB, true, false, false, NT, T, D>(smem, ns + (k + 31) / 32, src, xf, wf, Lr, Dr, ax, aw, li, lg,
+                                                active);
 
 #pragma unroll
   for (int b = 0; b < IB; ++b) {
