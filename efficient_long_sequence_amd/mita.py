@@ -133,18 +133,24 @@ class DebugOut:
 
 
 class Events:
-    """Per-stage HIP event pairs for mita_forward_timed."""
+    """Per-stage HIP event pairs for mita_forward_timed: every stage, or only
+    the stages named in `stages` (the others enqueue no record)."""
 
-    def __init__(self):
-        self.n = lib().mita_num_stages()
+    def __init__(self, stages=None):
+        L = lib()
+        self.n = L.mita_num_stages()
+        self.names = [L.mita_stage_name(i).decode() for i in range(self.n)]
         self.arr = (ctypes.c_void_p * (2 * self.n))()
-        _check(lib().mita_events_create(self.arr, 2 * self.n))
-        self.names = [lib().mita_stage_name(i).decode() for i in range(self.n)]
+        self.timed = [i for i, nm in enumerate(self.names) if stages is None or nm in stages]
+        for i in self.timed:
+            pair = (ctypes.c_void_p * 2)()
+            _check(L.mita_events_create(pair, 2))
+            self.arr[2 * i], self.arr[2 * i + 1] = pair[0], pair[1]
 
     def elapsed_ms(self) -> dict:
         ms = (ctypes.c_float * self.n)()
         _check(lib().mita_events_elapsed(self.arr, self.n, ms))
-        return {self.names[i]: float(ms[i]) for i in range(self.n)}
+        return {self.names[i]: float(ms[i]) for i in self.timed}
 
     def close(self):
         if self.arr is not None:

@@ -106,7 +106,8 @@ mita_status mita_forward(const void* Q, const void* K, const void* V, void* O, m
 
 /* Profiling variant: identical work, and additionally records a pair of HIP
  * events around each stage on `stream`.  `events` holds 2 * mita_num_stages()
- * hipEvent_t handles made by mita_events_create (start, stop per stage).
+ * hipEvent_t handles made by mita_events_create (start, stop per stage); a
+ * stage whose two handles are NULL is not timed (no record is enqueued).
  * Read the stage times with mita_events_elapsed after the stream finished. */
 mita_status mita_forward_timed(const void* Q, const void* K, const void* V, void* O,
                                mita_dtype dtype, int B, int H, int N, int d, mita_pool pool,
@@ -251,10 +252,12 @@ mita_status mita_probe_copy(const void* src, void* dst, size_t bytes, void* stre
 int mita_num_stages(void);
 const char* mita_stage_name(int stage);
 
-/* Create / destroy `count` HIP events with timing enabled (the handles are
- * written to events[0..count)).  mita_events_elapsed fills ms[i] with the time
- * between events[2i] and events[2i+1] for i < n_pairs, blocking until they
- * complete; a stage that launched nothing reports 0. */
+/* Create / destroy `count` HIP events with timing enabled and without the
+ * system-scope memory fence (they time the stream; they do not make device
+ * memory visible to the host), written to events[0..count).  Destroy skips
+ * NULL handles.  mita_events_elapsed fills ms[i] with the time between
+ * events[2i] and events[2i+1] for i < n_pairs, blocking until they complete;
+ * a stage that launched nothing reports 0, a pair of NULL handles NaN. */
 mita_status mita_events_create(void** events, int count);
 mita_status mita_events_destroy(void** events, int count);
 mita_status mita_events_elapsed(void* const* events, int n_pairs, float* ms);
