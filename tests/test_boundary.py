@@ -6,6 +6,7 @@ and validation happens before any HIP call, so no kernel is launched and no
 pointer is dereferenced (the device pointers are placeholders).
 """
 import ctypes
+import math
 import os
 import re
 
@@ -189,3 +190,14 @@ def test_probes_reject_invalid_arguments():
     assert L.mita_probe_copy(None, A, 16, None) == 1
     assert L.mita_probe_copy(A, A, 17, None) == 3
     assert L.mita_probe_copy(A + 8, A, 16, None) == 3
+
+
+def test_events_elapsed_reports_nan_for_untimed_stages():
+    """A stage whose two handles are NULL was not timed: NaN, no HIP call."""
+    L = mita.lib()
+    n = L.mita_num_stages()
+    arr = (ctypes.c_void_p * (2 * n))()
+    ms = (ctypes.c_float * n)()
+    assert L.mita_events_elapsed(arr, n, ms) == 0
+    assert all(math.isnan(x) for x in ms)
+    assert L.mita_events_destroy(arr, 2 * n) == 0  # NULL handles are skipped
