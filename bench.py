@@ -207,10 +207,12 @@ def measured_traffic(w, stage: str):
     return None if not ent else ent.get("bytes_per_launch")
 
 
-def ingest(trace_dir: str, fetch_dir: str, write_dir: str, workload: str, command: str):
+def ingest(trace_dir: str, fetch_dir: str, write_dir: str, workload: str, command: str, log: str | None = None):
     """Turn rocprofv3 output (kernel-trace stats, FETCH_SIZE and WRITE_SIZE
     counter runs of the same command with --copy-calib-mib) into the committed
-    text summaries under profiles/."""
+    text summaries under profiles/.  `log`: the traced run's stdout, whose
+    JSON line holds bench.py's own event times of the heavy kernels, set
+    beside the trace's durations of the same (timed) launches."""
     import csv
     import glob
 
@@ -270,6 +272,30 @@ def ingest(trace_dir: str, fetch_dir: str, write_dir: str, workload: str, comman
         t = kern.get(f"{key}:{workload}", {})
         lines.append(f"| {key} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} | "
                      f"{t.get('fetch_bytes', 0) / 1e6:.1f} | {t.get('write_bytes', 0) / 1e6:.1f} |")
+    if log:
+        with open(log) as f:
+            js = [json.loads(x) for x in f if x.startswith("{")]
+        if js:
+            rl = js[-1]["roofline"]
+            live = {rl["kernel"]: rl["kernel_ms"]}
+            live.update({v["kernel"]: v["kernel_ms"] for v in rl.get("others", {}).values()})
+            steps = int(js[-1]["steps"])
+            launches = {}
+            for r in sorted(rows(trace_dir, "*kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"])):
+                key = short(r["Kernel_Name"])
+                if key in live:
+                    launches.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6)
+            lines += ["", "Agreement with `bench.py`'s own HIP events in the same traced run (its timed region is "
+                      f"the last {steps} calls):", "",
+                      "| kernel | bench.py events, timed calls (ms) | trace, same launches (ms) | trace, all launches (ms) |",
+                      "|---|---|---|---|"]
+            for key, ms in live.items():
+                d = launches.get(key, [])
+                if d:
+                    lines.append(f"| {key} | {ms:.3f} | {sum(d[-steps:]) / len(d[-steps:]):.3f} | "
+                                 f"{sum(d) / len(d):.3f} |")
+            lines += ["", "The tracer lengthens each launch by a few percent; the kernel times of an untraced "
+                      "`bench.py` run are in its JSON line (`roofline.kernel_ms`)."]
     with open(os.path.join(ROOT, "profiles", f"mita_forward_{workload}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -500,6 +526,7 @@ def main():
     ap.add_argument("--ingest", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 output of the same command")
     ap.add_argument("--ingest-command", default="")
+    ap.add_argument("--ingest-log", default=None, help="stdout of the traced run (its JSON line)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (calibrates HBM byte counters)")
     ap.add_argument("--e2e", action="store_true",
@@ -513,7 +540,7 @@ def main():
                     help="instead: MiTA against the routing-only variant with matched entries per query")
     args = ap.parse_args()
     if args.ingest:
-        ingest(*args.ingest, workload=args.workload, command=args.ingest_command)
+        ingest(*args.ingest, workload=args.workload, command=args.ingest_command, log=args.ingest_log)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
