@@ -64,9 +64,10 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
   else { p.sc_nw = 8; p.sc_ib = 4; }
   p.sc_R = p.sc_nw * 16 * p.sc_ib;
   p.sc_rt = ceil_div(m, p.sc_R);
-  // key chunks: aim for about two workgroups per compute unit
-  // (512-row tiles run one workgroup per compute unit, smaller ones two)
-  const long long target = p.sc_R >= 512 ? 256 : 512;
+  // key chunks: about as many workgroups as fit on the chip at once (8-wave
+  // tiles of two or four 16-row blocks per wave run one workgroup per compute
+  // unit, the others two)
+  const long long target = (p.sc_nw == 8 && p.sc_ib >= 2) ? 256 : 512;
   int C = ceil_div(target, (long long)p.BH * p.sc_rt);
   C = C < 1 ? 1 : C;
   const int max_c = ceil_div(N, 32);
@@ -111,8 +112,10 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
   p.fast = (resident_bytes(p.dtype, d, m) + hist_bytes <= RES_MAX &&
             resident_bytes(p.dtype, d, k) + (size_t)(k + 32 + 2048) * 4 <= RES_MAX) ? 1 : 0;
   if (p.fast) {
-    // routing workgroups: about 1024 in all, 512 queries at least
-    long long qpw = ((long long)p.BH * N + 1023) / 1024;
+    // routing workgroups: about 256 in all (one per compute unit at a
+    // time, so each stages its landmarks once for many queries), 512
+    // queries at least
+    long long qpw = ((long long)p.BH * N + 255) / 256;
     qpw = (qpw + 511) / 512 * 512;
     p.rs_qpw = (int)(qpw < 512 ? 512 : qpw);
     if (p.dtype == 0 || avg <= 16) { p.ex_nw = 1; p.ex_ib = 1; }
