@@ -33,6 +33,9 @@ constexpr float M0 = -1.0e30f;
 // bf16 hold without overflow.
 constexpr float THRESH = 8.0f;
 
+// A compile-time flag passed as a value (selects a template form in a generic lambda).
+template <bool B> struct BoolTag { static constexpr bool value = B; };
+
 template <typename T> struct Frag;
 template <> struct Frag<__bf16> { bf16x8 v; };
 template <> struct Frag<float> { float v[8]; };

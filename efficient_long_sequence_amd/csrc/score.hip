@@ -202,7 +202,11 @@ __global__ __launch_bounds__(NW * 64, (score_waves_per_eu<T, NW, IB>())) void k_
   ld.load(rowK(j_begin), rowV(j_begin));
   ld.store(buf0, buf0 + TL::K_ELEMS);
   __syncthreads();
-  for (int st = 0; st < nsteps; ++st) {
+  // one 32-key step; MASKED: the chunk's last, partial step (its absent keys
+  // get score -inf).  The partial step is peeled off the loop: with both
+  // forms of the step in the loop body the kernel runs out of registers.
+  auto body = [&](int st, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int j0 = j_begin + st * 32;
     T* cur = (st & 1) ? buf1 : buf0;
     T* nxt = (st & 1) ? buf0 : buf1;
@@ -253,16 +257,14 @@ __global__ __launch_bounds__(NW * 64, (score_waves_per_eu<T, NW, IB>())) void k_
         wcnt = off;
       }
     };
-    if constexpr (SHARED) {
-      if (nv == 32) attn_step<IB, false>(f, one, qf, nv, lg, cscale, M, Z, acc, cands);
-      else attn_step<IB, true>(f, one, qf, nv, lg, cscale, M, Z, acc, cands);
-    } else {
-      if (nv == 32) score_step<IB, false>(f, qf, nv, lg, cands);
-      else score_step<IB, true>(f, qf, nv, lg, cands);
-    }
+    if constexpr (SHARED) attn_step<IB, MASKED>(f, one, qf, nv, lg, cscale, M, Z, acc, cands);
+    else score_step<IB, MASKED>(f, qf, nv, lg, cands);
     if (more) ld.store(nxt, nxt + TL::K_ELEMS);
     __syncthreads();
-  }
+  };
+  const int nfull = (j_end - j_begin) / 32;
+  for (int st = 0; st < nfull; ++st) body(st, BoolTag<false>{});
+  if (nfull < nsteps) body(nfull, BoolTag<true>{});
 
   // partial shared values of this chunk: (max, normaliser, 2 pad, unnormalised sums)
   if constexpr (SHARED) {
