@@ -543,7 +543,7 @@ def main():
         ingest(*args.ingest, workload=args.workload, command=args.ingest_command, log=args.ingest_log)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: runs on one GPU; --gpus {args.gpus} is not supported "
               "(every head is independent: a multi-GPU run would shard heads with no communication)",
               file=sys.stderr)
         sys.exit(2)
