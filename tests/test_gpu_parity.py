@@ -74,6 +74,9 @@ EDGE = {
     "few_clusters_uneven": (1, 2, 1, 3000, 64, 1, 30, 40, 1, "clustered", 2, "bf16"),
     "large_m": (1, 1, 1, 12000, 64, 1, 600, 24, 2, "runs", 32, "bf16"),
     "dense_limit_8192": (1, 1, 64, 128, 64, 8, 8, 100, 1, "clustered", 16, "bf16"),
+    # the widest routing (s = 8 of m = 16; s = 6 takes the same kernel form)
+    "s8_m16": (1, 2, 1, 2048, 64, 1, 16, 32, 8, "clustered", 8, "bf16"),
+    "s6_f32": (1, 1, 12, 16, 32, 3, 4, 10, 6, "iid", 0, "f32"),
 }
 
 
