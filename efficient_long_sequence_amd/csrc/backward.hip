@@ -122,6 +122,11 @@ __device__ __forceinline__ void grad_step(const StepFrags<T, D>& fy, const StepF
                                           int nv, int lg, float cscale, float cnat, const float (&Lr)[IB],
                                           const float (&Dr)[IB], const float* Le, const float* De,
                                           f32x4 (&ax)[IB][D / 16], f32x4 (&aw)[IB][D / 16]) {
+  // with per-row L and no P output, the softmax-gradient scale is folded
+  // into the exponent: exp2(s cscale - (L - log2 cnat)) = P cnat (exact for
+  // d = 64, where log2 cnat = -3)
+  constexpr bool FOLD = ROWL && !WANT_W;
+  const float lcn = FOLD ? __builtin_amdgcn_logf(cnat) : 0.f;
   float le[8], de[8];
   if constexpr (!ROWL) {
 #pragma unroll
@@ -137,14 +142,15 @@ __device__ __forceinline__ void grad_step(const StepFrags<T, D>& fy, const StepF
     step_scores(fy, xf[b], sc);
     step_scores(fz, wf[b], dp);
     float p[8], ds[8];
+    const float Lb = FOLD ? Lr[b] - lcn : 0.f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const float L = ROWL ? Lr[b] : le[t];
+      const float L = FOLD ? Lb : ROWL ? Lr[b] : le[t];
       const float dl = ROWL ? Dr[b] : de[t];
       float pt = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t], cscale, -L));
       if (MASK && slot_key(t, lg) >= nv) pt = 0.f;
       p[t] = pt;
-      ds[t] = pt * (dp[t] - dl) * cnat;
+      ds[t] = FOLD ? pt * (dp[t] - dl) : pt * (dp[t] - dl) * cnat;
     }
     Frag<T> df;
     set8(df, ds);
