@@ -116,7 +116,8 @@ struct GradLoader {
 // One 32-entry step for IB blocks of 16 stationary rows.  ROWL: L and delta
 // per stationary row (Lr, Dr: this lane's row) instead of per entry (Le, De
 // in LDS).  MASK: entries at offsets >= nv are absent.
-template <int IB, bool MASK, bool ROWL, bool WANT_W, typename T, int D>
+// DSCALED: De already holds delta * cnat.
+template <int IB, bool MASK, bool ROWL, bool WANT_W, typename T, int D, bool DSCALED = false>
 __device__ __forceinline__ void grad_step(const StepFrags<T, D>& fy, const StepFrags<T, D>& fz,
                                           const Frag<T> (&xf)[IB][D / 32], const Frag<T> (&wf)[IB][D / 32],
                                           int nv, int lg, float cscale, float cnat, const float (&Lr)[IB],
@@ -127,13 +128,15 @@ __device__ __forceinline__ void grad_step(const StepFrags<T, D>& fy, const StepF
   // d = 64, where log2 cnat = -3)
   constexpr bool FOLD = ROWL && !WANT_W;
   const float lcn = FOLD ? __builtin_amdgcn_logf(cnat) : 0.f;
+  // otherwise dS = P (dP cnat - delta cnat), one fused multiply-add, with
+  // delta cnat formed once per step (or already in De)
   float le[8], de[8];
   if constexpr (!ROWL) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int j = slot_key(t, lg);
       le[t] = Le[j];
-      de[t] = De[j];
+      de[t] = DSCALED ? De[j] : De[j] * cnat;
     }
   }
 #pragma unroll
@@ -143,14 +146,15 @@ __device__ __forceinline__ void grad_step(const StepFrags<T, D>& fy, const StepF
     step_scores(fz, wf[b], dp);
     float p[8], ds[8];
     const float Lb = FOLD ? Lr[b] - lcn : 0.f;
+    const float db = ROWL ? (FOLD ? Dr[b] : Dr[b] * cnat) : 0.f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const float L = FOLD ? Lb : ROWL ? Lr[b] : le[t];
-      const float dl = ROWL ? Dr[b] : de[t];
+      const float dl = ROWL ? db : de[t];
       float pt = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t], cscale, -L));
       if (MASK && slot_key(t, lg) >= nv) pt = 0.f;
       p[t] = pt;
-      ds[t] = FOLD ? pt * (dp[t] - dl) : pt * (dp[t] - dl) * cnat;
+      ds[t] = FOLD ? pt * (dp[t] - dl) : pt * __builtin_fmaf(dp[t], cnat, -dl);
     }
     Frag<T> df;
     set8(df, ds);
@@ -487,7 +491,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_bwd_keys_res(
   }
   for (int r = tid; r < Mp; r += NW * 64) {
     Le[r] = r < m ? Lm[(size_t)bh * m + r] : 0.f;
-    De[r] = r < m ? Dm[(size_t)bh * m + r] : 0.f;
+    De[r] = r < m ? Dm[(size_t)bh * m + r] * cnat : 0.f;  // delta cnat (see grad_step)
   }
   __syncthreads();
   const float Lr[IB] = {}, Dr[IB] = {};
@@ -516,8 +520,12 @@ __global__ __launch_bounds__(NW * 64, 2) void k_bwd_keys_res(
         tr_frag(fz.va[cb], Zr, KS, x0, cb, li, lg);
       }
       const int nv = m - x0;
-      if (nv >= 32) grad_step<IB, false, false, true>(fy, fz, xf, wf, nv, lg, cscale, cnat, Lr, Dr, Le + x0, De + x0, ax, aw);
-      else grad_step<IB, true, false, true>(fy, fz, xf, wf, nv, lg, cscale, cnat, Lr, Dr, Le + x0, De + x0, ax, aw);
+      if (nv >= 32)
+        grad_step<IB, false, false, true, T, D, true>(fy, fz, xf, wf, nv, lg, cscale, cnat, Lr, Dr, Le + x0, De + x0,
+                                                      ax, aw);
+      else
+        grad_step<IB, true, false, true, T, D, true>(fy, fz, xf, wf, nv, lg, cscale, cnat, Lr, Dr, Le + x0, De + x0,
+                                                     ax, aw);
     }
 #pragma unroll
     for (int b = 0; b < IB; ++b) {
