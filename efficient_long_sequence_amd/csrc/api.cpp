@@ -279,7 +279,7 @@ BPlan make_bplan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, i
   p.cnat_sh = p.cnat;
   p.cscale = (float)(1.4426950408889634 / std::sqrt((double)d));
   p.cscale_sh = p.cscale;
-  p.R = backward_rows(p.dtype);
+  p.R = backward_rows(p.dtype, m);
   // landmark-row passes: about 256 workgroups in all (one per compute unit: fewer chunks mean fewer partials to sum), whole 32-entry steps
   auto chunks = [&](int& L, int& C, int rows) {
     const long long rt = ceil_div(m, rows);
@@ -292,7 +292,7 @@ BPlan make_bplan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, i
     C = ceil_div(N, L);
   };
   chunks(p.L1, p.C1, p.R);
-  chunks(p.L4, p.C4, backward_lm4_rows(p.dtype));
+  chunks(p.L4, p.C4, backward_lm4_rows(p.dtype, m));
   // query grouping: tiles of R queries
   Plan& b = p.bk;
   b.dtype = p.dtype; b.esize = p.esize; b.B = B; b.H = H; b.BH = p.BH; b.N = N; b.d = d;

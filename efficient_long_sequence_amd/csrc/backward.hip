@@ -932,9 +932,43 @@ static void allow_lds(F fn, size_t lds) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
 
+// 16-row blocks per wave of a pass over `rows` stationary rows (bf16): a
+// workgroup's tile should not be mostly empty rows (m or k of 128 or 256)
+static int stat_blocks(int rows, int most) { return rows <= 128 ? 1 : (rows <= 256 || most == 2) ? 2 : 4; }
+
+template <typename T, int D, int NW, int IBK>
+static void launch_routed_keys(const BPlan& p, size_t lds) {
+  constexpr int R = NW * 16 * IBK;
+  auto fn = &k_bwd_keys<T, D, NW, IBK, true>;
+  allow_lds(fn, lds);
+  dim3 grid((unsigned)(p.s * p.UB2), (unsigned)((p.k + R - 1) / R));
+  hipLaunchKernelGGL(fn, grid, dim3(NW * 64), lds, p.stream, (const T*)p.K, (const T*)p.V, (const T*)p.Qg,
+                     (const T*)p.dOg, p.Lg, p.Dg, p.topk, p.wl2, p.wl2_count, p.G, (const int*)nullptr,
+                     (const int*)nullptr, (T*)nullptr, (T*)nullptr, p.N, p.m, p.k, 0, p.BH, p.UB2, p.cscale, p.cnat);
+}
+
+template <typename T, int D, int NW, int IBL>
+static void launch_lm_joint(const BPlan& p, size_t lds) {
+  constexpr int R = NW * 16 * IBL;
+  auto fn = &k_bwd_lm<T, D, NW, IBL, true>;
+  allow_lds(fn, lds);
+  dim3 grid((unsigned)((p.m + R - 1) / R), (unsigned)p.C1, (unsigned)p.BH);
+  hipLaunchKernelGGL(fn, grid, dim3(NW * 64), lds, p.stream, (const T*)p.Q, (const T*)p.dO, (const T*)p.qt,
+                     (const T*)p.vt, p.lse, p.Dn, p.part1, p.N, p.m, p.L1, p.C1, p.cscale_sh, p.cnat_sh);
+}
+
+template <typename T, int D, int NW, int IB4>
+static void launch_lm_shared(const BPlan& p, size_t lds) {
+  constexpr int R4 = NW * 16 * IB4;
+  auto fn = &k_bwd_lm<T, D, NW, IB4, false>;
+  allow_lds(fn, lds);
+  dim3 grid((unsigned)((p.m + R4 - 1) / R4), (unsigned)p.C4, (unsigned)p.BH);
+  hipLaunchKernelGGL(fn, grid, dim3(NW * 64), lds, p.stream, (const T*)p.K, (const T*)p.V, (const T*)p.qt,
+                     (const T*)p.dvtT, p.lse_lm, p.delta, p.part4, p.N, p.m, p.L4, p.C4, p.cscale, p.cnat);
+}
+
 template <typename T, int D, int NW, int IB>
 static void launch_backward_t(const BPlan& p) {
-  constexpr int R = NW * 16 * IB;
   const size_t lds = 2 * GradLds<T, D>::STEP_BYTES;
   const hipStream_t st = p.stream;
   const int BH = p.BH, N = p.N, m = p.m, k = p.k, s = p.s;
@@ -964,12 +998,8 @@ static void launch_backward_t(const BPlan& p) {
                        (const T*)p.Q, (const T*)p.dO, p.o32, p.lse, (const int32_t*)p.bk.perm, (T*)p.Qg, (T*)p.dOg,
                        p.Lg, p.Dg, p.Dn, N, BHN, rows);
     launch_items(p.bk, p.CH, p.UB2, p.wl2, p.wl2_count, p.efirst, p.epart);
-    auto fn = &k_bwd_keys<T, D, NW, IB, true>;
-    allow_lds(fn, lds);
-    dim3 grid((unsigned)(s * p.UB2), (unsigned)((k + R - 1) / R));
-    hipLaunchKernelGGL(fn, grid, dim3(NW * 64), lds, st, (const T*)p.K, (const T*)p.V, (const T*)p.Qg,
-                       (const T*)p.dOg, p.Lg, p.Dg, p.topk, p.wl2, p.wl2_count, p.G, (const int*)nullptr,
-                       (const int*)nullptr, (T*)nullptr, (T*)nullptr, N, m, k, 0, BH, p.UB2, p.cscale, p.cnat);
+    if (sizeof(T) == 2 && stat_blocks(k, IB) == 1) launch_routed_keys<T, D, NW, 1>(p, lds);
+    else launch_routed_keys<T, D, NW, IB>(p, lds);
     const long long mk = (long long)m * k, total = (long long)BH * mk, keys = (long long)BH * N;
     const unsigned gb = (unsigned)((total + 255) / 256);
     hipLaunchKernelGGL(k_bwd_inv_count, dim3(gb), dim3(256), 0, st, p.topk, p.icnt, N, mk, total);
@@ -981,11 +1011,8 @@ static void launch_backward_t(const BPlan& p) {
                        p.ikey, N, mk, total);
   }
   if (p.shared) {
-    auto fn = &k_bwd_lm<T, D, NW, IB, true>;
-    allow_lds(fn, lds);
-    dim3 grid((unsigned)((m + R - 1) / R), (unsigned)p.C1, (unsigned)BH);
-    hipLaunchKernelGGL(fn, grid, dim3(NW * 64), lds, st, (const T*)p.Q, (const T*)p.dO, (const T*)p.qt,
-                       (const T*)p.vt, p.lse, p.Dn, p.part1, N, m, p.L1, p.C1, p.cscale_sh, p.cnat_sh);
+    if (sizeof(T) == 2 && stat_blocks(m, IB) == 1) launch_lm_joint<T, D, NW, 1>(p, lds);
+    else launch_lm_joint<T, D, NW, IB>(p, lds);
     hipLaunchKernelGGL((k_bwd_red1<T, D>), dim3((unsigned)(BH * m)), dim3(64), 0, st, p.part1, p.vt32,
                        p.dqt, p.dvt, (T*)p.dvtT, p.delta, m, p.C1);
   }
@@ -1026,12 +1053,14 @@ static void launch_backward_t(const BPlan& p) {
   }
   if (p.shared) {
     // four 16-row blocks per wave for bf16 (one accumulator only in this pass)
-    constexpr int IB4 = sizeof(T) == 2 ? 4 : IB, R4 = NW * 16 * IB4;
-    auto fn = &k_bwd_lm<T, D, NW, IB4, false>;
-    allow_lds(fn, lds);
-    dim3 grid((unsigned)((m + R4 - 1) / R4), (unsigned)p.C4, (unsigned)BH);
-    hipLaunchKernelGGL(fn, grid, dim3(NW * 64), lds, st, (const T*)p.K, (const T*)p.V, (const T*)p.qt,
-                       (const T*)p.dvtT, p.lse_lm, p.delta, p.part4, N, m, p.L4, p.C4, p.cscale, p.cnat);
+    if constexpr (sizeof(T) == 2) {
+      const int b4 = stat_blocks(m, 4);
+      if (b4 == 1) launch_lm_shared<T, D, NW, 1>(p, lds);
+      else if (b4 == 2) launch_lm_shared<T, D, NW, 2>(p, lds);
+      else launch_lm_shared<T, D, NW, 4>(p, lds);
+    } else {
+      launch_lm_shared<T, D, NW, IB>(p, lds);
+    }
     hipLaunchKernelGGL((k_bwd_red4<D>), dim3((unsigned)(BH * m)), dim3(64), 0, st, p.part4, p.dqt, m, p.C4);
   }
   // queries: slots s-1 .. 1 store parts, slot 0 finishes dQ
@@ -1057,9 +1086,9 @@ static void launch_backward_t(const BPlan& p) {
 }
 
 // Rows per workgroup of every backward kernel for a dtype (the plan's R).
-int backward_rows(int dtype) { return dtype == 1 ? 8 * 16 * 2 : 4 * 16 * 1; }
+int backward_rows(int dtype, int m) { return dtype == 1 ? 8 * 16 * stat_blocks(m, 2) : 4 * 16 * 1; }
 int backward_query_rows(int dtype) { return dtype == 1 ? 8 * 16 * 3 : 4 * 16 * 1; }
-int backward_lm4_rows(int dtype) { return dtype == 1 ? 8 * 16 * 4 : 4 * 16 * 1; }
+int backward_lm4_rows(int dtype, int m) { return dtype == 1 ? 8 * 16 * stat_blocks(m, 4) : 4 * 16 * 1; }
 
 void launch_backward(const BPlan& p) {
   if (p.dtype == 0) {

@@ -182,12 +182,13 @@ void launch_backward(const BPlan& p);
 // peak probes (measurement only)
 void launch_probe_mfma(float* out, int blocks, int iters, hipStream_t stream);
 void launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
-// stationary rows per workgroup of the backward kernels (dtype 0 f32, 1 bf16)
-int backward_rows(int dtype);
+// stationary rows per workgroup of the backward's joint landmark pass for m
+// landmarks (dtype 0 f32, 1 bf16)
+int backward_rows(int dtype, int m);
 // queries per workgroup of the backward's query pass (its work-item size)
 int backward_query_rows(int dtype);
 // landmark rows per workgroup of the shared-value landmark pass
-int backward_lm4_rows(int dtype);
+int backward_lm4_rows(int dtype, int m);
 // LDS a resident entry set may take (of 160 KB per compute unit).
 constexpr size_t RES_MAX = 150 * 1024;
 

@@ -67,6 +67,9 @@ CASES = {
     "split_m2": (1, 1, 1, 8192, 64, 1, 2, 64, 1, "iid", 0, "bf16", "paper"),
     "split_routed_s2": (1, 2, 1, 6000, 64, 1, 3, 48, 2, "clustered", 4, "bf16", "routed"),
     "split_official_f32": (1, 1, 1, 5000, 32, 1, 2, 32, 1, "iid", 0, "f32", "official"),
+    # m and k between 128 and 256: two 16-row blocks per wave in the landmark
+    # and routed-key passes (one at or below 128, four above 256)
+    "m200_k160": (1, 1, 1, 4096, 64, 1, 200, 160, 1, "clustered", 8, "bf16", "paper"),
     # the widest routing: s = 8 of m = 16, and s = 5 with fp32
     "s8": (1, 1, 1, 1024, 64, 1, 16, 24, 8, "iid", 0, "bf16", "paper"),
     "s5_official_f32": (1, 1, 6, 8, 32, 2, 4, 10, 5, "iid", 0, "f32", "official"),
