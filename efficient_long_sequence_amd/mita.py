@@ -207,14 +207,13 @@ def forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, pool, k: int, s: 
     gh, gw, lh, lw = pool
     m = lh * lw if m is None else m
     dt = _dtype_code(Q.dtype)
-    for t in (Q, K, V):
-        if not t.is_cuda or not t.is_contiguous() or t.dtype != Q.dtype or t.shape != Q.shape:
-            raise MitaError(2, "Q, K, V must be contiguous device tensors of one shape and dtype")
     P = Pool(gh, gw, lh, lw)
     need = int(L.mita_workspace_bytes(dt, B, H, N, d, P, m, k, s))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=Q.device)
     O = torch.empty_like(Q) if out is None else out
+    _check_qkv(Q, K, V, O)
+    _check_workspace(workspace, Q)
     dbg_struct, dbg = None, None
     if debug:
         dev = Q.device
@@ -265,8 +264,30 @@ class SavedOut:
 def _check_qkv(*ts):
     Q = ts[0]
     for t in ts:
-        if not t.is_cuda or not t.is_contiguous() or t.dtype != Q.dtype or t.shape != Q.shape:
-            raise MitaError(2, "tensors must be contiguous device tensors of one shape and dtype")
+        if (not t.is_cuda or not t.is_contiguous() or t.dtype != Q.dtype or t.shape != Q.shape
+                or t.device != Q.device):
+            raise MitaError(2, "tensors must be contiguous tensors of one shape and dtype on one device")
+
+
+def _check_saved(saved: "SavedOut", Q: torch.Tensor, m: int, k: int, s: int):
+    """The C ABI cannot see tensor sizes: every saved tensor must have the
+    shape, dtype and device mita_forward_train wrote it with for this call's
+    sizes (else the kernels would read outside it)."""
+    B, H, N, d = Q.shape
+    want = {"qtilde": ((B, H, m, d), Q.dtype), "vtilde": ((B, H, m, d), torch.float32),
+            "topk": ((B, H, m, k), torch.int32), "route": ((B, H, N, s), torch.int32),
+            "lse": ((B, H, N), torch.float32), "lse_landmark": ((B, H, m), torch.float32),
+            "out_f32": ((B, H, N, d), torch.float32)}
+    for name, (shape, dtype) in want.items():
+        t = getattr(saved, name)
+        if (not isinstance(t, torch.Tensor) or tuple(t.shape) != shape or t.dtype != dtype
+                or t.device != Q.device or not t.is_contiguous()):
+            raise MitaError(2, f"saved.{name} must be a contiguous {dtype} tensor of shape {shape} on {Q.device}")
+
+
+def _check_workspace(ws: torch.Tensor, Q: torch.Tensor):
+    if ws.device != Q.device or not ws.is_contiguous():
+        raise MitaError(2, "workspace must be a contiguous tensor on the inputs' device")
 
 
 def forward_train(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, pool, k: int, s: int,
@@ -285,6 +306,7 @@ def forward_train(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, pool, k: in
     if workspace is None:
         workspace = torch.empty(max(int(L.mita_workspace_bytes(dt, B, H, N, d, P, m, k, s)), 16),
                                 dtype=torch.uint8, device=Q.device)
+    _check_workspace(workspace, Q)
     dev = Q.device
     sv = SavedOut(
         qtilde=torch.empty((B, H, m, d), dtype=Q.dtype, device=dev),
@@ -320,11 +342,13 @@ def backward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, O: torch.Tensor,
     B, H, N, d = Q.shape
     gh, gw, lh, lw = pool
     m = lh * lw
+    _check_saved(saved, Q, m, k, s)
     dt = _dtype_code(Q.dtype)
     P = Pool(gh, gw, lh, lw)
     if workspace is None:
         workspace = torch.empty(max(int(L.mita_backward_workspace_bytes(dt, B, H, N, d, P, m, k, s)), 16),
                                 dtype=torch.uint8, device=Q.device)
+    _check_workspace(workspace, Q)
     dQ, dK, dV = torch.empty_like(Q), torch.empty_like(Q), torch.empty_like(Q)
     st = saved.struct()
     stream = torch.cuda.current_stream(Q.device).cuda_stream

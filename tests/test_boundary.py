@@ -201,3 +201,23 @@ def test_events_elapsed_reports_nan_for_untimed_stages():
     assert L.mita_events_elapsed(arr, n, ms) == 0
     assert all(math.isnan(x) for x in ms)
     assert L.mita_events_destroy(arr, 2 * n) == 0  # NULL handles are skipped
+
+
+def test_saved_tensors_are_checked_before_the_call():
+    """mita.backward checks every saved tensor against the call's sizes (the
+    C ABI cannot see them); a mismatch raises before any launch."""
+    import torch
+    B, H, N, d, m, k, s = 1, 2, 64, 32, 4, 8, 1
+    Q = torch.zeros(B, H, N, d, dtype=torch.bfloat16)
+    good = dict(qtilde=torch.zeros(B, H, m, d, dtype=torch.bfloat16),
+                vtilde=torch.zeros(B, H, m, d), topk=torch.zeros(B, H, m, k, dtype=torch.int32),
+                route=torch.zeros(B, H, N, s, dtype=torch.int32), lse=torch.zeros(B, H, N),
+                lse_landmark=torch.zeros(B, H, m), out_f32=torch.zeros(B, H, N, d))
+    mita._check_saved(mita.SavedOut(**good), Q, m, k, s)
+    for name, bad in (("topk", torch.zeros(B, H, m, k + 1, dtype=torch.int32)),
+                      ("route", torch.zeros(B, H, N, s, dtype=torch.int64)),
+                      ("out_f32", torch.zeros(B, H, N, d, dtype=torch.bfloat16)),
+                      ("lse", torch.zeros(B, H, N + 1))):
+        with pytest.raises(mita.MitaError):
+            mita._check_saved(mita.SavedOut(**{**good, name: bad}), Q, m, k, s)
+
