@@ -305,10 +305,11 @@ def cpu_baseline(w, run):
     """Time the fp64 oracle on a bounded sample of the same workload.
 
     Sample: head 0.  Pooling runs in full; landmark scoring, top-k and shared
-    values run on 1/16 of the landmark rows; routing and the joint softmax on
-    1/16 of the queries (with the GPU's expert lists and shared values as
-    inputs, which the oracle's cost does not depend on).  Each part's time is
-    scaled by its sampling factor and summed over the B*H heads.
+    values run on 1/3 of the landmark rows; routing and the joint softmax on
+    1/3 of the queries (with the GPU's expert lists and shared values as
+    inputs, which the oracle's cost does not depend on): about ten seconds of
+    CPU work at N = 1M.  Each part's time is scaled by its sampling factor and
+    summed over the B*H heads.
     """
     import torch
     from oracle import mita_oracle as mo
@@ -323,7 +324,7 @@ def cpu_baseline(w, run):
     torch.cuda.synchronize()
     I_gpu = dbg.topk[0, 0].cpu().numpy().astype(np.int64)
     Vt_gpu = dbg.vtilde[0, 0].cpu().numpy().astype(np.float64)
-    fr, fq = 16, 16
+    fr, fq = 3, 3
     t0 = time.perf_counter()
     Qt = mo.landmarks(Q, w.grid_h, w.grid_w, w.land_h, w.land_w, w.dtype)
     t_pool = time.perf_counter() - t0
