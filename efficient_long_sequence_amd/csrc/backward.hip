@@ -510,7 +510,9 @@ __global__ __launch_bounds__(NW * 64, 2) void k_bwd_keys_res(
     f32x4 ax[IB][D / 16], aw[IB][D / 16];
     zero_acc<IB, D>(ax);
     zero_acc<IB, D>(aw);
-    for (int x0 = 0; x0 < m; x0 += 32) {
+    // full steps in the loop, the partial last one (m not a multiple of 32)
+    // after it: one form of the step per loop body keeps the registers
+    auto step = [&](int x0, auto masked) {
       StepFrags<T, D> fy, fz;
       fy.load_keys(Yr + (size_t)x0 * KS, li, lg);
       fz.load_keys(Zr + (size_t)x0 * KS, li, lg);
@@ -519,14 +521,12 @@ __global__ __launch_bounds__(NW * 64, 2) void k_bwd_keys_res(
         tr_frag(fy.va[cb], Yr, KS, x0, cb, li, lg);
         tr_frag(fz.va[cb], Zr, KS, x0, cb, li, lg);
       }
-      const int nv = m - x0;
-      if (nv >= 32)
-        grad_step<IB, false, false, true, T, D, true>(fy, fz, xf, wf, nv, lg, cscale, cnat, Lr, Dr, Le + x0, De + x0,
-                                                      ax, aw);
-      else
-        grad_step<IB, true, false, true, T, D, true>(fy, fz, xf, wf, nv, lg, cscale, cnat, Lr, Dr, Le + x0, De + x0,
-                                                     ax, aw);
-    }
+      grad_step<IB, decltype(masked)::value, false, true, T, D, true>(fy, fz, xf, wf, m - x0, lg, cscale, cnat, Lr,
+                                                                     Dr, Le + x0, De + x0, ax, aw);
+    };
+    int x0 = 0;
+    for (; x0 + 32 <= m; x0 += 32) step(x0, BoolTag<false>{});
+    if (x0 < m) step(x0, BoolTag<true>{});
 #pragma unroll
     for (int b = 0; b < IB; ++b) {
       if (jr[b] < 0) continue;
@@ -1029,7 +1029,7 @@ static void launch_backward_t(const BPlan& p) {
   if constexpr (sizeof(T) == 2) {
     if (p.shared && res_lds <= RES_MAX) {
       resident = true;
-      constexpr int IBR = 1;
+      constexpr int IBR = 2;
       auto fn = &k_bwd_keys_res<D, NW, IBR>;
       allow_lds(fn, res_lds);
       const int tiles = (N + NW * 16 * IBR - 1) / (NW * 16 * IBR);
