@@ -129,8 +129,9 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
   } else {
     if (p.dtype == 0 || avg <= 16) { p.at_nw = 1; p.at_ib = 1; }
     else if (avg <= 64) { p.at_nw = 4; p.at_ib = 1; }
-    else if (avg <= 512) { p.at_nw = 4; p.at_ib = 4; }
-    else { p.at_nw = 8; p.at_ib = 4; }
+    // (four waves of four 16-query blocks also for large experts: that form
+    // keeps all its registers at one wave per SIMD, the 8-wave one spills)
+    else { p.at_nw = 4; p.at_ib = 4; }
     p.T = p.at_nw * 16 * p.at_ib;
   }
   p.UB = (int)((long long)p.BH * (ceil_div(N, p.T) + m));  // <= B*H*N/16 + B*H*m: fits (see validate)

@@ -34,6 +34,7 @@ __global__ __launch_bounds__(NW * 64) void k_attend(
   constexpr int NT = NW * 64;
   using TL = TileLayout<T, D>;
   __shared__ __align__(16) T smem[2 * TL::ELEMS];
+  extern __shared__ __align__(16) int32_t s_idx[];  // the expert's k key indices (dynamic LDS)
   if ((int)blockIdx.x >= *wl_count) return;
   const WorkItem it = wl[blockIdx.x];
   const int bh = it.be / m;
@@ -75,16 +76,22 @@ __global__ __launch_bounds__(NW * 64) void k_attend(
     return [=](int r) -> const T* {
       if (st < ns) { const int x = st * 32 + r; return x < m0 ? Qth + (size_t)x * D : nullptr; }
       const int x = (st - ns) * 32 + r;
-      return x < k ? Kh + (size_t)Ie[x] * D : nullptr;
+      return x < k ? Kh + (size_t)s_idx[x] * D : nullptr;
     };
   };
   auto rowV = [&](int st) {
     return [=](int r) -> const T* {
       if (st < ns) { const int x = st * 32 + r; return x < m0 ? Vth + (size_t)x * D : nullptr; }
       const int x = (st - ns) * 32 + r;
-      return x < k ? Vh + (size_t)Ie[x] * D : nullptr;
+      return x < k ? Vh + (size_t)s_idx[x] * D : nullptr;
     };
   };
+
+  // the expert's indices go to LDS first, so a staged row's address does not
+  // wait on a global load of its index (the clamp only keeps other contents
+  // in bounds)
+  for (int x = tid; x < k; x += NT) s_idx[x] = min(max(Ie[x], 0), N - 1);
+  __syncthreads();
 
   TileLoader<T, D, NT, true> ld;
   T* buf0 = smem;
@@ -159,16 +166,23 @@ __global__ __launch_bounds__(NW * 64) void k_attend(
 
 template <typename T, int D, int NW, int IB>
 static void launch_attend_t(const Plan& p) {
+  const size_t dyn = (size_t)p.k * 4, stat = 2 * TileLayout<T, D>::ELEMS * sizeof(T);
+  if (stat + dyn > 65536) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attend<T, D, NW, IB, false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attend<T, D, NW, IB, true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+  }
   for (int t = p.s - 1; t >= 0; --t) {
     const int32_t* perm = p.perm + (size_t)t * p.BH * p.N;
     const WorkItem* wl = p.wl + (size_t)t * p.UB;
     const int* wlc = p.wl_count + t;
     if (t > 0)
-      hipLaunchKernelGGL((k_attend<T, D, NW, IB, false>), dim3((unsigned)p.UB), dim3(NW * 64), 0, p.stream,
+      hipLaunchKernelGGL((k_attend<T, D, NW, IB, false>), dim3((unsigned)p.UB), dim3(NW * 64), dyn, p.stream,
                          (const T*)p.Q, (const T*)p.K, (const T*)p.V, (const T*)p.qt, (const T*)p.vtT, p.topk, perm,
                          wl, wlc, p.part, (T*)p.O, p.lse_out, p.o32, p.N, p.m, p.k, p.s, t, p.BH, p.shared ? p.m : 0, p.cscale, p.cscale_sh);
     else
-      hipLaunchKernelGGL((k_attend<T, D, NW, IB, true>), dim3((unsigned)p.UB), dim3(NW * 64), 0, p.stream,
+      hipLaunchKernelGGL((k_attend<T, D, NW, IB, true>), dim3((unsigned)p.UB), dim3(NW * 64), dyn, p.stream,
                          (const T*)p.Q, (const T*)p.K, (const T*)p.V, (const T*)p.qt, (const T*)p.vtT, p.topk, perm,
                          wl, wlc, p.part, (T*)p.O, p.lse_out, p.o32, p.N, p.m, p.k, p.s, t, p.BH, p.shared ? p.m : 0, p.cscale, p.cscale_sh);
   }
