@@ -329,10 +329,13 @@ BPlan make_bplan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, i
   p.epart = (int*)take((size_t)s * Mr * 4);
   p.G = (float*)take((size_t)s * p.UB2 * k * 2 * d * 4);
   p.Gs = (float*)take(Mr * k * 2 * d * 4);
-  p.Qg = take((size_t)s * Nr * d * p.esize);
-  p.dOg = take((size_t)s * Nr * d * p.esize);
-  p.Lg = (float*)take((size_t)s * Nr * 4);
-  p.Dg = (float*)take((size_t)s * Nr * 4);
+  // expert-order copies of the queries (fp32 only: bf16 reads them through
+  // the permutation)
+  const size_t gath = p.dtype == 0 ? (size_t)s * Nr : 0;
+  p.Qg = take(gath * d * p.esize);
+  p.dOg = take(gath * d * p.esize);
+  p.Lg = (float*)take(gath * 4);
+  p.Dg = (float*)take(gath * 4);
   b.route = (int32_t*)take(Nr * s * 4);
   b.gpre = (int*)take((size_t)s * Mr * 4);
   b.perm = (int32_t*)take((size_t)s * Nr * 4);

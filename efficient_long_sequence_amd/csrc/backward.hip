@@ -172,7 +172,9 @@ __device__ __forceinline__ void grad_step(const StepFrags<T, D>& fy, const StepF
 // Streams nsteps steps of entries from `src` through LDS and applies
 // grad_step to the wave's blocks.  src.ry(st) / src.rz(st): row pointer
 // functions of step st (nullptr past the end); src.re(st): (L, delta) of an
-// entry; src.nv(st), src.cscale(st), src.cnat(st).  A wave with `active`
+// entry; src.nv(st), src.cscale(st), src.cnat(st); src.prefetch(st), called
+// a step before ry(st) (a source read through an index fetches it there).
+// A wave with `active`
 // false (none of its rows exists) only helps stage.  Ends with a barrier.
 template <int IB, bool ROWL, bool WANT_W, bool ENT, int NT, typename T, int D, class Src>
 __device__ __forceinline__ void grad_stream(unsigned char* smem, int nsteps, const Src& src,
@@ -186,7 +188,9 @@ __device__ __forceinline__ void grad_stream(unsigned char* smem, int nsteps, con
   unsigned char* b0 = smem;
   unsigned char* b1 = smem + GL::STEP_BYTES;
   if (nsteps > 0) {
+    src.prefetch(0);
     ld.load(src.ry(0), src.rz(0), src.re(0));
+    src.prefetch(1);
     ld.store(b0);
   }
   __syncthreads();
@@ -194,7 +198,10 @@ __device__ __forceinline__ void grad_stream(unsigned char* smem, int nsteps, con
     unsigned char* cur = (st & 1) ? b1 : b0;
     unsigned char* nxt = (st & 1) ? b0 : b1;
     const bool more = st + 1 < nsteps;
-    if (more) ld.load(src.ry(st + 1), src.rz(st + 1), src.re(st + 1));
+    if (more) {
+      ld.load(src.ry(st + 1), src.rz(st + 1), src.re(st + 1));
+      src.prefetch(st + 2);
+    }
     if (active) {
       StepFrags<T, D> fy, fz;
       const T* y = GL::y(cur);
@@ -250,6 +257,52 @@ struct SrcRows {
     return [=](int r) -> float2 { const int j = a + r; return j < e ? make_float2(l[j], d[j]) : make_float2(0.f, 0.f); };
   }
   __device__ int nv(int st) const { return min(32, j1 - j0 - st * 32); }
+  __device__ void prefetch(int) const {}
+  __device__ float cscale(int) const { return cs; }
+  __device__ float cnat(int) const { return cn; }
+};
+
+// Entries = the queries perm[a .. e) of one head (rows of Y and Z; L and
+// delta per entry from Lv, Dv), read through the permutation instead of from
+// copies in that order.  Each thread's index for the step it stages next is
+// fetched one step earlier (prefetch), so a row's address never waits on a
+// global load.  bf16 staging map: thread t < 32 * CPR stages row t / CPR of
+// a step (one 16-byte chunk), thread t < 32 the entry t.
+template <typename T, int D>
+struct SrcPerm {
+  static_assert(sizeof(T) == 2, "the staging map above is the bf16 one");
+  static constexpr int CPR = D * (int)sizeof(T) / 16;
+  const T* Y;
+  const T* Z;
+  const float* Lv;
+  const float* Dv;
+  const int32_t* perm;
+  int a, e, N;
+  float cs, cn;
+  mutable int ridx = -1, eidx = -1;
+  __device__ void prefetch(int st) const {
+    const int tid = threadIdx.x;
+    const int j = a + st * 32 + tid / CPR, je = a + st * 32 + tid;
+    ridx = (tid < 32 * CPR && j < e) ? min(max(perm[j], 0), N - 1) : -1;
+    eidx = (tid < 32 && je < e) ? min(max(perm[je], 0), N - 1) : -1;
+  }
+  __device__ auto ry(int) const {
+    const T* b = Y;
+    const int x = ridx;
+    return [=](int) -> const T* { return x >= 0 ? b + (size_t)x * D : nullptr; };
+  }
+  __device__ auto rz(int) const {
+    const T* b = Z;
+    const int x = ridx;
+    return [=](int) -> const T* { return x >= 0 ? b + (size_t)x * D : nullptr; };
+  }
+  __device__ auto re(int) const {
+    const float* l = Lv;
+    const float* d = Dv;
+    const int x = eidx;
+    return [=](int) -> float2 { return x >= 0 ? make_float2(l[x], d[x]) : make_float2(0.f, 0.f); };
+  }
+  __device__ int nv(int st) const { return min(32, e - a - st * 32); }
   __device__ float cscale(int) const { return cs; }
   __device__ float cnat(int) const { return cn; }
 };
@@ -282,6 +335,7 @@ struct SrcJoint {
   }
   __device__ auto re(int) const { return [](int) -> float2 { return make_float2(0.f, 0.f); }; }
   __device__ int nv(int st) const { return st < ns ? min(32, m0 - st * 32) : min(32, k - (st - ns) * 32); }
+  __device__ void prefetch(int) const {}
   __device__ float cscale(int st) const { return st < ns ? cs_sh : cs; }
   __device__ float cnat(int st) const { return st < ns ? cn_sh : cn; }
 };
@@ -371,10 +425,10 @@ __global__ __launch_bounds__(NW * 64, 2) void k_bwd_lm(const T* __restrict__ Y, 
 template <typename T, int D, int NW, int IB, bool ROUTED>
 __global__ __launch_bounds__(NW * 64, 2) void k_bwd_keys(
     const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ Ysrc, const T* __restrict__ Zsrc,
-    const float* __restrict__ Lv, const float* __restrict__ Dv, const int32_t* __restrict__ topk,
-    const WorkItem* __restrict__ wl2, const int* __restrict__ wl2_count, float* __restrict__ G,
-    const int* __restrict__ icnt, const int* __restrict__ ipos, T* __restrict__ dK, T* __restrict__ dV, int N,
-    int m, int k, int nent, int BH, int UB2, float cscale, float cnat) {
+    const float* __restrict__ Lv, const float* __restrict__ Dv, const int32_t* __restrict__ qperm,
+    const int32_t* __restrict__ topk, const WorkItem* __restrict__ wl2, const int* __restrict__ wl2_count,
+    float* __restrict__ G, const int* __restrict__ icnt, const int* __restrict__ ipos, T* __restrict__ dK,
+    T* __restrict__ dV, int N, int m, int k, int nent, int BH, int UB2, float cscale, float cnat) {
   constexpr int NT = NW * 64;
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, li = lane % 16, lg = lane / 16;
@@ -409,10 +463,19 @@ __global__ __launch_bounds__(NW * 64, 2) void k_bwd_keys(
   zero_acc<IB, D>(ax);
   zero_acc<IB, D>(aw);
   if constexpr (ROUTED) {
-    // the slot's queries gathered in expert order (q, dO, lse, dO . o)
     const size_t so = (size_t)slot * BH * N;
-    const SrcRows<T, D> src{Ysrc + so * D, Zsrc + so * D, Lv + so, Dv + so, start, start + cnt, cscale, cnat};
-    grad_stream<IB, false, true, true, NT, T, D>(smem, (cnt + 31) / 32, src, xf, wf, Lr, Dr, ax, aw, li, lg);
+    if constexpr (sizeof(T) == 2) {
+      // the item's queries read through the slot's expert-order permutation
+      // (q, dO, lse and dO . o in query order)
+      const size_t hb = (size_t)bh * N;
+      const SrcPerm<T, D> src{Ysrc + hb * D, Zsrc + hb * D, Lv + hb, Dv + hb, qperm + so, start, start + cnt, N,
+                              cscale, cnat};
+      grad_stream<IB, false, true, true, NT, T, D>(smem, (cnt + 31) / 32, src, xf, wf, Lr, Dr, ax, aw, li, lg);
+    } else {
+      // the slot's queries gathered in expert order (q, dO, lse, dO . o)
+      const SrcRows<T, D> src{Ysrc + so * D, Zsrc + so * D, Lv + so, Dv + so, start, start + cnt, cscale, cnat};
+      grad_stream<IB, false, true, true, NT, T, D>(smem, (cnt + 31) / 32, src, xf, wf, Lr, Dr, ax, aw, li, lg);
+    }
 #pragma unroll
     for (int b = 0; b < IB; ++b) {
       const int r = r0 + b * 16 + li;
@@ -551,6 +614,35 @@ __global__ __launch_bounds__(NW * 64, 2) void k_bwd_keys_res(
         }
     }
   }
+}
+
+// delta = dO . o per query, in query order, from the forward's fp32 output
+// (so that it equals sum_t P_t dP_t up to fp32 rounding even where one entry
+// dominates and dP_t - delta cancels).  CPR lanes per row.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_bwd_delta(const T* __restrict__ dO, const float* __restrict__ O32,
+                                                   float* __restrict__ Dn, long long rows) {
+  constexpr int EPC = 16 / (int)sizeof(T), CPR = D / EPC;
+  const long long g = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long pos = g / CPR;
+  const int c = (int)(g % CPR);
+  float acc = 0.f;
+  if (pos < rows) {
+    const uint4 gv = *(const uint4*)(dO + pos * D + c * EPC);
+    const T* pg = (const T*)&gv;
+    const float4* po = (const float4*)(O32 + pos * D + c * EPC);
+#pragma unroll
+    for (int q = 0; q < EPC / 4; ++q) {
+      const float4 o = po[q];
+      acc = __builtin_fmaf(o.x, to_f32(pg[4 * q]), acc);
+      acc = __builtin_fmaf(o.y, to_f32(pg[4 * q + 1]), acc);
+      acc = __builtin_fmaf(o.z, to_f32(pg[4 * q + 2]), acc);
+      acc = __builtin_fmaf(o.w, to_f32(pg[4 * q + 3]), acc);
+    }
+  }
+#pragma unroll
+  for (int off = CPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (pos < rows && c == 0) Dn[pos] = acc;
 }
 
 // Copies of q, dO, lse and delta = dO . o in each slot's expert order:
@@ -942,9 +1034,14 @@ static void launch_routed_keys(const BPlan& p, size_t lds) {
   auto fn = &k_bwd_keys<T, D, NW, IBK, true>;
   allow_lds(fn, lds);
   dim3 grid((unsigned)(p.s * p.UB2), (unsigned)((p.k + R - 1) / R));
-  hipLaunchKernelGGL(fn, grid, dim3(NW * 64), lds, p.stream, (const T*)p.K, (const T*)p.V, (const T*)p.Qg,
-                     (const T*)p.dOg, p.Lg, p.Dg, p.topk, p.wl2, p.wl2_count, p.G, (const int*)nullptr,
-                     (const int*)nullptr, (T*)nullptr, (T*)nullptr, p.N, p.m, p.k, 0, p.BH, p.UB2, p.cscale, p.cnat);
+  // bf16 reads the queries through the expert-order permutation; fp32 from
+  // copies gathered in that order
+  constexpr bool PERM = sizeof(T) == 2;
+  hipLaunchKernelGGL(fn, grid, dim3(NW * 64), lds, p.stream, (const T*)p.K, (const T*)p.V,
+                     (const T*)(PERM ? p.Q : p.Qg), (const T*)(PERM ? p.dO : p.dOg), PERM ? p.lse : p.Lg,
+                     PERM ? p.Dn : p.Dg, (const int32_t*)p.bk.perm, p.topk, p.wl2, p.wl2_count, p.G,
+                     (const int*)nullptr, (const int*)nullptr, (T*)nullptr, (T*)nullptr, p.N, p.m, p.k, 0, p.BH,
+                     p.UB2, p.cscale, p.cnat);
 }
 
 template <typename T, int D, int NW, int IBL>
@@ -994,9 +1091,15 @@ static void launch_backward_t(const BPlan& p) {
   {
     constexpr int CPR = D * (int)sizeof(T) / 16;
     const long long BHN = (long long)BH * N, rows = (long long)s * BHN;
-    hipLaunchKernelGGL((k_bwd_gather<T, D>), dim3((unsigned)((rows * CPR + 255) / 256)), dim3(256), 0, st,
-                       (const T*)p.Q, (const T*)p.dO, p.o32, p.lse, (const int32_t*)p.bk.perm, (T*)p.Qg, (T*)p.dOg,
-                       p.Lg, p.Dg, p.Dn, N, BHN, rows);
+    if constexpr (sizeof(T) == 2) {
+      // the routed pass reads the queries through the permutation: only delta
+      hipLaunchKernelGGL((k_bwd_delta<T, D>), dim3((unsigned)((BHN * CPR + 255) / 256)), dim3(256), 0, st,
+                         (const T*)p.dO, p.o32, p.Dn, BHN);
+    } else {
+      hipLaunchKernelGGL((k_bwd_gather<T, D>), dim3((unsigned)((rows * CPR + 255) / 256)), dim3(256), 0, st,
+                         (const T*)p.Q, (const T*)p.dO, p.o32, p.lse, (const int32_t*)p.bk.perm, (T*)p.Qg,
+                         (T*)p.dOg, p.Lg, p.Dg, p.Dn, N, BHN, rows);
+    }
     launch_items(p.bk, p.CH, p.UB2, p.wl2, p.wl2_count, p.efirst, p.epart);
     if (sizeof(T) == 2 && stat_blocks(k, IB) == 1) launch_routed_keys<T, D, NW, 1>(p, lds);
     else launch_routed_keys<T, D, NW, IB>(p, lds);
@@ -1047,7 +1150,8 @@ static void launch_backward_t(const BPlan& p) {
     allow_lds(fn, lds);
     dim3 grid((unsigned)((N + R3 - 1) / R3), (unsigned)BH);
     hipLaunchKernelGGL(fn, grid, dim3(NW * 64), lds, st, (const T*)p.K, (const T*)p.V, (const T*)p.qt,
-                       (const T*)p.dvtT, p.lse_lm, p.delta, p.topk, (const WorkItem*)nullptr, (const int*)nullptr,
+                       (const T*)p.dvtT, p.lse_lm, p.delta, (const int32_t*)nullptr, p.topk,
+                       (const WorkItem*)nullptr, (const int*)nullptr,
                        p.Gs, (const int*)p.icnt, (const int*)p.ipos, (T*)p.dK, (T*)p.dV, N, m, k,
                        p.shared ? m : 0, BH, p.UB2, p.cscale, p.cnat);
   }
