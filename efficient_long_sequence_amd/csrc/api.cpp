@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 
@@ -90,12 +91,10 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
     const long long est_target = 512;
     int gpb = ceil_div((long long)p.G * p.BH * p.sc_rt, est_target);
     p.est_gpb = gpb < 1 ? 1 : gpb;
-    // staged candidates per workgroup (split evenly over its waves): the
-    // threshold admits about 2.5 k keys per row; room for three times that
-    const double expect = (double)p.sc_R * p.L * (2.5 * k / N);
-    int cb = 256;
-    while (cb < 3.0 * expect && cb < 16384) cb <<= 1;
-    p.cb = cb;
+    // records per (row, chunk, lane group): a lane keeps at most one per
+    // 32-key step of its chunk
+    const int steps = ceil_div(p.L, 32);
+    p.s4 = steps < REC_MAX ? steps : REC_MAX;
     // Test hook (host-forced): MITA_TEST_FORCE_FALLBACK=1 sets every candidate
     // threshold to +inf, so no row collects candidates and every row is
     // selected by the exact fallback kernel instead.
@@ -149,9 +148,12 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
   p.tau = (float*)take(Mr * 4);
   p.mhat = (float*)take(Mr * 4);
   p.vpart = (float*)take(Mr * p.C * (d + 4) * 4);
-  p.cand = (uint64_t*)take(Mr * p.capg * 8);
+  p.cand = (uint64_t*)take(p.dense ? Mr * p.capg * 8 : 0);
+  const size_t nseg = p.dense ? 0 : Mr * p.C * 4;
+  p.rec_sc = (float*)take(nseg * p.s4 * 8 * 4);
+  p.rec_st = (int32_t*)take(nseg * p.s4 * 4);
+  p.rec_cnt = (int*)take(nseg * 4);
   const size_t zoff = off;
-  p.cand_cnt = (int*)take(Mr * 4);
   p.counts = (int*)take((size_t)s * Mr * 4);
   p.cursor = (int*)take((size_t)s * Mr * 4);
   p.zero_begin = base ? base + zoff : nullptr;
@@ -166,7 +168,7 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
   p.wl = (WorkItem*)take((size_t)s * p.UB * sizeof(WorkItem));
   p.wl_count = (int*)take(MAX_S * 4);
   p.part = (float*)take(!p.fast && s > 1 ? (size_t)(s - 1) * BH * N * (d + 4) * 4 : 0);
-  p.plse = (float*)take(p.fast ? BH * N * 4 : 0);
+  p.plse = (float2*)take(p.fast ? BH * N * 8 : 0);
   p.po = take(p.fast ? BH * N * d * (p.dtype ? 2 : 4) : 0);  // fp16 / fp32
   p.total_bytes = off;
   return p;
@@ -194,7 +196,16 @@ struct Timer {
   }
   void end(int stage) const {
     if (ev && ev[2 * stage + 1]) (void)hipEventRecord((hipEvent_t)ev[2 * stage + 1], st);
+    // Diagnostics (host-set MITA_DEBUG_SYNC): name each stage whose launches
+    // reported an error; with 1 also wait for the stage to finish.
+    if (debug_sync) {
+      const hipError_t e1 = hipGetLastError();
+      const hipError_t e2 = debug_sync == 1 ? hipStreamSynchronize(st) : hipSuccess;
+      if (e1 != hipSuccess || e2 != hipSuccess)
+        std::fprintf(stderr, "mita: stage %d: %s\n", stage, hipGetErrorString(e1 != hipSuccess ? e1 : e2));
+    }
   }
+  int debug_sync = 0;
 };
 
 mita_status run(const void* Q, const void* K, const void* V, void* O, mita_dtype dtype, int B, int H, int N,
@@ -218,7 +229,11 @@ mita_status run(const void* Q, const void* K, const void* V, void* O, mita_dtype
     p.lse_lm = p.shared ? sv->lse_landmark : nullptr;
     p.o32 = sv->out_f32;
   }
-  const Timer tm{events, p.stream};
+  Timer tm{events, p.stream};
+  {
+    const char* ds = std::getenv("MITA_DEBUG_SYNC");
+    tm.debug_sync = ds == nullptr ? 0 : ds[0] == '1' ? 1 : ds[0] == '2' ? 2 : 0;
+  }
 
   (void)hipGetLastError();  // clear any earlier sticky launch error
   tm.begin(ST_POOL);

@@ -11,9 +11,12 @@ namespace mita {
 // Rows of N up to this size keep every landmark score as a candidate ("dense"
 // selection); above it a sampled threshold filters candidates first.
 constexpr int NSMALL = 8192;
-// Candidate capacity per landmark row in sparse mode; also the largest block
-// sort in the selection kernel (8192 x 8 bytes of LDS).
+// Candidate capacity per landmark row in sparse mode: the selection kernel
+// gathers a row's candidates into LDS (8192 x 8 bytes).
 constexpr int CAPG = 8192;
+// Sparse mode: score records a lane may keep per (landmark row, key chunk,
+// lane group); a lane that needs more marks its row for the exact fallback.
+constexpr int REC_MAX = 32;
 constexpr int MAX_S = 8;
 constexpr int MAX_M = 4096;
 constexpr int MAX_K_SPARSE = 2048;
@@ -44,7 +47,7 @@ struct Plan {
   int capg;       // candidate slots per landmark row
   int sc_nw, sc_ib, sc_R, sc_rt;  // waves, 16-row blocks per wave, rows per tile, row tiles
   int L, C;       // keys per chunk, chunks per head
-  int cb;         // LDS candidate staging entries per workgroup
+  int s4;         // sparse mode: records per (row, chunk, lane group)
   // threshold estimate (sparse mode)
   int sigma;      // sample stride
   int NS;         // samples per head
@@ -69,8 +72,10 @@ struct Plan {
   float* tau;       // [BH, m] raw-score threshold
   float* mhat;      // [BH, m] sample maximum (raw)
   float* vpart;     // [BH, m, C, d + 4]: max, normaliser, 2 pad, d sums
-  uint64_t* cand;   // [BH, m, capg]
-  int* cand_cnt;    // [BH, m]           (zeroed each call)
+  uint64_t* cand;   // [BH, m, capg]     (dense mode: every score as a candidate key)
+  float* rec_sc;    // [BH, m, C, 4, s4, 8] sparse mode: the 8 raw scores of a lane step holding a candidate
+  int32_t* rec_st;  // [BH, m, C, 4, s4]    its step inside the chunk
+  int* rec_cnt;     // [BH, m, C, 4]        records the lane found (may exceed s4: the row falls back)
   int* counts;      // [s, BH, m]        (zeroed each call)
   int* cursor;      // [s, BH, m]        (zeroed each call)
   int* fail;        // [BH, m]
@@ -83,8 +88,9 @@ struct Plan {
   WorkItem* wl;     // [s, UB]
   int* wl_count;    // [s]
   float* part;      // [s - 1, BH, N, d + 4]  (streaming path)
-  float* plse;      // [BH, N] log2-sum-exp of the finished part (resident path)
-  void* po;         // [BH, N, d] normalised output of the finished part (fp16; fp32 for fp32 inputs)
+  float2* plse;     // [BH, N] (log2-sum-exp, row scale) of the finished part (resident path)
+  void* po;         // [BH, N, d] output of the finished part divided by its row scale (fp16, |x| <= 1;
+                    // fp32 with scale 1 for fp32 inputs)
   void* zero_begin;
   size_t zero_bytes;
   size_t total_bytes;

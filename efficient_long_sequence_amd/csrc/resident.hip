@@ -14,8 +14,10 @@
 //                   by 1/sqrt(d), are the shared logits of the joint softmax
 //                   (the reuse the tutorial's cost count of ch.6 assumes), so
 //                   the shared part of the output is finished here and stored
-//                   as a partial: log2-sum-exp and the normalised output
-//                   (fp16).
+//                   as a partial: log2-sum-exp, and the output row divided by
+//                   its largest magnitude (fp16, so every stored element lies
+//                   in [-1, 1] whatever the scale of V) with that magnitude
+//                   kept in fp32.
 //   k_expert        per (expert, range of its queries): the expert's k
 //                   gathered key/value rows staged once, the routed logits
 //                   and values on the matrix cores, then the merge with the
@@ -31,9 +33,35 @@ namespace mita {
 typedef _Float16 f16;
 
 // Storage type of the finished-part output between kernels: fp16 for bf16
-// inputs (a smaller rounding than the bf16 output itself), fp32 for fp32.
+// inputs, fp32 for fp32.  An fp16 row is stored divided by its largest
+// magnitude (a per-query fp32 scale kept beside it), so it never overflows
+// and its rounding is at most 2^-11 of the row's largest element, below the
+// bf16 rounding of the output itself; fp32 rows are stored as they are
+// (scale 1).
 template <typename T> struct PartT { typedef f16 type; };
 template <> struct PartT<float> { typedef float type; };
+
+// The per-query scale of a row of 16 values per lane (the four lane groups of
+// a query hold its d = 64 outputs): 1 / max|x| for the stored values and
+// max|x| * mul for the fp32 scale.  A row of zeros (or one below 1e-30 in
+// magnitude, whose rounding to zero is far inside any tolerance) gets 0 and 0.
+template <typename P, int NCB>
+__device__ __forceinline__ void row_scale(const f32x4 (&x)[NCB], float mul, float& inv_store, float& scale) {
+  if constexpr (sizeof(P) == 4) {
+    inv_store = 1.0f;
+    scale = mul;
+  } else {
+    float a = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a = fmaxf(a, fabsf(x[cb][r]));
+    a = wave_max_groups(a);
+    const bool nz = a > 1e-30f;
+    inv_store = nz ? 1.0f / a : 0.f;
+    scale = nz ? a * mul : 0.f;
+  }
+}
 
 // Row layout of the finished-part output: lane group g of a query holds
 // output dims cb*16 + 4g + r (cb < D/16, r < 4) in its accumulator tiles, and
@@ -170,7 +198,7 @@ __device__ __forceinline__ void list_insert(float* lv, int* lx, float v, int i) 
 template <typename T, int D, int NW, int SMAX>
 __global__ __launch_bounds__(NW * 64) void k_route_shared(
     const T* __restrict__ Q, const T* __restrict__ Qt, const T* __restrict__ VtT, int32_t* __restrict__ route,
-    int* __restrict__ counts, float* __restrict__ plse, typename PartT<T>::type* __restrict__ po, int N, int m, int s,
+    int* __restrict__ counts, float2* __restrict__ plse, typename PartT<T>::type* __restrict__ po, int N, int m, int s,
     int BH, int qpw, int hist_lds, float cscale) {  // cscale: log2(e) x the shared-logit scale
   using RL = Resident<T, D>;
   using P = typename PartT<T>::type;
@@ -265,6 +293,9 @@ __global__ __launch_bounds__(NW * 64) void k_route_shared(
       const int n = qb + b * 16 + li;
       if (n >= q1) continue;
       const size_t qrow = (size_t)bh * N + n;
+      // the stored row: acc / max|acc|; its scale: max|acc| / Z
+      float sn, scl;
+      row_scale<P, D / 16>(acc[b], 1.0f / Zt, sn, scl);
       if (lg == 0) {
         int32_t* dst = route + qrow * s;
 #pragma unroll
@@ -278,15 +309,14 @@ __global__ __launch_bounds__(NW * 64) void k_route_shared(
             else atomicAdd(counts + ((size_t)t * BH + bh) * m + e, 1);
           }
         }
-        plse[qrow] = M[b].M + __builtin_amdgcn_logf(Zt);
+        plse[qrow] = make_float2(M[b].M + __builtin_amdgcn_logf(Zt), scl);
       }
-      const float inv = 1.0f / Zt;
       P* o = po + qrow * D;
 #pragma unroll
       for (int cb = 0; cb < D / 16; ++cb) {
         PV h;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) h[r] = (P)(acc[b][cb][r] * inv);
+        for (int r = 0; r < 4; ++r) h[r] = (P)(acc[b][cb][r] * sn);
         *(PV*)(o + part_pos<D>(lg, cb)) = h;
       }
     }
@@ -307,7 +337,7 @@ __global__ __launch_bounds__(NW * 64) void k_route_shared(
 template <int IB, typename T, int D>
 __device__ __forceinline__ void expert_group(const Frag<T> (&qf)[IB][D / 32], const int (&qn)[IB], const T* Ks,
                                              const T* Vs, int Kp, int k, const Frag<T>& one, size_t row0,
-                                             float* __restrict__ plse, typename PartT<T>::type* __restrict__ po,
+                                             float2* __restrict__ plse, typename PartT<T>::type* __restrict__ po,
                                              T* __restrict__ O, TrainOut tr, int merge_in, int last, float cscale, int li,
                                              int lg) {
   using RL = Resident<T, D>;
@@ -340,47 +370,55 @@ __device__ __forceinline__ void expert_group(const Frag<T> (&qf)[IB][D / 32], co
     if (qn[b] < 0) continue;
     const size_t qrow = row0 + qn[b];
     // merge with the stored partial (none before the first routed slot of
-    // the routing-only variant): weights 2^lse of the two parts
-    const float la = merge_in ? plse[qrow] : M0;
+    // the routing-only variant): weights 2^lse of the two parts; the stored
+    // row comes back multiplied by its scale
+    const float2 pl = merge_in ? plse[qrow] : make_float2(M0, 0.f);
+    const float la = pl.x;
     const float lb = M[b].M + __builtin_amdgcn_logf(Zt);
     const float mx = fmaxf(la, lb);
     const float wa = __builtin_amdgcn_exp2f(la - mx), wb = __builtin_amdgcn_exp2f(lb - mx);
     const float den = wa + wb;
-    const float ca = wa / den, cb_ = wb / (den * Zt);
+    const float ca = wa / den * pl.y, cb_ = wb / (den * Zt);
     P* o = po + qrow * D;
+    f32x4 v[D / 16];
 #pragma unroll
     for (int cb = 0; cb < D / 16; ++cb) {
       PV h = PV{};
       if (merge_in) h = *(const PV*)(o + part_pos<D>(lg, cb));
-      float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = ca * (float)h[r] + cb_ * acc[b][cb][r];
-      if (last) {
+      for (int r = 0; r < 4; ++r) v[cb][r] = ca * (float)h[r] + cb_ * acc[b][cb][r];
+    }
+    // the log2-sum-exp of everything merged so far: the next slot's input,
+    // or after the last slot the query's whole normaliser (kept for the
+    // backward pass when requested)
+    const float lse = mx + __builtin_amdgcn_logf(den);
+    if (last) {
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb) {
         T* dst = O + qrow * D + cb * 16 + 4 * lg;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dst[r] = from_f32<T>(v[r]);
-        if (tr.o32) *(float4*)(tr.o32 + qrow * D + cb * 16 + 4 * lg) = make_float4(v[0], v[1], v[2], v[3]);
-      } else {
+        for (int r = 0; r < 4; ++r) dst[r] = from_f32<T>(v[cb][r]);
+        if (tr.o32) *(float4*)(tr.o32 + qrow * D + cb * 16 + 4 * lg) = make_float4(v[cb][0], v[cb][1], v[cb][2], v[cb][3]);
+      }
+      if (lg == 0 && tr.lse) tr.lse[qrow] = lse;
+    } else {
+      float sn, scl;
+      row_scale<P, D / 16>(v, 1.0f, sn, scl);
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb) {
         PV w;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = (P)v[r];
+        for (int r = 0; r < 4; ++r) w[r] = (P)(v[cb][r] * sn);
         *(PV*)(o + part_pos<D>(lg, cb)) = w;
       }
-    }
-    if (lg == 0) {
-      // the log2-sum-exp of everything merged so far: the next slot's input,
-      // or after the last slot the query's whole normaliser (kept for the
-      // backward pass when requested)
-      const float lse = mx + __builtin_amdgcn_logf(den);
-      if (!last) plse[qrow] = lse;
-      else if (tr.lse) tr.lse[qrow] = lse;
+      if (lg == 0) plse[qrow] = make_float2(lse, scl);
     }
   }
 }
 
 template <int IBX, typename T, int D, class QR>
 __device__ __forceinline__ void expert_blocks(const T* Qh, QR qrow, const T* Ks, const T* Vs, int Kp, int k,
-                                              const Frag<T>& one, size_t row0, float* plse,
+                                              const Frag<T>& one, size_t row0, float2* plse,
                                               typename PartT<T>::type* po, T* O, TrainOut tr, int merge_in, int last,
                                               float cscale, int li, int lg) {
   Frag<T> qf[IBX][D / 32];
@@ -395,7 +433,7 @@ template <typename T, int D, int NW, int IB>
 __global__ __launch_bounds__(NW * 64, 2) void k_expert(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const int32_t* __restrict__ topk,
     const int32_t* __restrict__ perm, const WorkItem* __restrict__ wl, const int* __restrict__ wl_count,
-    float* __restrict__ plse, typename PartT<T>::type* __restrict__ po, T* __restrict__ O, TrainOut tr, int N, int m, int k,
+    float2* __restrict__ plse, typename PartT<T>::type* __restrict__ po, T* __restrict__ O, TrainOut tr, int N, int m, int k,
     int merge_in, int last, float cscale) {
   using RL = Resident<T, D>;
   extern __shared__ __align__(16) unsigned char smem[];

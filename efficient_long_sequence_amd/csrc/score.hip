@@ -27,6 +27,8 @@
 // at least k of them, the k largest candidates (ties to the lower index) are
 // the k largest keys of the whole row; otherwise the row is redone by
 // k_fallback.  tau only decides how much work this takes, never the result.
+#include <algorithm>
+
 #include "mita_dev.h"
 #include "mita_plan.h"
 #include "tile.h"
@@ -139,18 +141,14 @@ template <typename T, int D, int NW, int IB, bool DENSE, bool SHARED>
 __global__ __launch_bounds__(NW * 64, (score_waves_per_eu<T, NW, IB>())) void k_score(
     const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ Qt,
     const float* __restrict__ tau_in, const float* __restrict__ mhat_in, float* __restrict__ vpart,
-    uint64_t* __restrict__ cand, int* __restrict__ cand_cnt, int N, int m, int L, int C, int capg,
-    int cb_cap, float cscale) {
+    uint64_t* __restrict__ cand, float* __restrict__ rec_sc, int32_t* __restrict__ rec_st,
+    int* __restrict__ rec_cnt, int N, int m, int L, int C, int capg, int s4, float cscale) {
   constexpr int NT = NW * 64;
   constexpr int R = NW * 16 * IB;
   using TL = TileLayout<T, D>;
   extern __shared__ __align__(16) unsigned char smem[];
   T* buf0 = (T*)smem;
   T* buf1 = buf0 + TL::ELEMS;
-  uint2* s_cand = (uint2*)(smem + 2 * TL::ELEMS * sizeof(T));
-  int* s_rowcnt = (int*)(s_cand + cb_cap);
-  int* s_rowbase = s_rowcnt + R;
-  int* s_wcnt = s_rowbase + R;  // staged entries per wave
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, li = lane % 16, lg = lane / 16;
   const Frag<T> one = ones_frag<T>(li);
@@ -159,15 +157,11 @@ __global__ __launch_bounds__(NW * 64, (score_waves_per_eu<T, NW, IB>())) void k_
   const T* Kh = K + (size_t)bh * N * D;
   const T* Vh = V + (size_t)bh * N * D;
   const int j_begin = ch * L, j_end = min(N, j_begin + L);
-  // each wave stages its candidates in its own LDS segment, counted in a
-  // wave-uniform register, so no LDS atomics sit on the inner loop
-  const int seg = cb_cap / NW;
-  uint2* w_cand = s_cand + wave * seg;
-  int wcnt = 0;
-
-  if constexpr (!DENSE) {
-    for (int r = tid; r < R; r += NT) s_rowcnt[r] = 0;
-  }
+  // sparse mode: every lane appends its own records (no cross-lane work on
+  // the inner loop); rcnt[b] counts those of block b
+  int rcnt[IB];
+#pragma unroll
+  for (int b = 0; b < IB; ++b) rcnt[b] = 0;
 
   Frag<T> qf[IB][D / 32];
   float tau[IB];
@@ -217,7 +211,8 @@ __global__ __launch_bounds__(NW * 64, (score_waves_per_eu<T, NW, IB>())) void k_
     if constexpr (SHARED) f.load_vals(cur + TL::K_ELEMS, li, lg);
     const int nv = min(32, j_end - j0);
     // per row block: every score of a small head is a candidate (DENSE);
-    // otherwise the scores >= tau are staged, one LDS reservation per lane
+    // otherwise a lane holding a score >= tau keeps a record: its 8 raw
+    // scores and the step (the selection filters them against tau)
     auto cands = [&](int b, const float* sc, float mx) {
       const int row = rbase + b * 16 + li;
       if constexpr (DENSE) {
@@ -230,31 +225,18 @@ __global__ __launch_bounds__(NW * 64, (score_waves_per_eu<T, NW, IB>())) void k_
           }
         }
       } else if (wave_any(mx >= tau[b])) {
-        // one ballot per key slot: the hits of a slot take the next entries
-        // of the wave's segment in lane order, and each hit's score comes
-        // straight from its register
-        const uint32_t rl = (uint32_t)(row - rt * R) << 23;
-        const float tb = tau[b];
-        int off = wcnt;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const bool hit = sc[t] >= tb;
-          const uint64_t bal = __builtin_amdgcn_ballot_w64(hit);
-          if (bal == 0) continue;
-          if (hit) {
-            const int e = off + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-            const int jl = j0 + slot_key(t, lg) - j_begin;
-            if (e < seg) {
-              w_cand[e] = make_uint2(__float_as_uint(sc[t]), rl | (uint32_t)jl);
-            } else {
-              const int pos = atomicAdd(cand_cnt + (size_t)bh * m + row, 1);
-              if (pos < capg) cand[((size_t)bh * m + row) * capg + pos] = ckey(sc[t], (uint32_t)(j_begin + jl));
-            }
+        // (rows past m have tau = +inf and never get here)
+        if (mx >= tau[b]) {
+          const int c = rcnt[b];
+          if (c < s4) {
+            const size_t e = ((((size_t)bh * m + row) * C + ch) * 4 + lg) * s4 + c;
+            float4* dst = (float4*)(rec_sc + e * 8);
+            dst[0] = make_float4(sc[0], sc[1], sc[2], sc[3]);
+            dst[1] = make_float4(sc[4], sc[5], sc[6], sc[7]);
+            rec_st[e] = st;
           }
-          off += (int)__builtin_popcountll(bal);
+          rcnt[b] = c + 1;
         }
-        wcnt = off;
       }
     };
     if constexpr (SHARED) attn_step<IB, MASKED>(f, one, qf, nv, lg, cscale, M, Z, acc, cands);
@@ -284,26 +266,10 @@ __global__ __launch_bounds__(NW * 64, (score_waves_per_eu<T, NW, IB>())) void k_
   }
 
   if constexpr (!DENSE) {
-    if (lane == 0) s_wcnt[wave] = min(wcnt, seg);
-    __syncthreads();
-    const int ns = NW * seg;
-    auto staged = [&](int e) { return e - (e / seg) * seg < s_wcnt[e / seg]; };
-    for (int e = tid; e < ns; e += NT)
-      if (staged(e)) atomicAdd(s_rowcnt + (s_cand[e].y >> 23), 1);
-    __syncthreads();
-    for (int r = tid; r < R; r += NT) {
-      const int row = rt * R + r, c = s_rowcnt[r];
-      s_rowbase[r] = (c > 0 && row < m) ? atomicAdd(cand_cnt + (size_t)bh * m + row, c) : 0;
-      s_rowcnt[r] = 0;
-    }
-    __syncthreads();
-    for (int e = tid; e < ns; e += NT) {
-      if (!staged(e)) continue;
-      const uint2 v = s_cand[e];
-      const int r = (int)(v.y >> 23), row = rt * R + r;
-      const int pos = s_rowbase[r] + atomicAdd(s_rowcnt + r, 1);
-      if (pos < capg)
-        cand[((size_t)bh * m + row) * capg + pos] = ckey(__uint_as_float(v.x), (uint32_t)(j_begin + (int)(v.y & 0x7FFFFFu)));
+#pragma unroll
+    for (int b = 0; b < IB; ++b) {
+      const int row = rbase + b * 16 + li;
+      if (row < m) rec_cnt[(((size_t)bh * m + row) * C + ch) * 4 + lg] = rcnt[b];
     }
   }
 }
@@ -324,10 +290,11 @@ __device__ void emit_topk(uint64_t* a, int k, int32_t* out) {
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_final(const float* __restrict__ vpart, const uint64_t* __restrict__ cand,
-                                               const int* __restrict__ cand_cnt, int32_t* __restrict__ topk,
-                                               float* __restrict__ vt32, T* __restrict__ vtT, int* __restrict__ fail,
-                                               float* __restrict__ lse_lm, int N, int k, int C, int capg, int dense,
-                                               int shared) {
+                                               const float* __restrict__ rec_sc, const int32_t* __restrict__ rec_st,
+                                               const int* __restrict__ rec_cnt, const float* __restrict__ tau,
+                                               int32_t* __restrict__ topk, float* __restrict__ vt32,
+                                               T* __restrict__ vtT, int* __restrict__ fail, float* __restrict__ lse_lm,
+                                               int N, int k, int C, int L, int capg, int s4, int dense, int shared) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint64_t* a = (uint64_t*)smem;
   __shared__ float red[256];
@@ -371,14 +338,108 @@ __global__ __launch_bounds__(256) void k_final(const float* __restrict__ vpart, 
       vtT[r * D + tid] = from_f32<T>(v);
     }
   }
-  const int cnt = dense ? N : cand_cnt[r];
+  __shared__ int s_over;
+  int cnt;
+  if (dense) {
+    cnt = N;
+    const uint64_t* src = cand + r * capg;
+    for (int j = tid; j < cnt; j += 256) a[j] = src[j];
+  } else {
+    // gather the row's candidates from its records: every recorded score
+    // >= tau.  The record counts of its (chunk, lane group) segments are
+    // staged and prefix-summed in LDS; then each thread takes records
+    // tid, tid + 256, ... of the row (its segment found by binary search),
+    // and each wave reserves its hits' slots with one LDS atomic.
+    int* s_pre = (int*)(a + capg);  // nseg + 1 prefix entries (reused by the selection later)
+    __shared__ int s_wt[4], s_fill;
+    if (tid == 0) { s_over = 0; s_fill = 0; }
+    __syncthreads();
+    const int nseg = 4 * C;
+    const size_t seg0 = r * (size_t)nseg;
+    // per-thread runs of consecutive segments, then a block scan of the run sums
+    const int per = (nseg + 255) / 256;
+    const int x0 = min(nseg, tid * per), x1 = min(nseg, x0 + per);
+    int run = 0, over = 0;
+    for (int x = x0; x < x1; ++x) {
+      const int n = rec_cnt[seg0 + x];
+      over |= n > s4;
+      const int c = min(n, s4);
+      s_pre[x] = c;
+      run += c;
+    }
+    int incl = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if ((tid & 63) >= off) incl += y;
+    }
+    if ((tid & 63) == 63) s_wt[tid >> 6] = incl;
+    if (wave_any(over != 0) && (tid & 63) == 0) s_over = 1;
+    __syncthreads();
+    int acc_ = incl - run;
+    for (int w = 0; w < (tid >> 6); ++w) acc_ += s_wt[w];
+    for (int x = x0; x < x1; ++x) {
+      const int c = s_pre[x];
+      s_pre[x] = acc_;
+      acc_ += c;
+    }
+    const int total_rec = s_wt[0] + s_wt[1] + s_wt[2] + s_wt[3];
+    if (tid == 0) s_pre[nseg] = total_rec;
+    __syncthreads();
+    const float tr = tau[r];
+    for (int q0 = 0; q0 < total_rec; q0 += 256) {
+      const int q = q0 + tid;
+      int h = 0;
+      float v[8];
+      int j0 = 0, lgq = 0;
+      if (q < total_rec) {
+        // last segment whose start is <= q
+        int lo = 0, hi = nseg;  // s_pre[lo] <= q < s_pre[hi]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (s_pre[mid] <= q) lo = mid; else hi = mid;
+        }
+        const size_t e = (seg0 + lo) * s4 + (q - s_pre[lo]);
+        const float4 a0 = ((const float4*)(rec_sc + e * 8))[0];
+        const float4 a1 = ((const float4*)(rec_sc + e * 8))[1];
+        v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
+        v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
+        j0 = (lo >> 2) * L + rec_st[e] * 32;
+        lgq = lo & 3;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) h += v[t] >= tr;
+      }
+      // wave prefix of the hit counts, one LDS reservation per wave
+      int hi_ = h;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(hi_, off);
+        if ((tid & 63) >= off) hi_ += y;
+      }
+      int wbase = 0;
+      if ((tid & 63) == 63) wbase = atomicAdd(&s_fill, hi_);
+      wbase = __shfl(wbase, 63);
+      int pos = wbase + hi_ - h;
+      if (h) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          if (v[t] >= tr) {
+            if (pos < capg) a[pos] = ckey(v[t], (uint32_t)(j0 + slot_key(t, lgq)));
+            ++pos;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    const int total = s_fill;
+    cnt = s_over ? -1 : total;
+  }
   if (cnt < k || cnt > capg) {
     if (tid == 0) fail[r] = 1;
     return;
   }
   if (tid == 0) fail[r] = 0;
-  const uint64_t* src = cand + r * capg;
-  for (int j = tid; j < cnt; j += 256) a[j] = src[j];
+  __syncthreads();
   // radix select of the k-th largest key, 8 bits a pass from the top; the
   // keys are distinct, so exactly k of them reach the final prefix
   __shared__ int hist[256];
@@ -502,20 +563,17 @@ static void launch_score_s(const Plan& p) {
   using TL = TileLayout<T, D>;
   constexpr int R = NW * 16 * IB;
   const bool dense = p.dense != 0;
-  const size_t lds = 2 * TL::ELEMS * sizeof(T) + (dense ? 0 : (size_t)p.cb * 8 + 2 * R * 4 + NW * 4);
+  const size_t lds = 2 * TL::ELEMS * sizeof(T);
   dim3 grid((unsigned)p.C, (unsigned)p.sc_rt, (unsigned)p.BH);
   if (dense) {
     hipLaunchKernelGGL((k_score<T, D, NW, IB, true, SHARED>), grid, dim3(NW * 64), lds, p.stream, (const T*)p.K,
-                       (const T*)p.V, (const T*)p.qt, nullptr, nullptr, p.vpart, p.cand, p.cand_cnt, p.N, p.m, p.L,
-                       p.C, p.capg, 0, p.cscale);
+                       (const T*)p.V, (const T*)p.qt, nullptr, nullptr, p.vpart, p.cand, nullptr, nullptr, nullptr,
+                       p.N, p.m, p.L, p.C, p.capg, 0, p.cscale);
     return;
   }
-  if (lds > 65536)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_score<T, D, NW, IB, false, SHARED>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   hipLaunchKernelGGL((k_score<T, D, NW, IB, false, SHARED>), grid, dim3(NW * 64), lds, p.stream, (const T*)p.K,
-                     (const T*)p.V, (const T*)p.qt, p.tau, p.force_fallback ? nullptr : p.mhat, p.vpart, p.cand,
-                     p.cand_cnt, p.N, p.m, p.L, p.C, p.capg, p.cb, p.cscale);
+                     (const T*)p.V, (const T*)p.qt, p.tau, p.force_fallback ? nullptr : p.mhat, p.vpart, nullptr,
+                     p.rec_sc, p.rec_st, p.rec_cnt, p.N, p.m, p.L, p.C, p.capg, p.s4, p.cscale);
 }
 
 template <typename T, int D, int NW, int IB>
@@ -526,12 +584,16 @@ static void launch_score_main(const Plan& p) {
 
 template <typename T, int D>
 static void launch_final_t(const Plan& p) {
-  const size_t lds = ((size_t)p.capg + next_pow2(p.k < 2 ? 2 : p.k)) * 8;
+  // candidates, then the selected keys (or, before the selection, the
+  // per-segment record counts of a sparse row)
+  const size_t sel = (size_t)next_pow2(p.k < 2 ? 2 : p.k) * 8;
+  const size_t lds = (size_t)p.capg * 8 + (p.dense ? sel : std::max(sel, ((size_t)4 * p.C + 1) * 4));
   if (lds > 65536)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_final<T, D>), hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)lds);
   hipLaunchKernelGGL((k_final<T, D>), dim3((unsigned)(p.BH * p.m)), dim3(256), lds, p.stream, p.vpart, p.cand,
-                     p.cand_cnt, p.topk, p.vt32, (T*)p.vtT, p.fail, p.lse_lm, p.N, p.k, p.C, p.capg, p.dense, p.shared);
+                     p.rec_sc, p.rec_st, p.rec_cnt, p.tau, p.topk, p.vt32, (T*)p.vtT, p.fail, p.lse_lm, p.N, p.k,
+                     p.C, p.L, p.capg, p.s4, p.dense, p.shared);
   if (!p.dense) {
     const size_t lds2 = (size_t)next_pow2(2 * p.k + 256) * 8;
     hipLaunchKernelGGL((k_fallback<T, D>), dim3((unsigned)(p.BH * p.m)), dim3(256), lds2, p.stream,
