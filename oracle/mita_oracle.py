@@ -251,8 +251,7 @@ def route(Q: np.ndarray, Qt: np.ndarray, s: int, counter: DotCounter | None = No
     Tutorial ch.4 step 4: compare q . q~_i and keep the top-s landmarks; the
     score only selects (no gate weights the experts' outputs).  Order: score
     descending, then landmark index ascending.  Also returns the unscaled
-    scores R [N, m] (reused for the shared logits, tutorial ch.6) and the
-    relative gap between the s-th and (s+1)-th scores (None when s = m).
+    scores R [N, m] (reused for the shared logits, tutorial ch.6).
     """
     Q = np.asarray(Q, dtype=np.float64)
     Qt = np.asarray(Qt, dtype=np.float64)
@@ -265,14 +264,7 @@ def route(Q: np.ndarray, Qt: np.ndarray, s: int, counter: DotCounter | None = No
     # a stable sort of -R keeps equal scores in ascending landmark order
     order = np.argsort(-R, axis=1, kind="stable")
     e = order[:, :s].astype(np.int64)
-    gaps = [None] * Q.shape[0]
-    if s < m:
-        rows = np.arange(Q.shape[0])
-        a = R[rows, order[:, s - 1]]
-        b = R[rows, order[:, s]]
-        den = np.maximum(np.maximum(np.abs(a), np.abs(b)), 1e-30)
-        gaps = list((a - b) / den)
-    return e, R, gaps
+    return e, R
 
 
 # ---------------------------------------------------------------------------
@@ -360,7 +352,6 @@ class HeadResult:
     e: np.ndarray
     Vt: np.ndarray
     topk_gaps: list
-    route_gaps: list
     topk_thresholds: np.ndarray
     counter: DotCounter = field(default_factory=DotCounter)
 
@@ -397,6 +388,6 @@ def forward(Q, K, V, grid_h, grid_w, land_h, land_w, k, s, dtype="bf16", row_blo
         tk_gaps += gb
         thr[rows] = tb
         Vt[rows] = shared_values(S, V)
-    e, R, rt_gaps = route(Q, Qt, s, counter=cnt)
+    e, R = route(Q, Qt, s, counter=cnt)
     O = attend(Q, K, V, Qt, Vt, I, e, R=R, counter=cnt, variant=variant)
-    return HeadResult(O, Qt, I, e, Vt, tk_gaps, rt_gaps, thr, cnt)
+    return HeadResult(O, Qt, I, e, Vt, tk_gaps, thr, cnt)

@@ -244,7 +244,7 @@ def test_route_bruteforce_with_ties():
         s = int(rng.integers(1, m + 1))
         Qt = rng.integers(-1, 2, size=(m, 3)).astype(np.float64)
         Q = rng.integers(-1, 2, size=(5, 3)).astype(np.float64)
-        e, R, _ = mo.route(Q, Qt, s)
+        e, R = mo.route(Q, Qt, s)
         for n in range(5):
             r = Q[n] @ Qt.T
             order = sorted(range(m), key=lambda i: (-r[i], i))
