@@ -59,33 +59,42 @@ def sources_sha() -> str:
 
 
 def algorithmic(w, stage: str):
-    """Algorithmic flops and HBM bytes of one launch of a stage's kernel.
+    """Algorithmic flops and compulsory HBM bytes of one launch of a stage's
+    kernel (the method's own work and traffic), and the design-overhead bytes
+    the kernel moves beyond them.
 
     score:  every landmark row against every key: one logit and one value sum
             of length d (4 d N m flops); reads K and V once and Q~, writes v~.
+            Overhead: the split-N partials of v~ (written, then merged).
     route:  every query against every landmark: the routing score, which is
             also the shared logit, and the shared value sum (4 d N m flops);
-            reads Q, Q~, v~, writes the routes and the shared-part partial
-            (fp16 output and log2-sum-exp per query).
+            reads Q, Q~ and v~, writes the routes.  Overhead: the shared part
+            of each query's softmax, handed to the attention kernel (fp16 row
+            and two fp32 per query for bf16 inputs; fp32 row for fp32).
     attend: every query against the k raw entries of each of its s experts
             (4 d N s k flops); reads Q, the m*k gathered key and value rows,
-            the partial, the expert index lists and the permutation, writes O.
+            the expert index lists and the permutation, writes O.  Overhead:
+            the shared part read back (and, for s >= 2, every later slot's
+            partial written and read again).
     """
     es = 2 if w.dtype == "bf16" else 4
-    ps = 2 if w.dtype == "bf16" else 4
+    part = (w.d * 2 + 8) if w.dtype == "bf16" else (w.d * 4 + 8)
     BH, N, d, m, k, s = w.B * w.H, w.N, w.d, w.m, w.k, w.s
     if stage == "score":
         flops = 4.0 * d * N * m * BH
         byts = BH * (2 * N * d * es + m * d * es + m * d * 4)
+        over = 0.0
     elif stage == "route":
         flops = 4.0 * d * N * m * BH
-        byts = BH * (N * d * es + 2 * m * d * es + N * s * 4 + N * (d * ps + 4))
+        byts = BH * (N * d * es + 2 * m * d * es + N * s * 4)
+        over = BH * N * part
     elif stage == "attend":
         flops = 4.0 * d * N * s * k * BH
-        byts = BH * (N * d * es + 2 * m * k * d * es + N * (d * ps + 4) + m * k * 4 + s * N * 4 + N * d * es)
+        byts = BH * (N * d * es + 2 * m * k * d * es + m * k * 4 + s * N * 4 + N * d * es)
+        over = BH * N * part * (1 + 2 * (s - 1))
     else:
-        return None, None
-    return flops, float(byts)
+        return None, None, None
+    return flops, float(byts), float(over)
 
 
 def make_device_inputs(w):
@@ -108,6 +117,8 @@ def time_workload(w, steps: int, warmup: int, variant: str = "paper", k: int | N
     host, (q, kk, v) = make_device_inputs(w) if inputs is None else inputs
     k = w.k if k is None else k
     pool = (w.grid_h, w.grid_w, w.land_h, w.land_w)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
     ws = torch.empty(mita.workspace_bytes(q.dtype, w.B, w.H, w.N, w.d, pool, k, w.s), dtype=torch.uint8,
                      device=q.device)
     out = torch.empty_like(q)
@@ -146,7 +157,10 @@ def time_workload(w, steps: int, warmup: int, variant: str = "paper", k: int | N
     heavy, _ = collect(events)
     # per-call device time (sum of the call's stage event pairs on its stream)
     call_ms = dict(median=float(np.median(per_call)), min=float(np.min(per_call)), max=float(np.max(per_call)))
-    return dict(seconds=dt, ms_per_step=1e3 * dt / steps, tokens_per_s=w.tokens * steps / dt, stages=stages,
+    # device memory of one call: the caller's tensors (Q, K, V, O) and the workspace, and the allocator's peak
+    memory = dict(tensor_bytes=4 * q.numel() * q.element_size(), workspace_bytes=ws.numel(),
+                  peak_allocated_bytes=int(torch.cuda.max_memory_allocated()))
+    return dict(seconds=dt, memory=memory, ms_per_step=1e3 * dt / steps, tokens_per_s=w.tokens * steps / dt, stages=stages,
                 heavy=heavy, call_ms=call_ms, tokens_per_s_median_call=w.tokens / (call_ms["median"] * 1e-3),
                 host=host, q=q, k=kk, v=v, pool=pool, ws=ws)
 
@@ -161,7 +175,7 @@ MEASURED_PEAKS = {}  # filled once per run by mita.probe_peaks()
 
 
 def roofline_of(w, stages: dict, stage: str, traffic):
-    flops, byts = algorithmic(w, stage)
+    flops, byts, over = algorithmic(w, stage)
     sec = stages[stage] * 1e-3
     peak_f = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
@@ -178,7 +192,9 @@ def roofline_of(w, stages: dict, stage: str, traffic):
         r["peak_measured"] = pm
         r["frac_measured"] = r["achieved"] / pm
     r.update(kernel=STAGE_KERNEL[stage], kernel_ms=stages[stage], alg_flops=flops, alg_bytes=byts,
-             hbm_gbs_alg=byts / sec / 1e9, mfma_tflops_alg=flops / sec / 1e12)
+             flop_per_byte=flops / byts, overhead_bytes=over,
+             hbm_gbs_alg=byts / sec / 1e9, mfma_tflops_alg=flops / sec / 1e12,
+             mfma_frac=flops / sec / 1e12 / peak_f, hbm_frac=byts / sec / 1e9 / PEAK_HBM_GBS)
     return r
 
 
@@ -188,7 +204,8 @@ def roofline(w, stages: dict):
     dom = max(heavy, key=lambda s: stages[s])
     r = roofline_of(w, stages, dom, measured_traffic(w, dom))
     r["others"] = {s: {k2: v for k2, v in roofline_of(w, stages, s, measured_traffic(w, s)).items()
-                       if k2 in ("bound", "achieved", "frac", "unit", "kernel", "kernel_ms", "traffic")}
+                       if k2 in ("bound", "achieved", "frac", "unit", "kernel", "kernel_ms", "traffic",
+                                 "mfma_frac", "hbm_frac", "overhead_bytes")}
                    for s in heavy if s != dom}
     return r
 
@@ -339,7 +356,7 @@ def cpu_baseline(w, run):
     t_rows = time.perf_counter() - t0
     qs = np.arange(0, w.N, fq)
     t0 = time.perf_counter()
-    e, R, _ = mo.route(Q[qs], Qt, w.s)
+    e, R = mo.route(Q[qs], Qt, w.s)
     mo.attend(Q[qs], K, V, Qt, Vt_gpu, I_gpu, e, R=R)
     t_query = time.perf_counter() - t0
     est_head = t_pool + t_rows * (w.m / rows.size) + t_query * (w.N / qs.size)
@@ -598,7 +615,7 @@ def main():
             r = time_workload(wo, args.steps, args.warmup)
             others.append(dict(workload=name, tokens_per_s=r["tokens_per_s"], ms_per_step=r["ms_per_step"],
                                call_ms=r["call_ms"], stages_ms=r["stages"], roofline=roofline(wo, r["heavy"]),
-                               tokens_per_s_graph=time_graph(wo, r, args.steps)))
+                               memory=r["memory"], tokens_per_s_graph=time_graph(wo, r, args.steps)))
             del r
             torch.cuda.empty_cache()
     # the same calls replayed from one captured HIP graph (launch cost removed)
@@ -611,6 +628,21 @@ def main():
         except Exception as exc:  # keep the forward line even if this extra measurement fails
             train = dict(error=f"{type(exc).__name__}: {exc}")
         torch.cuda.empty_cache()
+    e2e_pts = abl = None
+    if not args.only:
+        # the pages' end-to-end comparison with dense attention at 16K-256K
+        # (the 1M point, whose dense model forward takes seconds, is left to
+        # --e2e) and the routing-only ablation, beside the forward
+        try:
+            e2e_pts = e2e([p for p in E2E_POINTS if p[0] <= (1 << 18)], reps_mita=3, reps_dense=1)
+        except Exception as exc:
+            e2e_pts = dict(error=f"{type(exc).__name__}: {exc}")
+        torch.cuda.empty_cache()
+        try:
+            abl = ablation(5, 2)
+        except Exception as exc:
+            abl = dict(error=f"{type(exc).__name__}: {exc}")
+        torch.cuda.empty_cache()
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, run)
     line = dict(
         metric=METRIC, value=run["tokens_per_s"], unit="tokens/s", n_gpus=1, steps=args.steps,
@@ -622,8 +654,8 @@ def main():
         roofline=roofline(w, run["heavy"]), cpu_baseline=cpu, stages_ms=run["stages"],
         call_ms=run["call_ms"], tokens_per_s_median_call=run["tokens_per_s_median_call"],
         tokens_per_s_graph=graph_value,
-        measured_peaks=dict(MEASURED_PEAKS),
-        other_workloads=others, training_step=train,
+        measured_peaks=dict(MEASURED_PEAKS), memory=run["memory"],
+        other_workloads=others, training_step=train, end_to_end=e2e_pts, ablation_routing_only=abl,
     )
     print(json.dumps(line), flush=True)
 

@@ -239,10 +239,12 @@ __device__ __forceinline__ float max8(const float* s) {
 }
 
 // One 32-entry step for IB blocks of 16 queries: the score tiles of all
-// blocks first (so one block's softmax overlaps the others' matrix work),
-// then, per block, the hook `on(b, scores, lane_max)` (candidates, routing)
-// and the online-softmax update with P.V.  MASK marks the last, partial step:
-// entries at offsets >= nv get score -inf.
+// blocks first, then the hook `on(b, scores, lane_max)` of each block
+// (candidates, routing), then one check of every block's running maximum
+// (a single, rarely taken branch), and last the exponentials and P.V of all
+// blocks as one branch-free stretch, so the scheduler can overlap one
+// block's vector work with another's matrix work.  MASK marks the last,
+// partial step: entries at offsets >= nv get score -inf.
 template <int IB, bool MASK, typename T, int D, class On>
 __device__ __forceinline__ void attn_step(const StepFrags<T, D>& f, const Frag<T>& one,
                                           const Frag<T> (&qf)[IB][D / 32], int nv, int lg, float cscale,
@@ -257,11 +259,43 @@ __device__ __forceinline__ void attn_step(const StepFrags<T, D>& f, const Frag<T
       for (int t = 0; t < 8; ++t)
         if (slot_key(t, lg) >= nv) sc[b][t] = -INFINITY;
   }
+  float mx[IB];
+  bool up = false;
 #pragma unroll
   for (int b = 0; b < IB; ++b) {
-    const float mx = max8(sc[b]);
-    on(b, sc[b], mx);
-    softmax_step(f, one, sc[b], mx, cscale, M[b], Z[b], acc[b]);
+    mx[b] = max8(sc[b]);
+    on(b, sc[b], mx[b]);
+    up |= mx[b] > M[b].Mt;
+  }
+  if (wave_any(up)) {
+#pragma unroll
+    for (int b = 0; b < IB; ++b) {
+      // the query's own maximum over its four lane groups decides, so each
+      // query's running maximum is independent of the others in the wave
+      const float gm = wave_max_groups(mx[b]);
+      if (gm > M[b].Mt) {
+        const float nm = gm * cscale;
+        const float alpha = __builtin_amdgcn_exp2f(M[b].M - nm);
+        Z[b][0] *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[b][cb][r] *= alpha;
+        M[b].set(nm, cscale);
+      }
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < IB; ++b) {
+    const float nm = -M[b].M;
+    float p[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][t], cscale, nm));
+    Frag<T> pf;
+    set8(pf, p);
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb) mma16(acc[b][cb], f.va[cb], pf);
+    mma16(Z[b], one, pf);
   }
 }
 

@@ -98,6 +98,15 @@ size_t mita_workspace_bytes(mita_dtype dtype, int B, int H, int N, int d, mita_p
  *             16-byte aligned, owned by the caller; contents need not be
  *             initialised and are overwritten
  *   stream    a hipStream_t (NULL = the default stream)
+ * Inputs must be finite (non-finite values give unspecified, memory-safe
+ * results) and every logit of the three softmaxes -- q~_i . k_j, q_n . q~_i
+ * and q_n . k_j, times log2(e) / sqrt(d) -- must stay within 2^30 in
+ * magnitude: each exponent is formed by one fused multiply-add of the fp32
+ * score, whose rounding residual is half a unit in the last place of the
+ * logit (above 2^30 that is more than 2^5, and exp2 can overflow).  Up to
+ * 2^15 the residual is below the bf16 rounding of each probability; between
+ * 2^15 and 2^30 the softmaxes are one-hot to within that residual.  V may use
+ * the whole range of the input dtype.
  * Returns MITA_OK once all work is enqueued. */
 mita_status mita_forward(const void* Q, const void* K, const void* V, void* O, mita_dtype dtype,
                          int B, int H, int N, int d, mita_pool pool, int m, int k, int s,

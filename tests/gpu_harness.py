@@ -207,6 +207,9 @@ def run_and_check(Q, K, V, pool, k, s, dtype, heads=None, rows=None, queries=Non
     say(f"[gpu] {label} B={B} H={H} N={Q.shape[2]} d={Q.shape[3]} pool={pool} k={k} s={s} {dtype} {variant}")
     gpu = run_gpu(Q, K, V, pool, k, s, dtype, variant)
     say(f"[gpu] {label} ran in {time.time() - t0:.2f}s; checking")
+    # (a NaN would compare as no error below: every output must be finite)
+    for key in ("O", "vtilde", "qtilde"):
+        assert np.isfinite(gpu[key]).all(), f"{label}: non-finite values in {key}"
     stats = Stats()
     heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
     for (b, h) in heads:

@@ -73,6 +73,11 @@ CASES = {
     # the widest routing: s = 8 of m = 16, and s = 5 with fp32
     "s8": (1, 1, 1, 1024, 64, 1, 16, 24, 8, "iid", 0, "bf16", "paper"),
     "s5_official_f32": (1, 1, 6, 8, 32, 2, 4, 10, 5, "iid", 0, "f32", "official"),
+    # the 64K long-sequence shape (one head of it): m = k = 128, experts of
+    # 512 queries on average, the LDS-resident key and landmark passes at
+    # benchmark scale, elementwise against the oracle
+    "long64k_s1": (1, 1, 1, 65536, 64, 1, 128, 128, 1, "runs", 64, "bf16", "paper"),
+    "long64k_s2": (1, 1, 1, 65536, 64, 1, 128, 128, 2, "runs", 64, "bf16", "paper"),
 }
 SPLIT_ITEM = 2048  # queries per work item of the routed passes
 
