@@ -80,6 +80,7 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
   p.C = ceil_div(N, L);
 
   p.dense = N <= NSMALL ? 1 : 0;
+  p.small = (N <= SMALL_N && k <= SMALL_K) ? 1 : 0;
   p.capg = p.dense ? N : CAPG;
   if (!p.dense) {
     p.sigma = k / 32 > 1 ? k / 32 : 1;
@@ -148,7 +149,7 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
   p.tau = (float*)take(Mr * 4);
   p.mhat = (float*)take(Mr * 4);
   p.vpart = (float*)take(Mr * p.C * (d + 4) * 4);
-  p.cand = (uint64_t*)take(p.dense ? Mr * p.capg * 8 : 0);
+  p.cand = (uint64_t*)take(p.dense && !p.small ? Mr * p.capg * 8 : 0);
   const size_t nseg = p.dense ? 0 : Mr * p.C * 4;
   p.rec_sc = (float*)take(nseg * p.s4 * 8 * 4);
   p.rec_st = (int32_t*)take(nseg * p.s4 * 4);

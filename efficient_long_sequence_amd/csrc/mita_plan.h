@@ -11,6 +11,10 @@ namespace mita {
 // Rows of N up to this size keep every landmark score as a candidate ("dense"
 // selection); above it a sampled threshold filters candidates first.
 constexpr int NSMALL = 8192;
+// Rows of N up to SMALL_N keys with k <= SMALL_K select their top-k on chip
+// (k_topk_small) and write no candidates at all.
+constexpr int SMALL_N = 2048;
+constexpr int SMALL_K = 64;
 // Candidate capacity per landmark row in sparse mode: the selection kernel
 // gathers a row's candidates into LDS (8192 x 8 bytes).
 constexpr int CAPG = 8192;
@@ -44,6 +48,7 @@ struct Plan {
   int B, H, BH, N, d, gh, gw, lh, lw, m, k, s;
   // landmark scoring
   int dense;      // 1: every score is a candidate
+  int small;      // 1 (dense rows only): top-k selected on chip by k_topk_small
   int capg;       // candidate slots per landmark row
   int sc_nw, sc_ib, sc_R, sc_rt;  // waves, 16-row blocks per wave, rows per tile, row tiles
   int L, C;       // keys per chunk, chunks per head

@@ -13,12 +13,17 @@
 //             offset;
 //   k_score   one workgroup per (head, landmark-row tile, key chunk): the
 //             score tile Q~ K^T on the matrix cores, an online softmax with
-//             P.V on the matrix cores (partial v~ per chunk), and every score
-//             >= tau kept as a candidate (all scores when N is small).  The
-//             m x N score matrix never reaches HBM;
+//             P.V on the matrix cores (partial v~ per chunk), and a record of
+//             the 8 scores of every lane step holding a score >= tau (for
+//             N <= 8192 rows with k > 64 or N > 2048: every score as a
+//             candidate key).  Apart from that last case the m x N score
+//             matrix never reaches HBM;
 //   k_final   per landmark row: merges the v~ partials (the rescaled-sum
 //             identity (Z1 o1 + Z2 o2)/(Z1 + Z2) of tutorial ch.4) and selects
-//             the exact top-k from the candidates with a block bitonic sort;
+//             the exact top-k from the candidates with a block radix select;
+//   k_topk_small  (rows of at most 2048 keys, k <= 64, instead of the
+//             candidate path) rescores 16 rows into LDS and selects each
+//             row's top-k there with a wave-level radix select;
 //   k_fallback exact streaming top-k for any row whose candidate count was
 //             below k or above capacity (a threshold estimate that missed).
 //
@@ -135,9 +140,14 @@ __global__ __launch_bounds__(256) void k_tau(const float* __restrict__ gmax, flo
 template <typename T, int NW, int IB>
 constexpr int score_waves_per_eu() { return (sizeof(T) == 2 && NW == 8 && IB == 1) ? 4 : 2; }
 
+// Candidate output of the scoring kernel: SEL_SPARSE, score records of the
+// lanes holding a score >= tau; SEL_DENSE, every score as a candidate key;
+// SEL_NONE, nothing (small rows select on chip in k_topk_small).
+enum { SEL_SPARSE = 0, SEL_DENSE = 1, SEL_NONE = 2 };
+
 // SHARED = false (routing-only variant): keys only, no softmax, no P.V and no
 // shared-value partials; the scores feed the candidates alone.
-template <typename T, int D, int NW, int IB, bool DENSE, bool SHARED>
+template <typename T, int D, int NW, int IB, int SEL, bool SHARED>
 __global__ __launch_bounds__(NW * 64, (score_waves_per_eu<T, NW, IB>())) void k_score(
     const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ Qt,
     const float* __restrict__ tau_in, const float* __restrict__ mhat_in, float* __restrict__ vpart,
@@ -178,7 +188,7 @@ __global__ __launch_bounds__(NW * 64, (score_waves_per_eu<T, NW, IB>())) void k_
       else zero(qf[b][dc]);
     }
     M[b].set((mhat_in != nullptr && valid) ? mhat_in[(size_t)bh * m + row] * cscale : M0, cscale);
-    tau[b] = DENSE ? -INFINITY : (valid ? tau_in[(size_t)bh * m + row] : INFINITY);
+    tau[b] = SEL != SEL_SPARSE ? -INFINITY : (valid ? tau_in[(size_t)bh * m + row] : INFINITY);
     Z[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cb = 0; cb < D / 16; ++cb) acc[b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -215,7 +225,7 @@ __global__ __launch_bounds__(NW * 64, (score_waves_per_eu<T, NW, IB>())) void k_
     // scores and the step (the selection filters them against tau)
     auto cands = [&](int b, const float* sc, float mx) {
       const int row = rbase + b * 16 + li;
-      if constexpr (DENSE) {
+      if constexpr (SEL == SEL_DENSE) {
         if (row < m) {
           uint64_t* dst = cand + ((size_t)bh * m + row) * capg + j0;
 #pragma unroll
@@ -224,7 +234,7 @@ __global__ __launch_bounds__(NW * 64, (score_waves_per_eu<T, NW, IB>())) void k_
             if (kl < nv) dst[kl] = ckey(sc[t], (uint32_t)(j0 + kl));
           }
         }
-      } else if (wave_any(mx >= tau[b])) {
+      } else if (SEL == SEL_SPARSE && wave_any(mx >= tau[b])) {
         // (rows past m have tau = +inf and never get here)
         if (mx >= tau[b]) {
           const int c = rcnt[b];
@@ -265,7 +275,7 @@ __global__ __launch_bounds__(NW * 64, (score_waves_per_eu<T, NW, IB>())) void k_
     }
   }
 
-  if constexpr (!DENSE) {
+  if constexpr (SEL == SEL_SPARSE) {
 #pragma unroll
     for (int b = 0; b < IB; ++b) {
       const int row = rbase + b * 16 + li;
@@ -338,6 +348,7 @@ __global__ __launch_bounds__(256) void k_final(const float* __restrict__ vpart, 
       vtT[r * D + tid] = from_f32<T>(v);
     }
   }
+  if (dense == 2) return;  // small rows: selected by k_topk_small
   __shared__ int s_over;
   int cnt;
   if (dense) {
@@ -539,6 +550,215 @@ __global__ __launch_bounds__(256) void k_fallback(const T* __restrict__ K, const
   emit_topk(a, k, topk + r * k);
 }
 
+
+// ---------------------------------------------------------------------------
+// small rows (N <= SMALL_N, k <= SMALL_K): top-k selected on chip
+// ---------------------------------------------------------------------------
+// One workgroup of sixteen waves per (head, 16 landmark rows).  The waves
+// score the 16 rows against all N keys on the matrix cores (wave w takes the
+// 32-key steps w, w + 16, ...; each key row is used by one wave only, so its
+// operand fragments are read straight from global memory, one step ahead)
+// into an LDS tile of raw fp32 scores; then each wave finishes one row with
+// no barrier: a radix select of the k-th largest order-preserving score key
+// (four 8-bit passes over a wave-private LDS histogram, the row's keys held
+// in registers), one pass over the keys in index order that emits every key
+// above that value and, among the keys equal to it, the lowest indices, in
+// ascending order; and the merge of the row's shared-value partials (the
+// rescaled-sum identity of tutorial ch.4, one output dimension per lane).
+// Neither the scores nor candidate keys reach HBM.
+template <typename T, int D>
+__global__ __launch_bounds__(1024) void k_topk_small(const T* __restrict__ K, const T* __restrict__ Qt,
+                                                    const float* __restrict__ vpart, int32_t* __restrict__ topk,
+                                                    float* __restrict__ vt32, T* __restrict__ vtT,
+                                                    float* __restrict__ lse_lm, int N, int m, int k, int C,
+                                                    int stride, int shared) {
+  constexpr int UMAX = SMALL_N / 64;
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* S = (float*)smem;                       // [16][stride] raw scores
+  uint32_t* hist = (uint32_t*)(S + 16 * stride); // [16 waves][256]
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, li = lane % 16, lg = lane / 16;
+  const int bh = blockIdx.y, r0 = blockIdx.x * 16;
+  const T* Kh = K + (size_t)bh * N * D;
+  Frag<T> qf[D / 32];
+  {
+    const int row = r0 + li;
+#pragma unroll
+    for (int dc = 0; dc < D / 32; ++dc) {
+      if (row < m) load8(qf[dc], Qt + ((size_t)bh * m + row) * D + dc * 32 + 8 * lg);
+      else zero(qf[dc]);
+    }
+  }
+  // this wave's row: its first 8 shared-value chunk partials are fetched now,
+  // so their latency hides under the scoring and the selection
+  constexpr int CPRE = 8;
+  const size_t rw = (size_t)bh * m + min(r0 + wave, m - 1);
+  const float* prw = vpart + rw * C * (D + 4);
+  const int ew = lane < D ? lane : 0;
+  float pq0[CPRE], pq1[CPRE], pqv[CPRE];
+  if (shared) {
+#pragma unroll
+    for (int u = 0; u < CPRE; ++u) {
+      const float* q = prw + (size_t)min(u, C - 1) * (D + 4);
+      pq0[u] = q[0];
+      pq1[u] = q[1];
+      pqv[u] = q[4 + ew];
+    }
+  }
+  const int nsteps = (N + 31) / 32;
+  auto load_step = [&](StepFrags<T, D>& f, int st) {
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) {
+      const int j = st * 32 + jt * 16 + li;
+#pragma unroll
+      for (int dc = 0; dc < D / 32; ++dc) {
+        if (j < N) load8(f.ka[jt][dc], Kh + (size_t)j * D + dc * 32 + 8 * lg);
+        else zero(f.ka[jt][dc]);
+      }
+    }
+  };
+  StepFrags<T, D> fn;
+  if (wave < nsteps) load_step(fn, wave);
+  for (int st = wave; st < nsteps; st += 16) {
+    StepFrags<T, D> f = fn;
+    if (st + 16 < nsteps) load_step(fn, st + 16);
+    float sc[8];
+    step_scores(f, qf, sc);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int j = st * 32 + slot_key(t, lg);
+      if (j < N) S[li * stride + j] = sc[t];
+    }
+  }
+  __syncthreads();
+  uint32_t* h = hist + wave * 256;
+  const int U = (N + 63) / 64;
+  {
+    const int rl = wave, row = r0 + rl;
+    if (row >= m) return;  // wave-uniform; no barrier follows
+    const float* Sr = S + rl * stride;
+    const size_t r = (size_t)bh * m + row;
+    uint32_t kf[UMAX];
+#pragma unroll
+    for (int u = 0; u < UMAX; ++u) {
+      const int j = lane + 64 * u;
+      kf[u] = (u < U && j < N) ? fkey(Sr[j]) : 0u;  // 0: below every key of a score (the smallest is -inf's)
+    }
+    // the k-th largest key value (with multiplicity), 8 bits a pass from the top
+    uint32_t prefix = 0, mask = 0;
+    int krem = k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int x = lane; x < 256; x += 64) h[x] = 0;
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int u = 0; u < UMAX; ++u) {
+        const int j = lane + 64 * u;
+        if (u < U && j < N && (kf[u] & mask) == prefix) atomicAdd(h + ((kf[u] >> shift) & 255u), 1u);
+      }
+      __builtin_amdgcn_wave_barrier();
+      // bucket b with (keys in buckets > b) < krem <= (keys in buckets >= b):
+      // lane l holds buckets 4l .. 4l + 3, suffix sums across the lanes
+      const int h0 = h[4 * lane], h1 = h[4 * lane + 1], h2 = h[4 * lane + 2], h3 = h[4 * lane + 3];
+      const int own = h0 + h1 + h2 + h3;
+      int incl = own;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_down(incl, off);
+        if (lane + off < 64) incl += v;
+      }
+      const int s4 = incl - own, s3 = s4 + h3, s2 = s3 + h2, s1 = s2 + h1, s0 = s1 + h0;
+      int bsel = -1, above = 0;
+      if (s3 >= krem && s4 < krem) { bsel = 4 * lane + 3; above = s4; }
+      if (s2 >= krem && s3 < krem) { bsel = 4 * lane + 2; above = s3; }
+      if (s1 >= krem && s2 < krem) { bsel = 4 * lane + 1; above = s2; }
+      if (s0 >= krem && s1 < krem) { bsel = 4 * lane; above = s1; }
+      // exactly one lane found it (the keys matching the prefix number at
+      // least krem, and none lie above the top bucket)
+      const uint64_t who = __builtin_amdgcn_ballot_w64(bsel >= 0);
+      const int src = who ? (int)__builtin_ctzll(who) : 0;
+      bsel = __shfl(bsel, src);
+      above = __shfl(above, src);
+      prefix |= (uint32_t)(bsel & 255) << shift;
+      mask |= 0xFFu << shift;
+      krem -= above;
+      // the chosen bucket is taken whole: the remaining bits decide nothing
+      const int inb = __shfl(bsel == 4 * lane + 3 ? h3 : bsel == 4 * lane + 2 ? h2 : bsel == 4 * lane + 1 ? h1 : h0,
+                             src);
+      if (inb == krem) break;
+    }
+    // emit: every key above the k-th value, then the first krem keys equal to
+    // it, in index order
+    int32_t* out = topk + r * k;
+    int pos = 0, eq_seen = 0;
+#pragma unroll
+    for (int u = 0; u < UMAX; ++u) {
+      if (u < U) {
+        const int j = lane + 64 * u;
+        const bool valid = j < N;
+        const uint32_t km = kf[u] & mask;
+        const bool gt = valid && km > prefix, eq = valid && km == prefix;
+        const uint64_t be = __builtin_amdgcn_ballot_w64(eq);
+        const int er = eq_seen + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
+        const bool take = gt || (eq && er < krem);
+        const uint64_t bt = __builtin_amdgcn_ballot_w64(take);
+        const int o = pos + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bt >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)bt, 0u));
+        if (take && o < k) out[o] = j;  // (exactly k are taken; the bound only guards memory)
+        pos += (int)__builtin_popcountll(bt);
+        eq_seen += (int)__builtin_popcountll(be);
+      }
+    }
+    // shared value of the row: merge its C chunk partials (lane e owns
+    // output dim e); every load of a batch is in flight at once
+    if (shared) {
+      const float* pr = vpart + r * C * (D + 4);
+      float mx = M0;
+#pragma unroll
+      for (int u = 0; u < CPRE; ++u)
+        if (u < C) mx = fmaxf(mx, pq0[u]);
+      if (C > CPRE) {
+        for (int c = CPRE + lane; c < C; c += 64) mx = fmaxf(mx, pr[(size_t)c * (D + 4)]);
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      }
+      float zs = 0.f, sv = 0.f;
+#pragma unroll
+      for (int u = 0; u < CPRE; ++u) {
+        if (u < C) {
+          const float w = __builtin_amdgcn_exp2f(pq0[u] - mx);
+          zs += pq1[u] * w;
+          sv += pqv[u] * w;
+        }
+      }
+      for (int c0 = CPRE; c0 < C; c0 += 8) {
+        float q0[8], q1[8], qv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int c = min(c0 + u, C - 1);
+          const float* q = pr + (size_t)c * (D + 4);
+          q0[u] = q[0];
+          q1[u] = q[1];
+          qv[u] = q[4 + ew];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (c0 + u < C) {
+            const float w = __builtin_amdgcn_exp2f(q0[u] - mx);
+            zs += q1[u] * w;
+            sv += qv[u] * w;
+          }
+        }
+      }
+      if (lane < D) {
+        const float v = sv / zs;
+        vt32[r * D + lane] = v;
+        vtT[r * D + lane] = from_f32<T>(v);
+      }
+      if (lse_lm && lane == 0) lse_lm[r] = mx + __builtin_amdgcn_logf(zs);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
@@ -565,13 +785,19 @@ static void launch_score_s(const Plan& p) {
   const bool dense = p.dense != 0;
   const size_t lds = 2 * TL::ELEMS * sizeof(T);
   dim3 grid((unsigned)p.C, (unsigned)p.sc_rt, (unsigned)p.BH);
+  if (dense && p.small) {
+    hipLaunchKernelGGL((k_score<T, D, NW, IB, SEL_NONE, SHARED>), grid, dim3(NW * 64), lds, p.stream, (const T*)p.K,
+                       (const T*)p.V, (const T*)p.qt, nullptr, nullptr, p.vpart, nullptr, nullptr, nullptr, nullptr,
+                       p.N, p.m, p.L, p.C, 0, 0, p.cscale);
+    return;
+  }
   if (dense) {
-    hipLaunchKernelGGL((k_score<T, D, NW, IB, true, SHARED>), grid, dim3(NW * 64), lds, p.stream, (const T*)p.K,
+    hipLaunchKernelGGL((k_score<T, D, NW, IB, SEL_DENSE, SHARED>), grid, dim3(NW * 64), lds, p.stream, (const T*)p.K,
                        (const T*)p.V, (const T*)p.qt, nullptr, nullptr, p.vpart, p.cand, nullptr, nullptr, nullptr,
                        p.N, p.m, p.L, p.C, p.capg, 0, p.cscale);
     return;
   }
-  hipLaunchKernelGGL((k_score<T, D, NW, IB, false, SHARED>), grid, dim3(NW * 64), lds, p.stream, (const T*)p.K,
+  hipLaunchKernelGGL((k_score<T, D, NW, IB, SEL_SPARSE, SHARED>), grid, dim3(NW * 64), lds, p.stream, (const T*)p.K,
                      (const T*)p.V, (const T*)p.qt, p.tau, p.force_fallback ? nullptr : p.mhat, p.vpart, nullptr,
                      p.rec_sc, p.rec_st, p.rec_cnt, p.N, p.m, p.L, p.C, p.capg, p.s4, p.cscale);
 }
@@ -584,16 +810,28 @@ static void launch_score_main(const Plan& p) {
 
 template <typename T, int D>
 static void launch_final_t(const Plan& p) {
+  if (p.small) {
+    // top-k and the shared-value merge on chip; k_final is not needed
+    const int stride = (p.N + 63) / 64 * 64 + 1;
+    const size_t lds2 = (size_t)16 * stride * 4 + 16 * 256 * 4;
+    if (lds2 > 65536)
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_topk_small<T, D>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
+    hipLaunchKernelGGL((k_topk_small<T, D>), dim3((unsigned)((p.m + 15) / 16), (unsigned)p.BH), dim3(1024), lds2,
+                       p.stream, (const T*)p.K, (const T*)p.qt, p.vpart, p.topk, p.vt32, (T*)p.vtT, p.lse_lm, p.N,
+                       p.m, p.k, p.C, stride, p.shared);
+    return;
+  }
   // candidates, then the selected keys (or, before the selection, the
   // per-segment record counts of a sparse row)
   const size_t sel = (size_t)next_pow2(p.k < 2 ? 2 : p.k) * 8;
-  const size_t lds = (size_t)p.capg * 8 + (p.dense ? sel : std::max(sel, ((size_t)4 * p.C + 1) * 4));
+  const size_t lds = p.small ? 0 : (size_t)p.capg * 8 + (p.dense ? sel : std::max(sel, ((size_t)4 * p.C + 1) * 4));
   if (lds > 65536)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_final<T, D>), hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)lds);
   hipLaunchKernelGGL((k_final<T, D>), dim3((unsigned)(p.BH * p.m)), dim3(256), lds, p.stream, p.vpart, p.cand,
                      p.rec_sc, p.rec_st, p.rec_cnt, p.tau, p.topk, p.vt32, (T*)p.vtT, p.fail, p.lse_lm, p.N, p.k,
-                     p.C, p.L, p.capg, p.s4, p.dense, p.shared);
+                     p.C, p.L, p.capg, p.s4, p.small ? 2 : p.dense, p.shared);
   if (!p.dense) {
     const size_t lds2 = (size_t)next_pow2(2 * p.k + 256) * 8;
     hipLaunchKernelGGL((k_fallback<T, D>), dim3((unsigned)(p.BH * p.m)), dim3(256), lds2, p.stream,
