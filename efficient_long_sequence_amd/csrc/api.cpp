@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "mita.h"
 #include "mita_plan.h"
@@ -373,6 +374,36 @@ const char* const kStageNames[ST_COUNT] = {"pool", "estimate", "score", "select"
 
 }  // namespace
 
+// Scratch of mita_forward_noalloc: a file-scope device array, one copy on
+// every GPU the library runs on, held until the process ends.  Host code uses
+// the device address hipGetSymbolAddress returns for the current device
+// (kept per device below), never the array's name, which on the host is only
+// a stand-in for the symbol.
+static __device__ __align__(256) unsigned char scratch[MITA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // device address of `scratch` on each device (nullptr: not looked up yet)
+
+// The scratch array's address on the current device, looked up once per
+// device (with that device current).
+mita_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MITA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return MITA_ERR_HIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return MITA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t mita_workspace_bytes(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int m, int k, int s) {
@@ -385,6 +416,18 @@ mita_status mita_forward(const void* Q, const void* K, const void* V, void* O, m
                          size_t workspace_bytes, void* stream) {
   return run(Q, K, V, O, dtype, B, H, N, d, pool, m, k, s, MITA_VARIANT_PAPER, dbg, workspace, workspace_bytes,
              stream, nullptr);
+}
+
+mita_status mita_forward_noalloc(const void* Q, const void* K, const void* V, void* O, mita_dtype dtype, int B,
+                                 int H, int N, int d, mita_pool pool, int m, int k, int s, void* stream) {
+  mita_status st = validate(Q, K, V, O, dtype, B, H, N, d, pool, m, k, s, true);
+  if (st != MITA_OK) return st;
+  if (make_plan(dtype, B, H, N, d, pool, m, k, s, nullptr).total_bytes > MITA_NOALLOC_SCRATCH_BYTES)
+    return MITA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != MITA_OK) return st;
+  return run(Q, K, V, O, dtype, B, H, N, d, pool, m, k, s, MITA_VARIANT_PAPER, nullptr, ws,
+             MITA_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 mita_status mita_forward_timed(const void* Q, const void* K, const void* V, void* O, mita_dtype dtype, int B,

@@ -27,7 +27,7 @@ EXPORTS = [
     "mita_workspace_bytes", "mita_forward", "mita_forward_timed", "mita_forward_variant", "mita_dense_attention", "mita_num_stages",
     "mita_stage_name", "mita_events_create", "mita_events_destroy", "mita_events_elapsed",
     "mita_status_str", "mita_version", "mita_forward_train", "mita_backward_workspace_bytes", "mita_backward",
-    "mita_probe_mfma", "mita_probe_copy",
+    "mita_probe_mfma", "mita_probe_copy", "mita_forward_noalloc",
 ]
 
 
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
     L.mita_forward_timed.argtypes = fwd + [ctypes.POINTER(vp)]
     L.mita_forward_variant.restype = c_int
     L.mita_forward_variant.argtypes = fwd[:13] + [c_int] + fwd[13:] + [ctypes.POINTER(vp)]
+    L.mita_forward_noalloc.restype = c_int
+    L.mita_forward_noalloc.argtypes = fwd[:13] + [vp]
     L.mita_dense_attention.restype = c_int
     L.mita_dense_attention.argtypes = [vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, vp]
     L.mita_num_stages.restype = c_int
@@ -240,6 +242,28 @@ def forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, pool, k: int, s: 
         code = L.mita_forward_timed(*args, events.arr)
     _check(code)
     return (O, dbg) if debug else O
+
+
+# the library's own static scratch (bytes per GPU), for mita_forward_noalloc
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def forward_noalloc(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, pool, k: int, s: int,
+                    out: torch.Tensor | None = None, m: int | None = None):
+    """MiTA forward pass through mita_forward_noalloc: no workspace, the
+    library's static scratch instead (calls that overlap on one GPU race).
+    Raises MitaError(MITA_ERR_WORKSPACE) when the call needs more than
+    NOALLOC_SCRATCH_BYTES of it.  Pass ``out`` to allocate nothing here either."""
+    L = lib()
+    B, H, N, d = Q.shape
+    gh, gw, lh, lw = pool
+    m = lh * lw if m is None else m
+    O = torch.empty_like(Q) if out is None else out
+    _check_qkv(Q, K, V, O)
+    stream = torch.cuda.current_stream(Q.device).cuda_stream
+    _check(L.mita_forward_noalloc(Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), _dtype_code(Q.dtype),
+                                  B, H, N, d, Pool(gh, gw, lh, lw), m, k, s, stream))
+    return O
 
 
 # ---------------------------------------------------------------------------

@@ -113,6 +113,25 @@ mita_status mita_forward(const void* Q, const void* K, const void* V, void* O, m
                          const mita_debug* dbg, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): mita_forward
+ * with no workspace argument.  Its scratch is a device array inside the
+ * library, MITA_NOALLOC_SCRATCH_BYTES on every GPU it runs on, kept until the
+ * process ends; a call whose mita_workspace_bytes(...) exceeds that returns
+ * MITA_ERR_WORKSPACE before any launch (the vision-shaped workloads need
+ * 15-22 MiB; long sequences need the caller's workspace and mita_forward).
+ * The first call on a device looks the array's address up once (the device
+ * that owns Q, K, V, O and the stream must be current, as for every launch).
+ * Allocates nothing, synchronises nothing.  All calls on one GPU share its
+ * array and each clears what it needs at its start: calls that overlap on one
+ * GPU (other streams, other threads) race and give unspecified results --
+ * serialise them.  Same arguments, validation and results as mita_forward
+ * with dbg = NULL. */
+#define MITA_NOALLOC_SCRATCH_BYTES (64u << 20)
+mita_status mita_forward_noalloc(const void* Q, const void* K, const void* V, void* O, mita_dtype dtype,
+                                 int B, int H, int N, int d, mita_pool pool, int m, int k, int s,
+                                 void* stream);
+
 /* Profiling variant: identical work, and additionally records a pair of HIP
  * events around each stage on `stream`.  `events` holds 2 * mita_num_stages()
  * hipEvent_t handles made by mita_events_create (start, stop per stage); a

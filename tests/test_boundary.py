@@ -221,3 +221,26 @@ def test_saved_tensors_are_checked_before_the_call():
         with pytest.raises(mita.MitaError):
             mita._check_saved(mita.SavedOut(**{**good, name: bad}), Q, m, k, s)
 
+
+
+def _noalloc(**kw):
+    a = dict(Q=A, K=A, V=A, O=A, dt=mita.BF16, B=1, H=2, N=65536, d=64, pool=(1, 65536, 1, 128), m=128,
+             k=128, s=1)
+    a.update(kw)
+    P = mita.Pool(*a["pool"])
+    return mita.lib().mita_forward_noalloc(a["Q"], a["K"], a["V"], a["O"], a["dt"], a["B"], a["H"], a["N"],
+                                           a["d"], P, a["m"], a["k"], a["s"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), 5),  # valid, but needs more than the static scratch: rejected before any launch
+    (dict(Q=0), 1), (dict(N=65535), 2), (dict(k=0), 3), (dict(d=48), 4),
+])
+def test_noalloc_rejects_before_any_hip_call(kw, code):
+    """The entry point without allocation validates like mita_forward and
+    refuses a call whose workspace would exceed its static scratch, all on
+    the host (no HIP call: these run on the CPU)."""
+    assert _noalloc(**kw) == code
+    import torch
+    assert mita.workspace_bytes(torch.bfloat16, 1, 2, 65536, 64, (1, 65536, 1, 128), 128, 1) > \
+        mita.NOALLOC_SCRATCH_BYTES
