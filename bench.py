@@ -273,9 +273,21 @@ def ingest(trace_dir: str, fetch_dir: str, write_dir: str, workload: str, comman
             write = sum(wv) / len(wv) * 1024 * w_fac
             kern[f"{key}:{workload}"] = dict(fetch_bytes=fetch, write_bytes=write, bytes_per_launch=fetch + write)
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
-        json.dump(dict(sources_sha=sources_sha(), workload=workload, command=command,
-                       fetch_factor=f_fac, write_factor=w_fac, kernels=kern), f, indent=1)
+    # one record for every workload profiled on the current sources: the
+    # entries of other workloads are kept when they were taken on these sources
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    rec = dict(sources_sha=sources_sha(), kernels={}, commands={}, factors={})
+    if os.path.exists(path):
+        with open(path) as f:
+            old = json.load(f)
+        if old.get("sources_sha") == rec["sources_sha"] and "commands" in old:
+            rec = old
+    rec["kernels"] = {k2: v for k2, v in rec["kernels"].items() if not k2.endswith(":" + workload)}
+    rec["kernels"].update(kern)
+    rec["commands"][workload] = command
+    rec["factors"][workload] = dict(fetch_factor=f_fac, write_factor=w_fac)
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
     lines = [f"# rocprofv3 kernel trace and HBM traffic: mita_forward, {workload}", "",
              "Command (run from /tmp, TMPDIR=/tmp, repository at $R):", "",
              f"    rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- {command}",
