@@ -238,20 +238,24 @@ __device__ __forceinline__ float max8(const float* s) {
   return fmaxf(m, s[7]);
 }
 
-// One 32-entry step for IB blocks of 16 queries: the score tiles of all
-// blocks first, then the hook `on(b, scores, lane_max)` of each block
-// (candidates, routing), then one check of every block's running maximum
-// (a single, rarely taken branch), and last the exponentials and P.V of all
-// blocks as one branch-free stretch, so the scheduler can overlap one
-// block's vector work with another's matrix work.  MASK marks the last,
-// partial step: entries at offsets >= nv get score -inf.
-template <int IB, bool MASK, typename T, int D, class On>
-__device__ __forceinline__ void attn_step(const StepFrags<T, D>& f, const Frag<T>& one,
-                                          const Frag<T> (&qf)[IB][D / 32], int nv, int lg, float cscale,
-                                          RunMax (&M)[IB], f32x4 (&Z)[IB], f32x4 (&acc)[IB][D / 16], On on) {
-  float sc[IB][8];
+// The two halves of one 32-entry step for IB blocks of 16 queries.
+// attn_scores: the score tiles of all blocks on the matrix cores.
+template <int IB, typename T, int D>
+__device__ __forceinline__ void attn_scores(const StepFrags<T, D>& f, const Frag<T> (&qf)[IB][D / 32],
+                                            float (&sc)[IB][8]) {
 #pragma unroll
   for (int b = 0; b < IB; ++b) step_scores(f, qf[b], sc[b]);
+}
+
+// attn_finish: the hook `on(b, scores, lane_max)` of each block
+// (candidates, routing), then one check of every block's running maximum (a
+// single, rarely taken branch), and last the exponentials and P.V of all
+// blocks as one branch-free stretch.  MASK marks the last, partial step:
+// entries at offsets >= nv get score -inf.
+template <int IB, bool MASK, typename T, int D, class On>
+__device__ __forceinline__ void attn_finish(const StepFrags<T, D>& f, const Frag<T>& one, float (&sc)[IB][8], int nv,
+                                            int lg, float cscale, RunMax (&M)[IB], f32x4 (&Z)[IB],
+                                            f32x4 (&acc)[IB][D / 16], On on) {
   if constexpr (MASK) {
 #pragma unroll
     for (int b = 0; b < IB; ++b)
@@ -297,6 +301,18 @@ __device__ __forceinline__ void attn_step(const StepFrags<T, D>& f, const Frag<T
     for (int cb = 0; cb < D / 16; ++cb) mma16(acc[b][cb], f.va[cb], pf);
     mma16(Z[b], one, pf);
   }
+}
+
+// One whole 32-entry step: the score tiles of all blocks first, then
+// attn_finish, so the scheduler can overlap one block's vector work with
+// another's matrix work.
+template <int IB, bool MASK, typename T, int D, class On>
+__device__ __forceinline__ void attn_step(const StepFrags<T, D>& f, const Frag<T>& one,
+                                          const Frag<T> (&qf)[IB][D / 32], int nv, int lg, float cscale,
+                                          RunMax (&M)[IB], f32x4 (&Z)[IB], f32x4 (&acc)[IB][D / 16], On on) {
+  float sc[IB][8];
+  attn_scores<IB>(f, qf, sc);
+  attn_finish<IB, MASK>(f, one, sc, nv, lg, cscale, M, Z, acc, on);
 }
 
 struct NoHook {
