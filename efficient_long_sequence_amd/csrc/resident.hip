@@ -195,8 +195,10 @@ __device__ __forceinline__ void list_insert(float* lv, int* lx, float v, int i) 
 }
 
 // ---------------------------------------------------------------------------
-template <typename T, int D, int NW, int SMAX>
-__global__ __launch_bounds__(NW * 64) void k_route_shared(
+// IB: 16-query blocks per wave group (four with eight waves; one with sixteen
+// waves, four per SIMD, for mid-size heads)
+template <typename T, int D, int NW, int SMAX, int IB>
+__global__ __launch_bounds__(NW * 64, NW >= 16 ? 4 : 1) void k_route_shared(
     const T* __restrict__ Q, const T* __restrict__ Qt, const T* __restrict__ VtT, int32_t* __restrict__ route,
     int* __restrict__ counts, float2* __restrict__ plse, typename PartT<T>::type* __restrict__ po, int N, int m, int s,
     int BH, int qpw, int hist_lds, float cscale) {  // cscale: log2(e) x the shared-logit scale
@@ -219,28 +221,29 @@ __global__ __launch_bounds__(NW * 64) void k_route_shared(
            [&](int x) { return VtT + ((size_t)bh * m + x) * D; });
   __syncthreads();
 
-  const int ngroups = (q1 - q0 + 63) / 64;
+  constexpr int GQ = 16 * IB;
+  const int ngroups = (q1 - q0 + GQ - 1) / GQ;
   auto group_rows = [&](int gi) {
-    return [=](int b) -> long long { const int n = q0 + gi * 64 + b * 16 + li; return n < q1 ? n : -1; };
+    return [=](int b) -> long long { const int n = q0 + gi * GQ + b * 16 + li; return n < q1 ? n : -1; };
   };
   // the next group's query rows are fetched while the current one computes
-  Frag<T> qn[4][D / 32];
-  if (wave < ngroups) load_queries<T, D, 4>(qn, Qh, lg, group_rows(wave));
+  Frag<T> qn[IB][D / 32];
+  if (wave < ngroups) load_queries<T, D, IB>(qn, Qh, lg, group_rows(wave));
   for (int gi = wave; gi < ngroups; gi += NW) {
-    const int qb = q0 + gi * 64;
-    Frag<T> qf[4][D / 32];
+    const int qb = q0 + gi * GQ;
+    Frag<T> qf[IB][D / 32];
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < IB; ++b)
 #pragma unroll
       for (int dc = 0; dc < D / 32; ++dc) qf[b][dc] = qn[b][dc];
-    if (gi + NW < ngroups) load_queries<T, D, 4>(qn, Qh, lg, group_rows(gi + NW));
-    float lv[4][SMAX];
-    RunMax M[4];
-    f32x4 Z[4];
-    int lx[4][SMAX];
-    f32x4 acc[4][D / 16];
+    if (gi + NW < ngroups) load_queries<T, D, IB>(qn, Qh, lg, group_rows(gi + NW));
+    float lv[IB][SMAX];
+    RunMax M[IB];
+    f32x4 Z[IB];
+    int lx[IB][SMAX];
+    f32x4 acc[IB][D / 16];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+    for (int b = 0; b < IB; ++b) {
 #pragma unroll
       for (int t = 0; t < SMAX; ++t) { lv[b][t] = -INFINITY; lx[b][t] = 0x7FFFFFFF; }
       M[b].set(M0, cscale);
@@ -271,15 +274,15 @@ __global__ __launch_bounds__(NW * 64) void k_route_shared(
     for (; x0 + 32 <= m; x0 += 32) {
       StepFrags<T, D> f;
       RL::frags(f, Ks, Vs, Mp, x0, li, lg);
-      attn_step<4, false>(f, one, qf, 32, lg, cscale, M, Z, acc, topsel);
+      attn_step<IB, false>(f, one, qf, 32, lg, cscale, M, Z, acc, topsel);
     }
     if (x0 < m) {
       StepFrags<T, D> f;
       RL::frags(f, Ks, Vs, Mp, x0, li, lg);
-      attn_step<4, true>(f, one, qf, m - x0, lg, cscale, M, Z, acc, topsel);
+      attn_step<IB, true>(f, one, qf, m - x0, lg, cscale, M, Z, acc, topsel);
     }
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+    for (int b = 0; b < IB; ++b) {
 #pragma unroll
       for (int sh = 16; sh <= 32; sh <<= 1) {
         float ov[SMAX];
@@ -430,7 +433,9 @@ __device__ __forceinline__ void expert_blocks(const T* Qh, QR qrow, const T* Ks,
 }
 
 template <typename T, int D, int NW, int IB>
-__global__ __launch_bounds__(NW * 64, 2) void k_expert(
+// (sixteen waves of one 16-query block each: four waves per SIMD, so one
+// wave's dependency stalls are covered by the others)
+__global__ __launch_bounds__(NW * 64, NW >= 16 ? 4 : 2) void k_expert(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const int32_t* __restrict__ topk,
     const int32_t* __restrict__ perm, const WorkItem* __restrict__ wl, const int* __restrict__ wl_count,
     float2* __restrict__ plse, typename PartT<T>::type* __restrict__ po, T* __restrict__ O, TrainOut tr, int N, int m, int k,
@@ -509,12 +514,11 @@ size_t resident_bytes(int dtype, int d, int E) {
   return d == 64 ? Resident<float, 64>::bytes(Ep) : Resident<float, 32>::bytes(Ep);
 }
 
-template <typename T, int D, int SMAX>
+template <typename T, int D, int SMAX, int NW, int IB>
 static void launch_route_shared_t(const Plan& p) {
-  constexpr int NW = 8;
   const int hist_lds = (p.s * p.m <= 4096) ? 1 : 0;
   const size_t lds = resident_bytes(p.dtype, D, p.m) + (hist_lds ? (size_t)p.s * p.m * 4 : 0);
-  auto fn = &k_route_shared<T, D, NW, SMAX>;
+  auto fn = &k_route_shared<T, D, NW, SMAX, IB>;
   if (lds > 65536)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   dim3 grid((unsigned)((p.N + p.rs_qpw - 1) / p.rs_qpw), (unsigned)p.BH);
@@ -524,11 +528,20 @@ static void launch_route_shared_t(const Plan& p) {
 
 template <typename T, int D>
 static void launch_route_shared_d(const Plan& p) {
+  if (p.rs_nw == 16) {
+    switch (p.smax) {
+      case 1: launch_route_shared_t<T, D, 1, 16, 1>(p); break;
+      case 2: launch_route_shared_t<T, D, 2, 16, 1>(p); break;
+      case 4: launch_route_shared_t<T, D, 4, 16, 1>(p); break;
+      default: launch_route_shared_t<T, D, 8, 16, 1>(p); break;
+    }
+    return;
+  }
   switch (p.smax) {
-    case 1: launch_route_shared_t<T, D, 1>(p); break;
-    case 2: launch_route_shared_t<T, D, 2>(p); break;
-    case 4: launch_route_shared_t<T, D, 4>(p); break;
-    default: launch_route_shared_t<T, D, 8>(p); break;
+    case 1: launch_route_shared_t<T, D, 1, 8, 4>(p); break;
+    case 2: launch_route_shared_t<T, D, 2, 8, 4>(p); break;
+    case 4: launch_route_shared_t<T, D, 4, 8, 4>(p); break;
+    default: launch_route_shared_t<T, D, 8, 8, 4>(p); break;
   }
 }
 
@@ -561,6 +574,7 @@ static void launch_expert_d(const Plan& p) {
   if (p.ex_nw == 1 && p.ex_ib == 1) launch_expert_t<T, D, 1, 1>(p);
   else if (p.ex_nw == 1) launch_expert_t<T, D, 1, 2>(p);
   else if (p.ex_nw == 4) launch_expert_t<T, D, 4, 4>(p);
+  else if (p.ex_nw == 16) launch_expert_t<T, D, 16, 1>(p);
   else launch_expert_t<T, D, 8, 4>(p);
 }
 
