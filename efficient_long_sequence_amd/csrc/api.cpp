@@ -93,10 +93,17 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
     const long long est_target = 512;
     int gpb = ceil_div((long long)p.G * p.BH * p.sc_rt, est_target);
     p.est_gpb = gpb < 1 ? 1 : gpb;
-    // records per (row, chunk, lane group): a lane keeps at most one per
-    // 32-key step of its chunk
+    // records per (row, chunk, lane group): the threshold admits about 2.3 k
+    // keys per row and a record holds one or more of them, so a lane group
+    // holds at most e = 0.35 k L / N records per chunk on average (the
+    // seeded 1M-key inputs give 0.5 to 0.6 e); clustered keys come in bursts
+    // of up to about 10 times the mean, so room is left for 20 e and at least
+    // REC_MIN; a lane keeps at most one record per 32-key step
     const int steps = ceil_div(p.L, 32);
-    p.s4 = steps < REC_MAX ? steps : REC_MAX;
+    const double e = 0.35 * (double)k * p.L / N;
+    int s4 = (int)std::ceil(20.0 * e);
+    s4 = s4 < REC_MIN ? REC_MIN : s4;
+    p.s4 = steps < s4 ? steps : s4;
     // Test hook (host-forced): MITA_TEST_FORCE_FALLBACK=1 sets every candidate
     // threshold to +inf, so no row collects candidates and every row is
     // selected by the exact fallback kernel instead.

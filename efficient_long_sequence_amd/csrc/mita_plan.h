@@ -18,9 +18,10 @@ constexpr int SMALL_K = 64;
 // Candidate capacity per landmark row in sparse mode: the selection kernel
 // gathers a row's candidates into LDS (8192 x 8 bytes).
 constexpr int CAPG = 8192;
-// Sparse mode: score records a lane may keep per (landmark row, key chunk,
-// lane group); a lane that needs more marks its row for the exact fallback.
-constexpr int REC_MAX = 32;
+// Sparse mode: the least room for score records a lane keeps per (landmark
+// row, key chunk, lane group) (more when the expected count is larger); a lane
+// that needs more marks its row for the exact fallback.
+constexpr int REC_MIN = 32;
 constexpr int MAX_S = 8;
 constexpr int MAX_M = 4096;
 constexpr int MAX_K_SPARSE = 2048;
