@@ -191,6 +191,12 @@ def roofline_of(w, stages: dict, stage: str, traffic):
     if pm and (r["bound"] == "hbm" or w.dtype == "bf16"):
         r["peak_measured"] = pm
         r["frac_measured"] = r["achieved"] / pm
+    # and against the best rate of the bare online-softmax step these kernels
+    # are built on (d = 64 bf16, any of the probed launch shapes)
+    step = MEASURED_PEAKS.get("step_bf16_tflops")
+    if step and r["bound"] == "mfma" and w.dtype == "bf16" and w.d == 64:
+        r["step_ceiling"] = max(step.values())
+        r["frac_of_step_ceiling"] = r["achieved"] / r["step_ceiling"]
     r.update(kernel=STAGE_KERNEL[stage], kernel_ms=stages[stage], alg_flops=flops, alg_bytes=byts,
              flop_per_byte=flops / byts, overhead_bytes=over,
              hbm_gbs_alg=byts / sec / 1e9, mfma_tflops_alg=flops / sec / 1e12,

@@ -9,8 +9,16 @@
 //   k_probe_copy  a 16-byte-per-thread device copy with four loads in
 //                 flight per thread (reads + writes bytes through HBM once
 //                 each), grid-strided.
+//   k_probe_step  the attention kernels' own online-softmax step (attn_step:
+//                 scores on the matrix cores, running-maximum check,
+//                 exponentials, bf16 packing, P.V and the normaliser product)
+//                 with every operand already in registers: no loads, no
+//                 barriers, no hooks.  Its rate is the ceiling of a kernel
+//                 built on that step at the same waves per workgroup and
+//                 16-row blocks per wave.
 #include "mita_dev.h"
 #include "mita_plan.h"
+#include "tile.h"
 
 namespace mita {
 
@@ -60,6 +68,69 @@ __global__ __launch_bounds__(256) void k_probe_copy(const v4u* __restrict__ src,
     __builtin_nontemporal_store(x3, dst + i + 3 * stride);
   }
   for (; i < n16; i += stride) dst[i] = src[i];
+}
+
+template <int NW, int IB, int WPE>
+__global__ __launch_bounds__(NW * 64, WPE) void k_probe_step(float* __restrict__ out, int iters) {
+  typedef __bf16 T;
+  constexpr int D = 64;
+  const int lane = threadIdx.x % 64, li = lane % 16, lg = lane / 16;
+  StepFrags<T, D> f;
+#pragma unroll
+  for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+    for (int dc = 0; dc < D / 32; ++dc)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) f.ka[jt][dc].v[t] = (T)(0.01f * ((lane + t + jt + dc) % 7) - 0.03f);
+#pragma unroll
+  for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) f.va[cb].v[t] = (T)(0.02f * ((lane * 3 + t + cb) % 5));
+  Frag<T> qf[IB][D / 32];
+#pragma unroll
+  for (int b = 0; b < IB; ++b)
+#pragma unroll
+    for (int dc = 0; dc < D / 32; ++dc)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) qf[b][dc].v[t] = (T)(0.01f * ((lane + 2 * t + b + dc) % 9) - 0.04f);
+  const Frag<T> one = ones_frag<T>(li);
+  const float cscale = 0.18033688f;  // log2(e) / sqrt(64)
+  RunMax M[IB];
+  f32x4 Z[IB];
+  f32x4 acc[IB][D / 16];
+#pragma unroll
+  for (int b = 0; b < IB; ++b) {
+    M[b].set(1.0f, cscale);
+    Z[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb) acc[b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int i = 0; i < iters; ++i) {
+    attn_step<IB, false>(f, one, qf, 32, lg, cscale, M, Z, acc, NoHook{});
+    // a loop-carried key operand keeps the score products inside the loop
+    f.ka[0][0].v[0] = (T)((float)f.ka[0][0].v[0] + 1e-30f * Z[0][0]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int b = 0; b < IB; ++b) {
+    s += Z[b][0];
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb) s += acc[b][cb][0] + acc[b][cb][1] + acc[b][cb][2] + acc[b][cb][3];
+  }
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+int probe_step_threads(int shape) { return shape == 1 ? 1024 : 512; }
+
+void launch_probe_step(float* out, int shape, int blocks, int iters, hipStream_t stream) {
+  // shape 0: 8 waves x 4 blocks (two waves per SIMD); 1: 16 waves x 1 block
+  // (four per SIMD); 2: 8 waves x 2 blocks (two workgroups per compute unit)
+  if (shape == 0)
+    hipLaunchKernelGGL((k_probe_step<8, 4, 2>), dim3((unsigned)blocks), dim3(512), 0, stream, out, iters);
+  else if (shape == 1)
+    hipLaunchKernelGGL((k_probe_step<16, 1, 4>), dim3((unsigned)blocks), dim3(1024), 0, stream, out, iters);
+  else
+    hipLaunchKernelGGL((k_probe_step<8, 2, 2>), dim3((unsigned)blocks), dim3(512), 0, stream, out, iters);
 }
 
 void launch_probe_mfma(float* out, int blocks, int iters, hipStream_t stream) {

@@ -433,8 +433,8 @@ __device__ __forceinline__ void expert_blocks(const T* Qh, QR qrow, const T* Ks,
 }
 
 template <typename T, int D, int NW, int IB>
-// (sixteen waves of one 16-query block each: four waves per SIMD, so one
-// wave's dependency stalls are covered by the others)
+// (sixteen waves of one or two 16-query blocks each for bf16: four waves per
+// SIMD, so one wave's dependency stalls are covered by the others)
 __global__ __launch_bounds__(NW * 64, NW >= 16 ? 4 : 2) void k_expert(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const int32_t* __restrict__ topk,
     const int32_t* __restrict__ perm, const WorkItem* __restrict__ wl, const int* __restrict__ wl_count,
@@ -474,18 +474,26 @@ __global__ __launch_bounds__(NW * 64, NW >= 16 ? 4 : 2) void k_expert(
     return [=](int b) -> long long { return s_q[gi * GQ + b * 16 + li]; };
   };
   // the next group's query rows are fetched while the current one computes
-  Frag<T> qnx[IB][D / 32];
-  if (wave < nfull) load_queries<T, D, IB>(qnx, Qh, lg, group_rows(wave));
+  // (not with sixteen waves of two blocks: no registers for it, and the
+  // other three waves of the SIMD cover the load)
+  constexpr bool PREFETCH = !(NW == 16 && IB == 2);
+  Frag<T> qnx[PREFETCH ? IB : 1][D / 32];
+  if constexpr (PREFETCH)
+    if (wave < nfull) load_queries<T, D, IB>(qnx, Qh, lg, group_rows(wave));
   for (int gi = wave; gi < nfull; gi += NW) {
     Frag<T> qf[IB][D / 32];
     int qn[IB];
+    if constexpr (PREFETCH) {
 #pragma unroll
-    for (int b = 0; b < IB; ++b) {
+      for (int b = 0; b < IB; ++b)
 #pragma unroll
-      for (int dc = 0; dc < D / 32; ++dc) qf[b][dc] = qnx[b][dc];
-      qn[b] = s_q[gi * GQ + b * 16 + li];
+        for (int dc = 0; dc < D / 32; ++dc) qf[b][dc] = qnx[b][dc];
+      if (gi + NW < nfull) load_queries<T, D, IB>(qnx, Qh, lg, group_rows(gi + NW));
+    } else {
+      load_queries<T, D, IB>(qf, Qh, lg, group_rows(gi));
     }
-    if (gi + NW < nfull) load_queries<T, D, IB>(qnx, Qh, lg, group_rows(gi + NW));
+#pragma unroll
+    for (int b = 0; b < IB; ++b) qn[b] = s_q[gi * GQ + b * 16 + li];
     expert_group<IB, T, D>(qf, qn, Ks, Vs, Kp, k, one, row0, plse, po, O, tr, merge_in, last, cscale, li, lg);
   }
   // ... then the rest in blocks of 16 queries dealt to the waves in turn, so
@@ -574,8 +582,8 @@ static void launch_expert_d(const Plan& p) {
   if (p.ex_nw == 1 && p.ex_ib == 1) launch_expert_t<T, D, 1, 1>(p);
   else if (p.ex_nw == 1) launch_expert_t<T, D, 1, 2>(p);
   else if (p.ex_nw == 4) launch_expert_t<T, D, 4, 4>(p);
-  else if (p.ex_nw == 16) launch_expert_t<T, D, 16, 1>(p);
-  else launch_expert_t<T, D, 8, 4>(p);
+  else if (p.ex_ib == 1) launch_expert_t<T, D, 16, 1>(p);
+  else launch_expert_t<T, D, 16, 2>(p);
 }
 
 void launch_expert(const Plan& p) {

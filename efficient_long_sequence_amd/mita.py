@@ -27,7 +27,7 @@ EXPORTS = [
     "mita_workspace_bytes", "mita_forward", "mita_forward_timed", "mita_forward_variant", "mita_dense_attention", "mita_num_stages",
     "mita_stage_name", "mita_events_create", "mita_events_destroy", "mita_events_elapsed",
     "mita_status_str", "mita_version", "mita_forward_train", "mita_backward_workspace_bytes", "mita_backward",
-    "mita_probe_mfma", "mita_probe_copy", "mita_forward_noalloc",
+    "mita_probe_mfma", "mita_probe_copy", "mita_probe_step", "mita_forward_noalloc",
 ]
 
 
@@ -100,6 +100,8 @@ def lib() -> ctypes.CDLL:
     L.mita_probe_mfma.argtypes = [vp, c_int, c_int, vp]
     L.mita_probe_copy.restype = c_int
     L.mita_probe_copy.argtypes = [vp, vp, c_size, vp]
+    L.mita_probe_step.restype = c_int
+    L.mita_probe_step.argtypes = [vp, c_int, c_int, c_int, vp]
     L.mita_status_str.restype = ctypes.c_char_p
     L.mita_status_str.argtypes = [c_int]
     L.mita_version.restype = ctypes.c_char_p
@@ -404,10 +406,16 @@ class MitaFunction(torch.autograd.Function):
         return dQ, dK, dV, None, None, None, None
 
 
-def probe_peaks(mfma_blocks: int = 2048, mfma_iters: int = 16384, copy_mib: int = 1024, reps: int = 3) -> dict:
-    """Measured peaks of this GPU: bf16 matrix-core TFLOP/s (mita_probe_mfma)
-    and device-copy HBM GB/s (bytes read + written, mita_probe_copy); the
-    best of `reps` timed launches after one warm-up."""
+STEP_SHAPES = {0: (8, 4, 256), 1: (16, 1, 256), 2: (8, 2, 512)}  # shape: (waves, blocks per wave, workgroups)
+
+
+def probe_peaks(mfma_blocks: int = 2048, mfma_iters: int = 16384, copy_mib: int = 1024, reps: int = 3,
+                step_iters: int = 2000) -> dict:
+    """Measured peaks of this GPU: bf16 matrix-core TFLOP/s (mita_probe_mfma),
+    device-copy HBM GB/s (bytes read + written, mita_probe_copy) and the
+    useful TFLOP/s of the bare online-softmax step at each launch shape
+    (mita_probe_step: 8 useful 16x16x32 products per block-step); the best of
+    `reps` timed launches after one warm-up."""
     L = lib()
     dev = torch.device("cuda")
     stream = torch.cuda.current_stream(dev).cuda_stream
@@ -430,6 +438,14 @@ def probe_peaks(mfma_blocks: int = 2048, mfma_iters: int = 16384, copy_mib: int 
     t_mfma = best(lambda: _check(L.mita_probe_mfma(out.data_ptr(), mfma_blocks, mfma_iters, stream)))
     t_copy = best(lambda: _check(L.mita_probe_copy(src.data_ptr(), dst.data_ptr(), src.numel(), stream)))
     flops = mfma_blocks * 4 * mfma_iters * 8 * 16384.0
+    step = {}
+    sout = torch.empty(max(w * 64 * g for w, _, g in STEP_SHAPES.values()), dtype=torch.float32, device=dev)
+    for shape, (nw, ib, grid) in STEP_SHAPES.items():
+        t = best(lambda: _check(L.mita_probe_step(sout.data_ptr(), shape, grid, step_iters, stream)))
+        step[f"{nw}x{ib}"] = grid * nw * ib * step_iters * 131072.0 / (t * 1e-3) * 1e-12
     return dict(mfma_bf16_tflops=flops / (t_mfma * 1e-3) * 1e-12, hbm_copy_gbs=2.0 * src.numel() / (t_copy * 1e-3) * 1e-9,
+                step_bf16_tflops=step,
                 probe="mita_probe_mfma (eight independent 16x16x32 bf16 MFMA chains on varied operands), "
-                      "mita_probe_copy (16-byte copy, four loads in flight per thread)")
+                      "mita_probe_copy (16-byte copy, four loads in flight per thread), "
+                      "mita_probe_step (the online-softmax step alone, operands in registers; "
+                      "key: waves x 16-row blocks per wave)")

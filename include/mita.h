@@ -271,10 +271,24 @@ mita_status mita_backward(const void* Q, const void* K, const void* V, const voi
  *                    in all; writes blocks * 256 floats to `out` (device).
  *   mita_probe_copy  copies `bytes` (a multiple of 16) from src to dst
  *                    (device, 16-byte aligned, not overlapping).
+ *   mita_probe_step  the online-softmax step the attention kernels are built
+ *                    on (MiTA tutorial (iwxt.cn) ch.4: softmax over
+ *                    q~ . k / sqrt(d) weighting V; here d = 64, bf16), run
+ *                    `iters` times per 16-row block with every operand in
+ *                    registers: the ceiling of a kernel made of that step at
+ *                    one launch shape.  `shape` 0: workgroups of 8 waves x 4
+ *                    blocks (two waves per SIMD); 1: 16 waves x 1 block (four
+ *                    per SIMD); 2: 8 waves x 2 blocks (two workgroups per
+ *                    compute unit).  One step of one block is 8 useful
+ *                    16x16x32 products (scores and P.V, 131072 flops) plus
+ *                    one for the normaliser.  Writes blocks * (512 or 1024
+ *                    for shape 1) floats to `out` (device).
  * Errors: MITA_ERR_NULL (NULL pointer), MITA_ERR_PARAM (blocks or iters
- * <= 0, bytes not a multiple of 16, misaligned pointer), MITA_ERR_HIP. */
+ * <= 0, shape outside 0..2, bytes not a multiple of 16, misaligned pointer),
+ * MITA_ERR_HIP. */
 mita_status mita_probe_mfma(float* out, int blocks, int iters, void* stream);
 mita_status mita_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
+mita_status mita_probe_step(float* out, int shape, int blocks, int iters, void* stream);
 
 /* Number of timed stages and their names ("pool", "estimate", "score", ...). */
 int mita_num_stages(void);
