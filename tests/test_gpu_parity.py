@@ -148,12 +148,13 @@ def test_deterministic():
         np.testing.assert_array_equal(a[key], b[key], err_msg=key)
 
 
-def test_loose_score_bound_falls_back_to_running_maximum():
-    """The routed-part kernel offsets its softmax by a norm bound on the
-    scores.  A key of huge norm orthogonal to every query makes that bound
-    tens of thousands of binades too loose, so the bounded pass underflows and
-    the group must be recomputed with a running maximum; the output must
-    still match the oracle."""
+def test_huge_norm_key_orthogonal_to_every_query():
+    """A key of huge norm (1000 per element) exactly orthogonal to every
+    query and landmark: its scores are exactly 0, but any offset or bound
+    derived from key norms instead of the scores themselves would be tens of
+    thousands of binades too large and underflow every probability.  The
+    running maximum formed from the scores keeps the output equal to the
+    oracle's."""
     B, H, N, d = 1, 2, 256, 64
     rng = np.random.default_rng(77)
     Q = rng.standard_normal((B, H, N, d)).astype(np.float32)
@@ -165,4 +166,4 @@ def test_loose_score_bound_falls_back_to_running_maximum():
     K[:, :, 7, 32:] = 1000.0  # exactly orthogonal to every query and landmark
     Q, K, V = (synth.f32_to_bf16_bits(x).astype(np.uint32) << 16 for x in (Q, K, V))
     Q, K, V = (x.view(np.float32) for x in (Q, K, V))
-    gh_.run_and_check(Q, K, V, (1, N, 1, 4), N, 1, "bf16", label="loose_bound")
+    gh_.run_and_check(Q, K, V, (1, N, 1, 4), N, 1, "bf16", label="huge_norm_key")
