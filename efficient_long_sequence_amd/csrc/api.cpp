@@ -544,7 +544,7 @@ mita_status mita_probe_copy(const void* src, void* dst, size_t bytes, void* stre
 
 mita_status mita_probe_step(float* out, int shape, int blocks, int iters, void* stream) {
   if (!out) return MITA_ERR_NULL;
-  if (shape < 0 || shape > 2 || blocks <= 0 || iters <= 0 || ((uintptr_t)out & 15u)) return MITA_ERR_PARAM;
+  if (shape < 0 || shape > 3 || blocks <= 0 || iters <= 0 || ((uintptr_t)out & 15u)) return MITA_ERR_PARAM;
   (void)hipGetLastError();
   launch_probe_step(out, shape, blocks, iters, (hipStream_t)stream);
   return hipGetLastError() == hipSuccess ? MITA_OK : MITA_ERR_HIP;

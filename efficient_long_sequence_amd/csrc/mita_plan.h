@@ -196,7 +196,7 @@ void launch_backward(const BPlan& p);
 void launch_probe_mfma(float* out, int blocks, int iters, hipStream_t stream);
 void launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 // the online-softmax step alone (shape 0: 8 waves x 4 blocks, 1: 16 x 1,
-// 2: 8 x 2); probe_step_threads: its workgroup size
+// 2: 8 x 2, 3: 16 x 2); probe_step_threads: its workgroup size
 void launch_probe_step(float* out, int shape, int blocks, int iters, hipStream_t stream);
 int probe_step_threads(int shape);
 // stationary rows per workgroup of the backward's joint landmark pass for m

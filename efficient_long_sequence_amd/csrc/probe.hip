@@ -120,17 +120,20 @@ __global__ __launch_bounds__(NW * 64, WPE) void k_probe_step(float* __restrict__
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
-int probe_step_threads(int shape) { return shape == 1 ? 1024 : 512; }
+int probe_step_threads(int shape) { return (shape == 1 || shape == 3) ? 1024 : 512; }
 
 void launch_probe_step(float* out, int shape, int blocks, int iters, hipStream_t stream) {
   // shape 0: 8 waves x 4 blocks (two waves per SIMD); 1: 16 waves x 1 block
-  // (four per SIMD); 2: 8 waves x 2 blocks (two workgroups per compute unit)
+  // (four per SIMD); 2: 8 waves x 2 blocks (two workgroups per compute
+  // unit); 3: 16 waves x 2 blocks (four per SIMD)
   if (shape == 0)
     hipLaunchKernelGGL((k_probe_step<8, 4, 2>), dim3((unsigned)blocks), dim3(512), 0, stream, out, iters);
   else if (shape == 1)
     hipLaunchKernelGGL((k_probe_step<16, 1, 4>), dim3((unsigned)blocks), dim3(1024), 0, stream, out, iters);
-  else
+  else if (shape == 2)
     hipLaunchKernelGGL((k_probe_step<8, 2, 2>), dim3((unsigned)blocks), dim3(512), 0, stream, out, iters);
+  else
+    hipLaunchKernelGGL((k_probe_step<16, 2, 4>), dim3((unsigned)blocks), dim3(1024), 0, stream, out, iters);
 }
 
 void launch_probe_mfma(float* out, int blocks, int iters, hipStream_t stream) {

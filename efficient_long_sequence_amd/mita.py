@@ -406,7 +406,7 @@ class MitaFunction(torch.autograd.Function):
         return dQ, dK, dV, None, None, None, None
 
 
-STEP_SHAPES = {0: (8, 4, 256), 1: (16, 1, 256), 2: (8, 2, 512)}  # shape: (waves, blocks per wave, workgroups)
+STEP_SHAPES = {0: (8, 4, 256), 1: (16, 1, 256), 2: (8, 2, 512), 3: (16, 2, 256)}  # shape: (waves, blocks per wave, workgroups)
 
 
 def probe_peaks(mfma_blocks: int = 2048, mfma_iters: int = 16384, copy_mib: int = 1024, reps: int = 3,

@@ -279,12 +279,13 @@ mita_status mita_backward(const void* Q, const void* K, const void* V, const voi
  *                    one launch shape.  `shape` 0: workgroups of 8 waves x 4
  *                    blocks (two waves per SIMD); 1: 16 waves x 1 block (four
  *                    per SIMD); 2: 8 waves x 2 blocks (two workgroups per
- *                    compute unit).  One step of one block is 8 useful
- *                    16x16x32 products (scores and P.V, 131072 flops) plus
- *                    one for the normaliser.  Writes blocks * (512 or 1024
- *                    for shape 1) floats to `out` (device).
+ *                    compute unit); 3: 16 waves x 2 blocks.  One step of one
+ *                    block is 8 useful 16x16x32 products (scores and P.V,
+ *                    131072 flops) plus one for the normaliser.  Writes
+ *                    blocks * (512, or 1024 for shapes 1 and 3) floats to
+ *                    `out` (device).
  * Errors: MITA_ERR_NULL (NULL pointer), MITA_ERR_PARAM (blocks or iters
- * <= 0, shape outside 0..2, bytes not a multiple of 16, misaligned pointer),
+ * <= 0, shape outside 0..3, bytes not a multiple of 16, misaligned pointer),
  * MITA_ERR_HIP. */
 mita_status mita_probe_mfma(float* out, int blocks, int iters, void* stream);
 mita_status mita_probe_copy(const void* src, void* dst, size_t bytes, void* stream);

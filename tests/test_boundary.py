@@ -191,7 +191,7 @@ def test_probes_reject_invalid_arguments():
     assert L.mita_probe_copy(A, A, 17, None) == 3
     assert L.mita_probe_copy(A + 8, A, 16, None) == 3
     assert L.mita_probe_step(None, 0, 1, 1, None) == 1
-    assert L.mita_probe_step(A, 3, 1, 1, None) == 3
+    assert L.mita_probe_step(A, 4, 1, 1, None) == 3
     assert L.mita_probe_step(A, -1, 1, 1, None) == 3
     assert L.mita_probe_step(A, 0, 0, 1, None) == 3
     assert L.mita_probe_step(A, 1, 1, 0, None) == 3
