@@ -23,7 +23,7 @@
 //             the exact top-k from the candidates with a block radix select;
 //   k_topk_small  (rows of at most 2048 keys, k <= 64, instead of the
 //             candidate path) rescores 16 rows into LDS and selects each
-//             row's top-k there with a wave-level radix select;
+//             row's top-k there with a wave-level bitwise search;
 //   k_fallback exact streaming top-k for any row whose candidate count was
 //             below k or above capacity (a threshold estimate that missed).
 //
@@ -559,23 +559,82 @@ __global__ __launch_bounds__(256) void k_fallback(const T* __restrict__ K, const
 // 32-key steps w, w + 16, ...; each key row is used by one wave only, so its
 // operand fragments are read straight from global memory, one step ahead)
 // into an LDS tile of raw fp32 scores; then each wave finishes one row with
-// no barrier: a radix select of the k-th largest order-preserving score key
-// (four 8-bit passes over a wave-private LDS histogram, the row's keys held
-// in registers), one pass over the keys in index order that emits every key
+// no barrier: a search for the k-th largest order-preserving score key (one
+// bit a pass from the top, each pass counting the keys at or above a
+// candidate value with one ballot per register of the row's keys; it stops
+// as soon as exactly k keys lie at or above the known leading bits), one
+// pass over the keys in index order that emits every key
 // above that value and, among the keys equal to it, the lowest indices, in
 // ascending order; and the merge of the row's shared-value partials (the
 // rescaled-sum identity of tutorial ch.4, one output dimension per lane).
 // Neither the scores nor candidate keys reach HBM.
-template <typename T, int D>
-__global__ __launch_bounds__(1024) void k_topk_small(const T* __restrict__ K, const T* __restrict__ Qt,
+// Wave-level selection helpers of k_topk_small.  A lane holds NU keys
+// (register u: key index lane + 64 u of the set); nu of them are in use.
+// Number of keys of the wave that are >= t (t >= 1: unused slots hold 0).
+template <int NU>
+__device__ __forceinline__ int wave_count_ge(const uint32_t (&kk)[NU], int nu, uint32_t t) {
+  int c = 0;
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+    if (u < nu) c += (int)__builtin_popcountll(__builtin_amdgcn_ballot_w64(kk[u] >= t));
+  return c;
+}
+// Bitwise search for the k-th largest key T from bit `bit` down: on entry
+// and exit, cge keys are >= prefix and every key that can reach the top k is
+// >= prefix.  Stops when exactly k keys are >= prefix (they are the top k),
+// when the bits run out (prefix = T), or once at most `stop` keys remain.
+template <int NU>
+__device__ __forceinline__ void wave_bit_search(const uint32_t (&kk)[NU], int nu, int k, int stop, int& bit,
+                                                uint32_t& prefix, int& cge) {
+  for (; bit >= 0 && cge != k && cge > stop; --bit) {
+    const uint32_t cand = prefix | (1u << bit);
+    const int c = wave_count_ge(kk, nu, cand);
+    if (c >= k) { prefix = cand; cge = c; }
+  }
+}
+// Writes the top k in ascending index order: every key above T, then the
+// first keys equal to T (by index) until k are taken; with exact (exactly k
+// keys >= prefix) the keys >= prefix.  idx(u): this lane's key index in
+// register u, or -1 for an unused slot; the set is in ascending index order
+// (register-major, then lane).
+template <int NU, class Idx>
+__device__ __forceinline__ void wave_emit_topk(const uint32_t (&kk)[NU], int nu, int k, bool exact, uint32_t prefix,
+                                               int cge, Idx idx, int32_t* out) {
+  const int ngt = exact ? k : wave_count_ge(kk, nu, prefix + 1u);
+  const int krem = k - ngt;
+  int pos = 0, eq_seen = 0;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    if (u < nu) {
+      const int j = idx(u);
+      const bool valid = j >= 0;
+      const bool gt = valid && (exact ? kk[u] >= prefix : kk[u] > prefix);
+      const bool eq = valid && !exact && kk[u] == prefix;
+      const uint64_t be = __builtin_amdgcn_ballot_w64(eq);
+      const int er = eq_seen + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
+      const bool take = gt || (eq && er < krem);
+      const uint64_t bt = __builtin_amdgcn_ballot_w64(take);
+      const int o = pos + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bt >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)bt, 0u));
+      if (take && o < k) out[o] = j;  // (exactly k are taken; the bound only guards memory)
+      pos += (int)__builtin_popcountll(bt);
+      eq_seen += (int)__builtin_popcountll(be);
+    }
+  }
+}
+
+// UMAX: keys per lane (N <= 64 UMAX); the kernel is compiled for 4, 8, 16
+// and 32 so the per-key loops are unrolled to the row's length.
+template <typename T, int D, int UMAX>
+__global__ __launch_bounds__(1024, UMAX <= 8 ? 2 : 1) void k_topk_small(const T* __restrict__ K, const T* __restrict__ Qt,
                                                     const float* __restrict__ vpart, int32_t* __restrict__ topk,
                                                     float* __restrict__ vt32, T* __restrict__ vtT,
                                                     float* __restrict__ lse_lm, int N, int m, int k, int C,
                                                     int stride, int shared) {
-  constexpr int UMAX = SMALL_N / 64;
+  constexpr bool COMPACT = UMAX > 4;  // (the compaction area needs a row stride >= 256)
   extern __shared__ __align__(16) unsigned char smem[];
-  float* S = (float*)smem;                       // [16][stride] raw scores
-  uint32_t* hist = (uint32_t*)(S + 16 * stride); // [16 waves][256]
+  float* S = (float*)smem;  // [16][stride] raw scores
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, li = lane % 16, lg = lane / 16;
   const int bh = blockIdx.y, r0 = blockIdx.x * 16;
   const T* Kh = K + (size_t)bh * N * D;
@@ -588,9 +647,11 @@ __global__ __launch_bounds__(1024) void k_topk_small(const T* __restrict__ K, co
       else zero(qf[dc]);
     }
   }
-  // this wave's row: its first 8 shared-value chunk partials are fetched now,
-  // so their latency hides under the scoring and the selection
-  constexpr int CPRE = 8;
+  // this wave's row: its first shared-value chunk partials are fetched now,
+  // so their latency hides under the scoring and the selection (fewer for
+  // short rows, whose workgroups run two to a compute unit on half the
+  // registers)
+  constexpr int CPRE = UMAX <= 8 ? 2 : 8;
   const size_t rw = (size_t)bh * m + min(r0 + wave, m - 1);
   const float* prw = vpart + rw * C * (D + 4);
   const int ew = lane < D ? lane : 0;
@@ -616,11 +677,18 @@ __global__ __launch_bounds__(1024) void k_topk_small(const T* __restrict__ K, co
       }
     }
   };
+  // (rows of up to 512 keys: at most one step per wave, nothing to prefetch)
+  constexpr bool PF = UMAX > 8;
   StepFrags<T, D> fn;
-  if (wave < nsteps) load_step(fn, wave);
+  if (PF && wave < nsteps) load_step(fn, wave);
   for (int st = wave; st < nsteps; st += 16) {
-    StepFrags<T, D> f = fn;
-    if (st + 16 < nsteps) load_step(fn, st + 16);
+    StepFrags<T, D> f;
+    if constexpr (PF) {
+      f = fn;
+      if (st + 16 < nsteps) load_step(fn, st + 16);
+    } else {
+      load_step(f, st);
+    }
     float sc[8];
     step_scores(f, qf, sc);
 #pragma unroll
@@ -630,7 +698,6 @@ __global__ __launch_bounds__(1024) void k_topk_small(const T* __restrict__ K, co
     }
   }
   __syncthreads();
-  uint32_t* h = hist + wave * 256;
   const int U = (N + 63) / 64;
   {
     const int rl = wave, row = r0 + rl;
@@ -643,70 +710,47 @@ __global__ __launch_bounds__(1024) void k_topk_small(const T* __restrict__ K, co
       const int j = lane + 64 * u;
       kf[u] = (u < U && j < N) ? fkey(Sr[j]) : 0u;  // 0: below every key of a score (the smallest is -inf's)
     }
-    // the k-th largest key value (with multiplicity), 8 bits a pass from the top
-    uint32_t prefix = 0, mask = 0;
-    int krem = k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int x = lane; x < 256; x += 64) h[x] = 0;
-      __builtin_amdgcn_wave_barrier();
+    // the k-th largest key value T, one bit a pass from the top (counts are
+    // ballots over the lane registers).  With more than four keys per lane,
+    // once at most 128 keys can still reach the top k (those >= the bits
+    // found so far) they are moved, in index order, to two registers per
+    // lane through this row's LDS scores (no longer needed), and the search
+    // and the emission continue on those.
+    int32_t* out = topk + r * k;
+    uint32_t prefix = 0;
+    int cge = N;  // keys >= 0: every key of the row (unused slots hold 0)
+    int bit = 31;
+    wave_bit_search(kf, U, k, COMPACT ? 128 : -1, bit, prefix, cge);
+    if (COMPACT && cge != k && bit >= 0) {
+      uint32_t* kb = (uint32_t*)(S + rl * stride);  // cge <= 128 keys, then their indices
+      int* ib = (int*)(kb + 128);
+      int base = 0;
 #pragma unroll
       for (int u = 0; u < UMAX; ++u) {
-        const int j = lane + 64 * u;
-        if (u < U && j < N && (kf[u] & mask) == prefix) atomicAdd(h + ((kf[u] >> shift) & 255u), 1u);
+        if (u < U) {
+          const int j = lane + 64 * u;
+          const bool sel = j < N && kf[u] >= prefix;
+          const uint64_t bs = __builtin_amdgcn_ballot_w64(sel);
+          const int o = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bs >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bs, 0u));
+          if (sel) { kb[o] = kf[u]; ib[o] = j; }
+          base += (int)__builtin_popcountll(bs);
+        }
       }
       __builtin_amdgcn_wave_barrier();
-      // bucket b with (keys in buckets > b) < krem <= (keys in buckets >= b):
-      // lane l holds buckets 4l .. 4l + 3, suffix sums across the lanes
-      const int h0 = h[4 * lane], h1 = h[4 * lane + 1], h2 = h[4 * lane + 2], h3 = h[4 * lane + 3];
-      const int own = h0 + h1 + h2 + h3;
-      int incl = own;
+      uint32_t kc[2];
+      int ic[2];
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int v = __shfl_down(incl, off);
-        if (lane + off < 64) incl += v;
+      for (int v = 0; v < 2; ++v) {
+        const int x = lane + 64 * v;
+        kc[v] = x < base ? kb[x] : 0u;
+        ic[v] = x < base ? ib[x] : -1;
       }
-      const int s4 = incl - own, s3 = s4 + h3, s2 = s3 + h2, s1 = s2 + h1, s0 = s1 + h0;
-      int bsel = -1, above = 0;
-      if (s3 >= krem && s4 < krem) { bsel = 4 * lane + 3; above = s4; }
-      if (s2 >= krem && s3 < krem) { bsel = 4 * lane + 2; above = s3; }
-      if (s1 >= krem && s2 < krem) { bsel = 4 * lane + 1; above = s2; }
-      if (s0 >= krem && s1 < krem) { bsel = 4 * lane; above = s1; }
-      // exactly one lane found it (the keys matching the prefix number at
-      // least krem, and none lie above the top bucket)
-      const uint64_t who = __builtin_amdgcn_ballot_w64(bsel >= 0);
-      const int src = who ? (int)__builtin_ctzll(who) : 0;
-      bsel = __shfl(bsel, src);
-      above = __shfl(above, src);
-      prefix |= (uint32_t)(bsel & 255) << shift;
-      mask |= 0xFFu << shift;
-      krem -= above;
-      // the chosen bucket is taken whole: the remaining bits decide nothing
-      const int inb = __shfl(bsel == 4 * lane + 3 ? h3 : bsel == 4 * lane + 2 ? h2 : bsel == 4 * lane + 1 ? h1 : h0,
-                             src);
-      if (inb == krem) break;
-    }
-    // emit: every key above the k-th value, then the first krem keys equal to
-    // it, in index order
-    int32_t* out = topk + r * k;
-    int pos = 0, eq_seen = 0;
-#pragma unroll
-    for (int u = 0; u < UMAX; ++u) {
-      if (u < U) {
-        const int j = lane + 64 * u;
-        const bool valid = j < N;
-        const uint32_t km = kf[u] & mask;
-        const bool gt = valid && km > prefix, eq = valid && km == prefix;
-        const uint64_t be = __builtin_amdgcn_ballot_w64(eq);
-        const int er = eq_seen + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32),
-                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
-        const bool take = gt || (eq && er < krem);
-        const uint64_t bt = __builtin_amdgcn_ballot_w64(take);
-        const int o = pos + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bt >> 32),
-                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)bt, 0u));
-        if (take && o < k) out[o] = j;  // (exactly k are taken; the bound only guards memory)
-        pos += (int)__builtin_popcountll(bt);
-        eq_seen += (int)__builtin_popcountll(be);
-      }
+      wave_bit_search(kc, 2, k, -1, bit, prefix, cge);
+      wave_emit_topk(kc, 2, k, cge == k, prefix, cge, [&](int v) { return ic[v]; }, out);
+    } else {
+      wave_emit_topk(kf, U, k, cge == k, prefix, cge,
+                     [&](int u) { const int j = lane + 64 * u; return j < N ? j : -1; }, out);
     }
     // shared value of the row: merge its C chunk partials (lane e owns
     // output dim e); every load of a batch is in flight at once
@@ -813,13 +857,19 @@ static void launch_final_t(const Plan& p) {
   if (p.small) {
     // top-k and the shared-value merge on chip; k_final is not needed
     const int stride = (p.N + 63) / 64 * 64 + 1;
-    const size_t lds2 = (size_t)16 * stride * 4 + 16 * 256 * 4;
-    if (lds2 > 65536)
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_topk_small<T, D>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
-    hipLaunchKernelGGL((k_topk_small<T, D>), dim3((unsigned)((p.m + 15) / 16), (unsigned)p.BH), dim3(1024), lds2,
-                       p.stream, (const T*)p.K, (const T*)p.qt, p.vpart, p.topk, p.vt32, (T*)p.vtT, p.lse_lm, p.N,
-                       p.m, p.k, p.C, stride, p.shared);
+    const size_t lds2 = (size_t)16 * stride * 4;
+    auto go = [&](auto fn) {
+      if (lds2 > 65536)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)lds2);
+      hipLaunchKernelGGL(fn, dim3((unsigned)((p.m + 15) / 16), (unsigned)p.BH), dim3(1024), lds2, p.stream,
+                         (const T*)p.K, (const T*)p.qt, p.vpart, p.topk, p.vt32, (T*)p.vtT, p.lse_lm, p.N, p.m, p.k,
+                         p.C, stride, p.shared);
+    };
+    if (p.N <= 256) go(&k_topk_small<T, D, 4>);
+    else if (p.N <= 512) go(&k_topk_small<T, D, 8>);
+    else if (p.N <= 1024) go(&k_topk_small<T, D, 16>);
+    else go(&k_topk_small<T, D, SMALL_N / 64>);
     return;
   }
   // candidates, then the selected keys (or, before the selection, the

@@ -139,6 +139,28 @@ def test_sparse_overflow_fallback_with_ties():
     gh_.run_and_check(Q, K, V, (1, N, 1, 16), k, 1, "bf16", queries=np.arange(0, N, 7), label="overflow")
 
 
+@pytest.mark.parametrize("n_distinct", [10, 5])
+def test_small_rows_with_tie_groups(n_distinct):
+    """Rows of 1000 keys (selected on chip) whose keys repeat n_distinct rows:
+    every score comes in tie groups of ~1000/n_distinct equal values.  With
+    10 groups (~100 keys each) the top group mostly fits the on-chip
+    selection's compacted set (at most 128 keys), so the search finishes
+    there among equal keys; with 5 (~200 each) it never compacts.  Either way the k = 40 selected keys are
+    the lowest indices of the top group, as the oracle's."""
+    N, d, k = 1000, 64, 40
+    rng = np.random.default_rng(100 + n_distinct)
+    Q, K0, V = _inputs(1, 2, N, d, "iid", 0, "bf16", seed=41 + n_distinct)
+    K = K0[:, :, rng.integers(0, n_distinct, size=N)].copy()
+    pool = (1, N, 1, 10)
+    gpu = gh_.run_gpu(Q, K, V, pool, k, 1, "bf16")
+    for h in range(2):
+        Qt = mo.landmarks(Q[0, h].astype(np.float64), 1, N, 1, 10, "bf16")
+        S = mo.landmark_scores(Qt, K[0, h].astype(np.float64))
+        for r in range(10):
+            np.testing.assert_array_equal(gpu["topk"][0, h, r], mo.topk_row(S[r], k)[0])
+    gh_.run_and_check(Q, K, V, pool, k, 1, "bf16", label=f"tie_groups_{n_distinct}")
+
+
 def test_deterministic():
     w = WORKLOADS["ade_n1024"]
     Q, K, V = synth.make_from_workload(w)
