@@ -65,7 +65,10 @@ def algorithmic(w, stage: str):
 
     score:  every landmark row against every key: one logit and one value sum
             of length d (4 d N m flops); reads K and V once and Q~, writes v~.
-            Overhead: the split-N partials of v~ (written, then merged).
+            Overhead: reported as 0 here; the kernel also writes the split-N
+            partials of v~ (B H m C (d + 4) fp32, C key chunks from the launch
+            plan, 36 MB at N = 1M) and the score records of the candidate
+            filter (data-dependent), which the measured traffic includes.
     route:  every query against every landmark: the routing score, which is
             also the shared logit, and the shared value sum (4 d N m flops);
             reads Q, Q~ and v~, writes the routes.  Overhead: the shared part
@@ -247,8 +250,8 @@ def ingest(trace_dir: str, fetch_dir: str, write_dir: str, workload: str, comman
 
     def short(name):
         n = name.split("(")[0]
-        for key in ("k_score", "k_expert", "k_route_shared", "k_route", "k_attend", "k_final", "k_pool", "k_scatter",
-                    "k_est", "k_tau", "k_scan", "k_zero", "k_fallback"):
+        for key in ("k_score", "k_expert", "k_route_shared", "k_route", "k_attend", "k_final", "k_pool_short", "k_pool",
+                    "k_scatter", "k_est", "k_tau", "k_scan", "k_topk_small", "k_fallback"):
             if f"{len(key)}{key}I" in n or n.endswith(key) or f"::{key}" in n or f"{len(key)}{key}E" in n:
                 return key
         return n[:48]

@@ -255,8 +255,7 @@ mita_status run(const void* Q, const void* K, const void* V, void* O, mita_dtype
 
   (void)hipGetLastError();  // clear any earlier sticky launch error
   tm.begin(ST_POOL);
-  launch_zero(p);
-  launch_pool(p);
+  launch_pool(p);  // (also clears the zero-initialised counters)
   tm.end(ST_POOL);
   tm.begin(ST_EST);
   if (!p.dense) launch_estimate(p);

@@ -116,8 +116,7 @@ struct Plan {
 };
 
 // Launchers (one per translation unit); each enqueues on plan.stream.
-void launch_zero(const Plan& p);
-void launch_pool(const Plan& p);
+void launch_pool(const Plan& p);  // also clears zero_bytes at zero_begin
 void launch_estimate(const Plan& p);
 void launch_score(const Plan& p);
 void launch_final(const Plan& p);

@@ -157,62 +157,124 @@ __global__ __launch_bounds__(NW * 64) void k_route(const T* __restrict__ Q, cons
 // blocks), so the longest items start first and the short ones fill the tail.
 constexpr int SCAN_BUCKETS = 128;  // T <= 2048 queries per item
 
+// atomicAdd(&base[b], 1) for every lane with b >= 0.  When all of a
+// wave's lanes that add use one b (small experts all fall in the first size
+// bucket), the wave makes a single LDS atomic and hands out the slots by
+// rank; otherwise each lane adds on its own.  Returns the lane's slot, or -1
+// for b < 0.
+__device__ __forceinline__ int wave_bucket_add(int* base, int b) {
+  const uint64_t act = __builtin_amdgcn_ballot_w64(b >= 0);
+  if (!act) return -1;
+  const int lane = threadIdx.x % 64;
+  const int first = (int)__builtin_ctzll(act);
+  const int b0 = __shfl(b, first);
+  const uint64_t same = __builtin_amdgcn_ballot_w64(b == b0) & act;
+  if (same == act) {
+    int old = 0;
+    if (lane == first) old = atomicAdd(base + b0, (int)__builtin_popcountll(act));
+    old = __shfl(old, first);
+    return b >= 0 ? old + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(act >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)act, 0u))
+                  : -1;
+  }
+  return b >= 0 ? atomicAdd(base + b, 1) : -1;
+}
+
+// Counts staged in LDS per slot (read coalesced, then each thread walks its
+// contiguous segment there); above this many experts they are read from
+// global memory directly.
+constexpr int SCAN_STAGE = 8192;
+
 __global__ __launch_bounds__(1024) void k_scan(const int* __restrict__ counts, int* __restrict__ gpre,
                                                WorkItem* __restrict__ wl, int* __restrict__ wl_count,
                                                int E, int m, int s, int T, int UB, int* __restrict__ efirst,
                                                int* __restrict__ epart) {
-  __shared__ int sn[1024], stl[1024];
+  __shared__ int sn[32], stl[32];  // wave totals, then exclusive wave offsets
   __shared__ int bcnt[SCAN_BUCKETS];
+  __shared__ int cst[SCAN_STAGE];
   const int tid = threadIdx.x;
   const int seg = (E + 1023) / 1024;
   const int lo = min(E, tid * seg), hi = min(E, lo + seg);
   auto bucket = [&](int rem) { return min(SCAN_BUCKETS - 1, (rem + 15) / 16 - 1); };
+  const bool staged = E <= SCAN_STAGE;
   for (int t = 0; t < s; ++t) {
-    const int* c = counts + (size_t)t * E;
+    const int* cg = counts + (size_t)t * E;
+    if (staged) {
+      for (int x0 = tid; x0 < E; x0 += 8 * 1024) {  // eight loads in flight per thread
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = x0 + u * 1024 < E ? cg[x0 + u * 1024] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (x0 + u * 1024 < E) cst[x0 + u * 1024] = v[u];
+      }
+    }
+    const int* c = staged ? cst : cg;
     if (tid < SCAN_BUCKETS) bcnt[tid] = 0;
     __syncthreads();
     int n_sum = 0, t_sum = 0;
-    for (int x = lo; x < hi; ++x) {
-      const int n = c[x];
+    // (every thread runs the same trip count, so the wave-wide counting
+    // below sees all its lanes)
+    for (int i = 0; i < seg; ++i) {
+      const int x = lo + i;
+      const int n = x < hi ? c[x] : 0;
       n_sum += n;
       t_sum += n / T;
-      if (n % T) atomicAdd(bcnt + bucket(n % T), 1);
+      wave_bucket_add(bcnt, n % T ? bucket(n % T) : -1);
     }
-    sn[tid] = n_sum;
-    stl[tid] = t_sum;
+    // inclusive scan of the segment totals: within each wave by shuffles,
+    // then over the 16 wave totals
+    const int lane = tid % 64, wv = tid / 64;
+    int in_n = n_sum, in_t = t_sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int yn = __shfl_up(in_n, off), yt = __shfl_up(in_t, off);
+      if (lane >= off) { in_n += yn; in_t += yt; }
+    }
+    if (lane == 63) { sn[wv] = in_n; stl[wv] = in_t; }
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
-      const int a = tid >= off ? sn[tid - off] : 0, b = tid >= off ? stl[tid - off] : 0;
-      __syncthreads();
-      sn[tid] += a;
-      stl[tid] += b;
-      __syncthreads();
-    }
-    const int nfull = stl[1023];
-    if (tid == 0) {  // partial items: bucket starts, largest bucket first
-      int acc = nfull;
-      for (int b = SCAN_BUCKETS - 1; b >= 0; --b) {
-        const int n = bcnt[b];
-        bcnt[b] = acc;
-        acc += n;
+    if (wv == 0) {
+      // wave totals -> exclusive wave offsets (lanes 0..15)
+      int wn = lane < 16 ? sn[lane] : 0, wt = lane < 16 ? stl[lane] : 0;
+      const int own_n = wn, own_t = wt;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) {
+        const int yn = __shfl_up(wn, off), yt = __shfl_up(wt, off);
+        if (lane >= off) { wn += yn; wt += yt; }
       }
-      wl_count[t] = acc;
+      const int nfull = __shfl(wt, 15);
+      // partial items: bucket starts, largest bucket first; lane l holds
+      // buckets 127 - 2l and 126 - 2l
+      const int bh_ = SCAN_BUCKETS - 1 - 2 * lane, bl_ = bh_ - 1;
+      const int ch = bcnt[bh_], cl = bcnt[bl_];
+      int inc = ch + cl;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(inc, off);
+        if (lane >= off) inc += y;
+      }
+      const int start = nfull + inc - (ch + cl);
+      bcnt[bh_] = start;
+      bcnt[bl_] = start + ch;
+      if (lane == 63) wl_count[t] = nfull + inc;
+      if (lane < 16) { sn[lane + 16] = wn - own_n; stl[lane + 16] = wt - own_t; }
     }
     __syncthreads();
-    int nb = sn[tid] - n_sum, tb = stl[tid] - t_sum;
+    int nb = in_n - n_sum + sn[16 + wv], tb = in_t - t_sum + stl[16 + wv];
     WorkItem* w = wl + (size_t)t * UB;
-    for (int x = lo; x < hi; ++x) {
-      const int n = c[x];
-      gpre[(size_t)t * E + x] = nb;
+    for (int i = 0; i < seg; ++i) {
+      const int x = lo + i;
+      const bool in = x < hi;
+      const int n = in ? c[x] : 0;
       const int nf = n / T;
-      if (efirst) efirst[(size_t)t * E + x] = tb;
-      for (int q = 0; q < nf; ++q) w[tb++] = WorkItem{nb + q * T, T, x, 0};
-      int pi = -1;
-      if (n % T) {
-        pi = atomicAdd(bcnt + bucket(n % T), 1);
-        w[pi] = WorkItem{nb + nf * T, n % T, x, 0};
+      if (in) {
+        gpre[(size_t)t * E + x] = nb;
+        if (efirst) efirst[(size_t)t * E + x] = tb;
+        for (int q = 0; q < nf; ++q) w[tb++] = WorkItem{nb + q * T, T, x, 0};
       }
-      if (epart) epart[(size_t)t * E + x] = pi;
+      const int pi = wave_bucket_add(bcnt, in && n % T ? bucket(n % T) : -1);
+      if (pi >= 0) w[pi] = WorkItem{nb + nf * T, n % T, x, 0};
+      if (in && epart) epart[(size_t)t * E + x] = pi;
       nb += n;
     }
     __syncthreads();
