@@ -82,7 +82,11 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
 
   p.dense = N <= NSMALL ? 1 : 0;
   p.small = (N <= SMALL_N && k <= SMALL_K) ? 1 : 0;
-  p.capg = p.dense ? N : CAPG;
+  {
+    int cap = CAPG_MIN;
+    while (cap < 8 * k && cap < CAPG) cap *= 2;
+    p.capg = p.dense ? N : cap;
+  }
   if (!p.dense) {
     p.sigma = k / 32 > 1 ? k / 32 : 1;
     p.NS = N / p.sigma;

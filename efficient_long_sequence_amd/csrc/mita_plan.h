@@ -16,8 +16,13 @@ constexpr int NSMALL = 8192;
 constexpr int SMALL_N = 2048;
 constexpr int SMALL_K = 64;
 // Candidate capacity per landmark row in sparse mode: the selection kernel
-// gathers a row's candidates into LDS (8192 x 8 bytes).
+// gathers a row's candidates into LDS (up to 8192 x 8 bytes).  The threshold
+// admits about 2.3 k keys per row, so the capacity follows k (8 k rounded up
+// to a power of two, at least 2048), and a row past it falls back to the
+// exact kernel; smaller buffers let more selection workgroups share a
+// compute unit.
 constexpr int CAPG = 8192;
+constexpr int CAPG_MIN = 2048;
 // Sparse mode: the least room for score records a lane keeps per (landmark
 // row, key chunk, lane group) (more when the expected count is larger); a lane
 // that needs more marks its row for the exact fallback.

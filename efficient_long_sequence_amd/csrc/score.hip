@@ -298,6 +298,60 @@ __device__ void emit_topk(uint64_t* a, int k, int32_t* out) {
   for (int j = threadIdx.x; j < k; j += blockDim.x) out[j] = (int32_t)a[j];
 }
 
+// Ascending sort of 64 E values held E per lane (position lane * E + i) by
+// one wave: a bitonic network whose strides below E swap registers and the
+// others exchange with lane ^ (stride / E) by shuffles; no barrier.
+template <int E>
+__device__ __forceinline__ void wave_sort_asc(uint32_t (&v)[E], int lane) {
+  constexpr int P = 64 * E;
+#pragma unroll
+  for (int size = 2; size <= P; size <<= 1) {
+#pragma unroll
+    for (int stride = size / 2; stride > 0; stride >>= 1) {
+      if (stride >= E) {
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+          const int p = lane * E + i;
+          const uint32_t o = (uint32_t)__shfl_xor((int)v[i], stride / E);
+          const bool asc = (p & size) == 0, lower = (p & stride) == 0;
+          v[i] = asc == lower ? min(v[i], o) : max(v[i], o);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+          const int j = i ^ stride;
+          if (j > i) {
+            const bool asc = ((lane * E + i) & size) == 0;
+            const uint32_t x = v[i], y = v[j];
+            v[i] = asc ? min(x, y) : max(x, y);
+            v[j] = asc ? max(x, y) : min(x, y);
+          }
+        }
+      }
+    }
+  }
+}
+
+// emit_topk for k <= 64 E by wave 0 alone (the others return): the keys'
+// indices sorted in registers, then written in order.
+template <int E>
+__device__ __forceinline__ void wave_emit_sorted(const uint64_t* a, int k, int32_t* out) {
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  uint32_t v[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int p = lane * E + i;
+    v[i] = p < k ? ckey_idx(a[p]) : 0xFFFFFFFFu;
+  }
+  wave_sort_asc<E>(v, lane);
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int p = lane * E + i;
+    if (p < k) out[p] = (int32_t)v[i];
+  }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_final(const float* __restrict__ vpart, const uint64_t* __restrict__ cand,
                                                const float* __restrict__ rec_sc, const int32_t* __restrict__ rec_st,
@@ -451,13 +505,45 @@ __global__ __launch_bounds__(256) void k_final(const float* __restrict__ vpart, 
   }
   if (tid == 0) fail[r] = 0;
   __syncthreads();
-  // radix select of the k-th largest key, 8 bits a pass from the top; the
-  // keys are distinct, so exactly k of them reach the final prefix
+  // radix select of the k-th largest key, 8 bits a pass; the keys are
+  // distinct, so exactly k of them reach the final prefix.  The candidates
+  // all lie near the top of the row, so their leading bits (sign, most of
+  // the exponent) agree: the passes start at the highest bit where the
+  // smallest and the largest key differ (a histogram of identical leading
+  // digits would put every count on one LDS address).
   __shared__ int hist[256];
   __shared__ int s_b, s_above, s_in, s_nsel;
-  uint64_t prefix = 0, mask = 0;
+  __shared__ uint64_t s_lo[4], s_hi[4];
+  {
+    uint64_t lo = ~0ull, hi = 0;
+    for (int j = tid; j < cnt; j += 256) {
+      const uint64_t key = a[j];
+      lo = key < lo ? key : lo;
+      hi = key > hi ? key : hi;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const uint64_t ol = __shfl_xor(lo, off), oh = __shfl_xor(hi, off);
+      lo = ol < lo ? ol : lo;
+      hi = oh > hi ? oh : hi;
+    }
+    if ((tid & 63) == 0) { s_lo[tid >> 6] = lo; s_hi[tid >> 6] = hi; }
+  }
+  __syncthreads();
+  uint64_t klo = s_lo[0], khi = s_hi[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) {
+    klo = s_lo[w] < klo ? s_lo[w] : klo;
+    khi = s_hi[w] > khi ? s_hi[w] : khi;
+  }
+  // bits above hb are the same in every key (cnt >= k >= 1 distinct keys)
+  const int hb = klo == khi ? 0 : 63 - __builtin_clzll(klo ^ khi);
+  uint64_t mask = hb >= 63 ? 0ull : ~((2ull << hb) - 1ull);
+  uint64_t prefix = khi & mask;
   int krem = k;
-  for (int shift = 56; shift >= 0; shift -= 8) {
+  // (a digit may also cover known bits above the unknown ones: those are the
+  // same in every key still matching the prefix, so the histogram is unchanged)
+  for (int shift = hb >= 7 ? hb - 7 : 0;;) {
     hist[tid] = 0;
     __syncthreads();
     for (int j = tid; j < cnt; j += 256) {
@@ -489,7 +575,8 @@ __global__ __launch_bounds__(256) void k_final(const float* __restrict__ vpart, 
     krem -= s_above;
     const bool whole = s_in == krem;  // the bucket's keys are all taken
     __syncthreads();
-    if (whole) break;
+    if (whole || shift == 0) break;  // (after the pass at bit 0 every bit is known)
+    shift = shift >= 8 ? shift - 8 : 0;
   }
   uint64_t* sel = a + capg;
   if (tid == 0) s_nsel = 0;
@@ -499,7 +586,14 @@ __global__ __launch_bounds__(256) void k_final(const float* __restrict__ vpart, 
     if ((key & mask) >= prefix) sel[atomicAdd(&s_nsel, 1)] = key;
   }
   __syncthreads();
-  emit_topk(sel, k, topk + r * k);
+  // the selected indices in ascending order: one wave sorts up to 512 of
+  // them in registers (a block-wide sort pays a barrier per network stage)
+  int32_t* out = topk + r * k;
+  if (k <= 64) wave_emit_sorted<1>(sel, k, out);
+  else if (k <= 128) wave_emit_sorted<2>(sel, k, out);
+  else if (k <= 256) wave_emit_sorted<4>(sel, k, out);
+  else if (k <= 512) wave_emit_sorted<8>(sel, k, out);
+  else emit_topk(sel, k, out);
 }
 
 // Exact streaming top-k of one landmark row over all N keys (fp32 dot
