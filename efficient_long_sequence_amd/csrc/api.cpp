@@ -94,7 +94,7 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
     const double lam = (double)k / p.sigma;
     int J = (int)std::ceil(lam + 6.0 * std::sqrt(lam) + 3.0);
     p.J = J > p.G ? p.G : J;
-    const long long est_target = 512;
+    const long long est_target = 2048;  // (few sample groups per workgroup: each costs a load round trip)
     int gpb = ceil_div((long long)p.G * p.BH * p.sc_rt, est_target);
     p.est_gpb = gpb < 1 ? 1 : gpb;
     // records per (row, chunk, lane group): the threshold admits about 2.3 k

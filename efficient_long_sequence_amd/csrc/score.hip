@@ -118,19 +118,6 @@ __global__ void k_fill(float* __restrict__ p, int n, float v) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = v;
 }
 
-__global__ __launch_bounds__(256) void k_tau(const float* __restrict__ gmax, float* __restrict__ tau,
-                                             float* __restrict__ mhat, int G, int J) {
-  __shared__ float a[512];
-  const size_t r = blockIdx.x;
-  const int P = next_pow2(G);
-  for (int i = threadIdx.x; i < P; i += blockDim.x) a[i] = i < G ? gmax[r * G + i] : -INFINITY;
-  __syncthreads();
-  block_bitonic_sort(a, P, true);
-  if (threadIdx.x == 0) {
-    tau[r] = a[J - 1];
-    mhat[r] = a[0];
-  }
-}
 
 // ---------------------------------------------------------------------------
 // fused scores, partial shared values and candidates
@@ -349,6 +336,36 @@ __device__ __forceinline__ void wave_emit_sorted(const uint64_t* a, int k, int32
   for (int i = 0; i < E; ++i) {
     const int p = lane * E + i;
     if (p < k) out[p] = (int32_t)v[i];
+  }
+}
+
+// Per landmark row: the J-th largest of its G <= 512 sample-group maxima is
+// the candidate threshold tau, the largest one the first softmax offset.
+// One wave per row (four rows per workgroup): the maxima, as order-preserving
+// keys, sorted in registers.
+__global__ __launch_bounds__(256) void k_tau(const float* __restrict__ gmax, float* __restrict__ tau,
+                                             float* __restrict__ mhat, int rows, int G, int J) {
+  const int lane = threadIdx.x % 64;
+  const size_t r = (size_t)blockIdx.x * 4 + threadIdx.x / 64;
+  if (r >= (size_t)rows) return;  // wave-uniform; no barrier follows
+  uint32_t v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int p = lane * 8 + i;
+    v[i] = p < G ? fkey(gmax[r * G + p]) : 0u;  // 0: below every key of a score
+  }
+  wave_sort_asc<8>(v, lane);
+  // position 511 holds the largest, 512 - J the J-th largest
+  const int pj = 512 - J;
+  uint32_t kj = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (i == pj % 8) kj = v[i];
+  kj = (uint32_t)__shfl((int)kj, pj / 8);
+  const uint32_t kmax = (uint32_t)__shfl((int)v[7], 63);
+  if (lane == 0) {
+    tau[r] = fkey_inv(kj);
+    mhat[r] = fkey_inv(kmax);
   }
 }
 
@@ -912,7 +929,9 @@ static void launch_score_t(const Plan& p) {
     dim3 grid((unsigned)((p.G + p.est_gpb - 1) / p.est_gpb), (unsigned)p.sc_rt, (unsigned)p.BH);
     hipLaunchKernelGGL((k_est<T, D, NW, IB>), grid, dim3(NW * 64), 0, p.stream, (const T*)p.K, (const T*)p.qt,
                        p.gmax, p.N, p.m, p.sigma, p.NS, p.G, p.est_gpb);
-    hipLaunchKernelGGL(k_tau, dim3((unsigned)(p.BH * p.m)), dim3(256), 0, p.stream, p.gmax, p.tau, p.mhat, p.G, p.J);
+    const int rows = p.BH * p.m;
+    hipLaunchKernelGGL(k_tau, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, p.stream, p.gmax, p.tau, p.mhat, rows, p.G,
+                       p.J);
   }
 }
 
