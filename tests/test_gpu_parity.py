@@ -77,6 +77,10 @@ EDGE = {
     # the widest routing (s = 8 of m = 16; s = 6 takes the same kernel form)
     "s8_m16": (1, 2, 1, 2048, 64, 1, 16, 32, 8, "clustered", 8, "bf16"),
     "s6_f32": (1, 1, 12, 16, 32, 3, 4, 10, 6, "iid", 0, "f32"),
+    # on-chip selection with eight keys per lane (rows of 257..512 keys, the
+    # compacting search) and with 64 keys selected (the largest on-chip k)
+    "small_n400": (1, 2, 20, 20, 64, 4, 4, 30, 1, "clustered", 8, "bf16"),
+    "small_n512_k64": (1, 1, 1, 512, 64, 1, 8, 64, 2, "runs", 8, "bf16"),
 }
 
 
