@@ -113,8 +113,41 @@ def test_backward_parity(label):
     seed = zlib.crc32(label.encode()) % 1000
     Q, K, V = synth.make(B, H, N, d, kind, nc, dtype, seed)
     dO = synth.make_grad(B, H, N, d, dtype, seed)
+    _check_backward(label, CASES[label], Q, K, V, dO)
+
+
+# Inputs far from unit scale (powers of two, exact in bf16): V and dO scale
+# the gradients linearly; Q up with K down leaves the routed logits unchanged
+# while pooling, routing and the shared logits run at shifted magnitudes;
+# Q and K together sharpen every softmax.  The bar is relative to each
+# gradient's largest entry, so it needs no rescaling.
+SCALED = {
+    # label: (case, factor on Q, on K, on V, on dO)
+    "v_up12_do_down8": ("long_s2", 1.0, 1.0, 2.0 ** 12, 2.0 ** -8),
+    "q_up4_k_down4": ("ade_2d", 2.0 ** 4, 2.0 ** -4, 1.0, 1.0),
+    "qk_up2_v_down12": ("long_s2", 2.0, 2.0, 2.0 ** -12, 1.0),
+}
+
+
+@pytest.mark.parametrize("label", list(SCALED))
+def test_backward_scaled(label):
+    case, fq, fk, fv, fd = SCALED[label]
+    B, H, gh, gw, d, lh, lw, k, s, kind, nc, dtype, variant = CASES[case]
+    N = gh * gw
+    seed = zlib.crc32(case.encode()) % 1000
+    Q, K, V = synth.make(B, H, N, d, kind, nc, dtype, seed)
+    dO = synth.make_grad(B, H, N, d, dtype, seed)
+    _check_backward(label, CASES[case], Q * np.float32(fq), K * np.float32(fk), V * np.float32(fv),
+                    dO * np.float32(fd))
+
+
+def _check_backward(label, case, Q, K, V, dO):
+    B, H, gh, gw, d, lh, lw, k, s, kind, nc, dtype, variant = case
+    N = gh * gw
     gh_.say(f"[gpu] backward {label} B={B} H={H} N={N} d={d} m={lh * lw} k={k} s={s} {dtype} {variant}")
     r = _run(Q, K, V, dO, (gh, gw, lh, lw), k, s, dtype, variant)
+    for key in ("O", "dQ", "dK", "dV"):
+        assert np.isfinite(r[key]).all(), f"{label}: non-finite values in {key}"
     for b in range(B):
         for h in range(H):
             I, e = r["topk"][b, h], r["route"][b, h]
