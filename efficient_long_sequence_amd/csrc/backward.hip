@@ -193,6 +193,11 @@ __device__ __forceinline__ void grad_stream(unsigned char* smem, int nsteps, con
     src.prefetch(1);
     ld.store(b0);
   }
+  // Every load issued so far has landed on every path into the loop (the
+  // stationary rows included): otherwise the compiler's wait bookkeeping
+  // merges a path where one may still be pending and waits for the step's
+  // own staging loads before the step's first product.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int st = 0; st < nsteps; ++st) {
     unsigned char* cur = (st & 1) ? b1 : b0;
@@ -266,8 +271,11 @@ struct SrcRows {
 // delta per entry from Lv, Dv), read through the permutation instead of from
 // copies in that order.  Each thread's index for the step it stages next is
 // fetched one step earlier (prefetch), so a row's address never waits on a
-// global load.  bf16 staging map: thread t < 32 * CPR stages row t / CPR of
-// a step (one 16-byte chunk), thread t < 32 the entry t.
+// global load: the fetched value is kept raw and only checked and clamped
+// when it is used (a clamp at fetch time would make the wave wait for that
+// load, and with it for the row loads issued just before).  bf16 staging
+// map: thread t < 32 * CPR stages row t / CPR of a step (one 16-byte chunk),
+// thread t < 32 the entry t.
 template <typename T, int D>
 struct SrcPerm {
   static_assert(sizeof(T) == 2, "the staging map above is the bf16 one");
@@ -279,28 +287,33 @@ struct SrcPerm {
   const int32_t* perm;
   int a, e, N;
   float cs, cn;
-  mutable int ridx = -1, eidx = -1;
+  mutable int ridx = -1, eidx = -1;  // raw permutation entries (-1: none)
   __device__ void prefetch(int st) const {
     const int tid = threadIdx.x;
     const int j = a + st * 32 + tid / CPR, je = a + st * 32 + tid;
-    ridx = (tid < 32 * CPR && j < e) ? min(max(perm[j], 0), N - 1) : -1;
-    eidx = (tid < 32 && je < e) ? min(max(perm[je], 0), N - 1) : -1;
+    ridx = -1;
+    eidx = -1;
+    if (tid < 32 * CPR && j < e) ridx = perm[j];
+    if (tid < 32 && je < e) eidx = perm[je];
   }
   __device__ auto ry(int) const {
     const T* b = Y;
-    const int x = ridx;
-    return [=](int) -> const T* { return x >= 0 ? b + (size_t)x * D : nullptr; };
+    const int x = ridx, n = N;
+    return [=](int) -> const T* { return x >= 0 ? b + (size_t)min(x, n - 1) * D : nullptr; };
   }
   __device__ auto rz(int) const {
     const T* b = Z;
-    const int x = ridx;
-    return [=](int) -> const T* { return x >= 0 ? b + (size_t)x * D : nullptr; };
+    const int x = ridx, n = N;
+    return [=](int) -> const T* { return x >= 0 ? b + (size_t)min(x, n - 1) * D : nullptr; };
   }
   __device__ auto re(int) const {
     const float* l = Lv;
     const float* d = Dv;
-    const int x = eidx;
-    return [=](int) -> float2 { return x >= 0 ? make_float2(l[x], d[x]) : make_float2(0.f, 0.f); };
+    const int x = eidx, n = N;
+    return [=](int) -> float2 {
+      const int y = min(x, n - 1);
+      return x >= 0 ? make_float2(l[y], d[y]) : make_float2(0.f, 0.f);
+    };
   }
   __device__ int nv(int st) const { return min(32, e - a - st * 32); }
   __device__ float cscale(int) const { return cs; }
@@ -1170,10 +1183,13 @@ static void launch_backward_t(const BPlan& p) {
   // queries: slots s-1 .. 1 store parts, slot 0 finishes dQ
   {
     // three 16-query blocks per wave for bf16 (no transposed values or
-    // second accumulator in this pass leaves the registers for it)
+    // second accumulator in this pass leaves the registers for it), in
+    // four-wave workgroups: two per compute unit, so one's per-step barrier
+    // and staging overlap the other's arithmetic
     constexpr int IBQ = sizeof(T) == 2 ? 3 : IB;
-    auto f1 = &k_bwd_q<T, D, NW, IBQ, false>;
-    auto f0 = &k_bwd_q<T, D, NW, IBQ, true>;
+    constexpr int NWQ = sizeof(T) == 2 ? 4 : NW;
+    auto f1 = &k_bwd_q<T, D, NWQ, IBQ, false>;
+    auto f0 = &k_bwd_q<T, D, NWQ, IBQ, true>;
     const size_t lq = lds + (size_t)k * 4;
     allow_lds(f1, lq);
     allow_lds(f0, lq);
@@ -1181,7 +1197,7 @@ static void launch_backward_t(const BPlan& p) {
       const int32_t* perm = p.bk.perm + (size_t)t * BH * N;
       const WorkItem* wl = p.bk.wl + (size_t)t * p.bk.UB;
       const int* wlc = p.bk.wl_count + t;
-      hipLaunchKernelGGL(t > 0 ? f1 : f0, dim3((unsigned)p.bk.UB), dim3(NW * 64), lq, st, (const T*)p.Q,
+      hipLaunchKernelGGL(t > 0 ? f1 : f0, dim3((unsigned)p.bk.UB), dim3(NWQ * 64), lq, st, (const T*)p.Q,
                          (const T*)p.K, (const T*)p.V, (const T*)p.dO, (const T*)p.qt, (const T*)p.vt, p.lse, p.Dn,
                          p.topk, perm, wl, wlc, p.dqt, p.qpart, (T*)p.dQ, N, m, k, s, t, BH, p.shared ? m : 0,
                          p.gh, p.gw, p.lh, p.lw, p.cscale, p.cscale_sh, p.cnat, p.cnat_sh);
@@ -1191,7 +1207,7 @@ static void launch_backward_t(const BPlan& p) {
 
 // Rows per workgroup of every backward kernel for a dtype (the plan's R).
 int backward_rows(int dtype, int m) { return dtype == 1 ? 8 * 16 * stat_blocks(m, 2) : 4 * 16 * 1; }
-int backward_query_rows(int dtype) { return dtype == 1 ? 8 * 16 * 3 : 4 * 16 * 1; }
+int backward_query_rows(int dtype) { return dtype == 1 ? 4 * 16 * 3 : 4 * 16 * 1; }
 int backward_lm4_rows(int dtype, int m) { return dtype == 1 ? 8 * 16 * stat_blocks(m, 4) : 4 * 16 * 1; }
 
 void launch_backward(const BPlan& p) {
