@@ -12,7 +12,9 @@
 // log2-sum-exp L, so a probability is exp2(score * cscale - L) with no
 // running maximum.  The gradient of a softmax entry t is
 // dS_t = P_t (dP_t - delta), with dP_t = g . w_t (g the upstream gradient of
-// the softmax's output, w_t the entry's value) and delta = g . output.
+// the softmax's output, w_t the entry's value) and delta = g . output; the
+// matrix-core product that forms dP_t starts from -delta instead of zero, so
+// it yields dP_t - delta directly.
 //
 // One step shape serves every pass: a workgroup keeps 16*IB*NW "stationary"
 // rows in registers (matrix-core columns) and streams 32 "entries" at a time
@@ -66,8 +68,8 @@ __device__ __forceinline__ void tr_frag(Frag<__bf16>& f, const __bf16* rows, int
   f.v = __builtin_shufflevector(a4, b4, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// LDS of one step: Y (row-major + transposed), Z (likewise), then L and delta
-// of the 32 entries.
+// LDS of one step: Y (row-major + transposed), Z (likewise), then L and
+// -delta of the 32 entries.
 template <typename T, int D>
 struct GradLds {
   using TL = TileLayout<T, D>;
@@ -107,54 +109,74 @@ struct GradLoader {
       if (threadIdx.x < 32) {
         float* f = GL::ent(b);
         f[threadIdx.x] = e.x;
-        f[32 + threadIdx.x] = e.y;
+        f[32 + threadIdx.x] = -e.y;
       }
     }
   }
 };
 
+// Scores of one 16-row block against the 32 entries of the step, added to
+// c0 (entries 0-15) and c1 (entries 16-31) instead of to zero.
+template <typename T, int D>
+__device__ __forceinline__ void step_scores_from(const StepFrags<T, D>& f, const Frag<T>* qf, float* sc, f32x4 s0,
+                                                 f32x4 s1) {
+#pragma unroll
+  for (int dc = 0; dc < D / 32; ++dc) {
+    mma16(s0, f.ka[0][dc], qf[dc]);
+    mma16(s1, f.ka[1][dc], qf[dc]);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) { sc[r] = s0[r]; sc[4 + r] = s1[r]; }
+}
+
 // One 32-entry step for IB blocks of 16 stationary rows.  ROWL: L and delta
-// per stationary row (Lr, Dr: this lane's row) instead of per entry (Le, De
-// in LDS).  MASK: entries at offsets >= nv are absent.
-// DSCALED: De already holds delta * cnat.
-template <int IB, bool MASK, bool ROWL, bool WANT_W, typename T, int D, bool DSCALED = false>
+// per stationary row (Lr, Dr: this lane's row) instead of per entry (Le, and
+// -delta in NDe, in LDS).  MASK: entries at offsets >= nv are absent.
+//
+// With per-row L (a pass with no P output), the softmax-gradient scale is
+// folded into the exponent: exp2(s cscale - (L - log2 cnat)) = P cnat (exact
+// for d = 64, where log2 cnat = -3), and dS comes out scaled.  With per-entry
+// L and delta the step accumulates the unscaled dS: the caller multiplies
+// the ax accumulators by cnat once at the end (scale_acc).
+template <int IB, bool MASK, bool ROWL, bool WANT_W, typename T, int D>
 __device__ __forceinline__ void grad_step(const StepFrags<T, D>& fy, const StepFrags<T, D>& fz,
                                           const Frag<T> (&xf)[IB][D / 32], const Frag<T> (&wf)[IB][D / 32],
                                           int nv, int lg, float cscale, float cnat, const float (&Lr)[IB],
-                                          const float (&Dr)[IB], const float* Le, const float* De,
+                                          const float (&Dr)[IB], const float* Le, const float* NDe,
                                           f32x4 (&ax)[IB][D / 16], f32x4 (&aw)[IB][D / 16]) {
-  // with per-row L and no P output, the softmax-gradient scale is folded
-  // into the exponent: exp2(s cscale - (L - log2 cnat)) = P cnat (exact for
-  // d = 64, where log2 cnat = -3)
-  constexpr bool FOLD = ROWL && !WANT_W;
+  static_assert(ROWL != WANT_W, "per-row statistics go with the no-P passes, per-entry ones with the others");
+  constexpr bool FOLD = ROWL;
   const float lcn = FOLD ? __builtin_amdgcn_logf(cnat) : 0.f;
-  // otherwise dS = P (dP cnat - delta cnat), one fused multiply-add, with
-  // delta cnat formed once per step (or already in De)
-  float le[8], de[8];
+  // per entry: L of this lane's 8 entry slots, and -delta of its slots as
+  // the starting values of the dP product (slots 0-3 are entries 4 lg ..,
+  // slots 4-7 entries 16 + 4 lg .., the product's output rows)
+  float le[8];
+  f32x4 nd0 = {0.f, 0.f, 0.f, 0.f}, nd1 = {0.f, 0.f, 0.f, 0.f};
   if constexpr (!ROWL) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int j = slot_key(t, lg);
-      le[t] = Le[j];
-      de[t] = DSCALED ? De[j] : De[j] * cnat;
-    }
+    for (int t = 0; t < 8; ++t) le[t] = Le[slot_key(t, lg)];
+    nd0 = *(const f32x4*)(NDe + 4 * lg);
+    nd1 = *(const f32x4*)(NDe + 16 + 4 * lg);
   }
 #pragma unroll
   for (int b = 0; b < IB; ++b) {
     float sc[8], dp[8];
     step_scores(fy, xf[b], sc);
-    step_scores(fz, wf[b], dp);
+    if constexpr (ROWL) {
+      const f32x4 nd = {-Dr[b], -Dr[b], -Dr[b], -Dr[b]};
+      step_scores_from(fz, wf[b], dp, nd, nd);
+    } else {
+      step_scores_from(fz, wf[b], dp, nd0, nd1);
+    }
     float p[8], ds[8];
     const float Lb = FOLD ? Lr[b] - lcn : 0.f;
-    const float db = ROWL ? (FOLD ? Dr[b] : Dr[b] * cnat) : 0.f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const float L = FOLD ? Lb : ROWL ? Lr[b] : le[t];
-      const float dl = ROWL ? db : de[t];
+      const float L = FOLD ? Lb : le[t];
       float pt = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t], cscale, -L));
       if (MASK && slot_key(t, lg) >= nv) pt = 0.f;
       p[t] = pt;
-      ds[t] = FOLD ? pt * (dp[t] - dl) : pt * __builtin_fmaf(dp[t], cnat, -dl);
+      ds[t] = pt * dp[t];
     }
     Frag<T> df;
     set8(df, ds);
@@ -374,6 +396,17 @@ __device__ __forceinline__ void zero_acc(f32x4 (&a)[IB][D / 16]) {
     for (int cb = 0; cb < D / 16; ++cb) a[b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
+// The logit scale of a per-entry pass's dS, applied once to its sums.
+template <int IB, int D>
+__device__ __forceinline__ void scale_acc(f32x4 (&a)[IB][D / 16], float c) {
+#pragma unroll
+  for (int b = 0; b < IB; ++b)
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a[b][cb][r] *= c;
+}
+
 // ---------------------------------------------------------------------------
 // Landmark rows over one chunk of entries (all heads' chunks in the grid).
 // JOINT: entries are queries (Y q, Z dO, per-entry lse and dO . o); outputs
@@ -411,6 +444,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_bwd_lm(const T* __restrict__ Y, 
   const SrcRows<T, D> src{Y + (size_t)bh * N * D, Z + (size_t)bh * N * D, JOINT ? Lv + (size_t)bh * N : nullptr,
                           JOINT ? Dv + (size_t)bh * N : nullptr, j0, j1, cscale, cnat};
   grad_stream<IB, !JOINT, JOINT, JOINT, NT, T, D>(smem, (j1 - j0 + 31) / 32, src, xf, wf, Lr, Dr, ax, aw, li, lg);
+  if constexpr (JOINT) scale_acc<IB, D>(ax, cnat);
 #pragma unroll
   for (int b = 0; b < IB; ++b) {
     const int i = i0 + b * 16 + li;
@@ -484,10 +518,12 @@ __global__ __launch_bounds__(NW * 64, 2) void k_bwd_keys(
       const SrcPerm<T, D> src{Ysrc + hb * D, Zsrc + hb * D, Lv + hb, Dv + hb, qperm + so, start, start + cnt, N,
                               cscale, cnat};
       grad_stream<IB, false, true, true, NT, T, D>(smem, (cnt + 31) / 32, src, xf, wf, Lr, Dr, ax, aw, li, lg);
+      scale_acc<IB, D>(ax, cnat);
     } else {
       // the slot's queries gathered in expert order (q, dO, lse, dO . o)
       const SrcRows<T, D> src{Ysrc + so * D, Zsrc + so * D, Lv + so, Dv + so, start, start + cnt, cscale, cnat};
       grad_stream<IB, false, true, true, NT, T, D>(smem, (cnt + 31) / 32, src, xf, wf, Lr, Dr, ax, aw, li, lg);
+      scale_acc<IB, D>(ax, cnat);
     }
 #pragma unroll
     for (int b = 0; b < IB; ++b) {
@@ -504,6 +540,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_bwd_keys(
     const SrcRows<T, D> src{Ysrc + (size_t)bh * m * D, Zsrc + (size_t)bh * m * D, Lv + (size_t)bh * m,
                             Dv + (size_t)bh * m, 0, nent, cscale, cnat};
     grad_stream<IB, false, true, true, NT, T, D>(smem, (nent + 31) / 32, src, xf, wf, Lr, Dr, ax, aw, li, lg);
+    scale_acc<IB, D>(ax, cnat);
 #pragma unroll
     for (int b = 0; b < IB; ++b) {
       if (jr[b] < 0) continue;
@@ -567,7 +604,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_bwd_keys_res(
   }
   for (int r = tid; r < Mp; r += NW * 64) {
     Le[r] = r < m ? Lm[(size_t)bh * m + r] : 0.f;
-    De[r] = r < m ? Dm[(size_t)bh * m + r] * cnat : 0.f;  // delta cnat (see grad_step)
+    De[r] = r < m ? -Dm[(size_t)bh * m + r] : 0.f;  // -delta (see grad_step)
   }
   __syncthreads();
   const float Lr[IB] = {}, Dr[IB] = {};
@@ -597,12 +634,13 @@ __global__ __launch_bounds__(NW * 64, 2) void k_bwd_keys_res(
         tr_frag(fy.va[cb], Yr, KS, x0, cb, li, lg);
         tr_frag(fz.va[cb], Zr, KS, x0, cb, li, lg);
       }
-      grad_step<IB, decltype(masked)::value, false, true, T, D, true>(fy, fz, xf, wf, m - x0, lg, cscale, cnat, Lr,
-                                                                     Dr, Le + x0, De + x0, ax, aw);
+      grad_step<IB, decltype(masked)::value, false, true, T, D>(fy, fz, xf, wf, m - x0, lg, cscale, cnat, Lr, Dr,
+                                                               Le + x0, De + x0, ax, aw);
     };
     int x0 = 0;
     for (; x0 + 32 <= m; x0 += 32) step(x0, BoolTag<false>{});
     if (x0 < m) step(x0, BoolTag<true>{});
+    scale_acc<IB, D>(ax, cnat);
 #pragma unroll
     for (int b = 0; b < IB; ++b) {
       if (jr[b] < 0) continue;
