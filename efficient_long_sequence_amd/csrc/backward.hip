@@ -759,23 +759,36 @@ __global__ __launch_bounds__(256) void k_bwd_route_sum(const float* __restrict__
   const long long p0 = g / LPK;
   const int c = (int)(g % LPK) * 4;
   if (p0 >= total) return;
+  // the key's first (expert, row) slot is read beside the key itself and
+  // that slot's item bounds in slot 0 beside the key's count, and its parts
+  // are added before the loop over the rest (every key listed here has at
+  // least one slot), so a key held by one expert row (most of them) waits
+  // for three dependent loads (key and slot, item bounds, parts) instead of
+  // five; the parts are added in the same order as before
   const int key = ikey[p0];
+  const int er0 = ilist[p0];
   if (p0 > 0 && ikey[p0 - 1] == key) return;  // not the key's first position
-  const int n = icnt[key];
   const int bh = key / N;
   const size_t E = (size_t)BH * m;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto add_items = [&](int t, int r, int f0, int nf, int pi) {
+    for (int q = f0; q < f0 + nf + (pi >= 0 ? 1 : 0); ++q) {
+      const int item = q < f0 + nf ? q : pi;
+      const float4 v = *(const float4*)(G + (((size_t)t * UB2 + item) * k + r) * (2 * D) + c);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+  };
+  const int n = icnt[key];
+  {
+    const size_t xe = (size_t)bh * m + er0 / k;
+    add_items(0, er0 % k, efirst[xe], counts[xe] / CH, epart[xe]);
+  }
   for (int x = 0; x < n; ++x) {
-    const int er = ilist[p0 + x];
+    const int er = x == 0 ? er0 : ilist[p0 + x];
     const int ee = er / k, r = er % k;
-    for (int t = 0; t < s; ++t) {
+    for (int t = x == 0 ? 1 : 0; t < s; ++t) {
       const size_t xe = (size_t)t * E + (size_t)bh * m + ee;
-      const int f0 = efirst[xe], nf = counts[xe] / CH, pi = epart[xe];
-      for (int q = f0; q < f0 + nf + (pi >= 0 ? 1 : 0); ++q) {
-        const int item = q < f0 + nf ? q : pi;
-        const float4 v = *(const float4*)(G + (((size_t)t * UB2 + item) * k + r) * (2 * D) + c);
-        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-      }
+      add_items(t, r, efirst[xe], counts[xe] / CH, epart[xe]);
     }
   }
   *(float4*)(Gs + (size_t)p0 * (2 * D) + c) = acc;
