@@ -48,26 +48,6 @@
 
 namespace mita {
 
-// The V^T-order operand of one 16-column block `cb` for the 32 rows x0 ..
-// x0+31 of a row-major bf16 tile (row stride KS), in the slot permutation of
-// the score layout (slot t < 4: row x0 + 4g + t; t >= 4: row x0 + 16 + 4g +
-// t - 4), read with the LDS transpose read ds_read_b64_tr_b16: in each
-// 16-lane group, lane i receives element i mod 4 of the 8-byte words supplied
-// by lanes i/4 + 4t (t = 0..3); lane j supplies row x0 + 4g + j/4, columns
-// 16 cb + 4 (j mod 4) .. + 3, so lane (li, g) receives column 16 cb + li of
-// the four rows of its slots.  The two results are joined as whole vectors.
-typedef short tr_v4s __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void tr_frag(Frag<__bf16>& f, const __bf16* rows, int KS, int x0, int cb, int lane16,
-                                        int g) {
-  const int r = lane16 / 4, c = cb * 16 + 4 * (lane16 % 4);
-  const tr_v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) tr_v4s*)(rows + (size_t)(x0 + 4 * g + r) * KS + c));
-  const tr_v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) tr_v4s*)(rows + (size_t)(x0 + 16 + 4 * g + r) * KS + c));
-  const bf16x4 a4 = __builtin_bit_cast(bf16x4, a), b4 = __builtin_bit_cast(bf16x4, b);
-  f.v = __builtin_shufflevector(a4, b4, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
 // LDS of one step: Y (row-major + transposed), Z (likewise), then L and
 // -delta of the 32 entries.
 template <typename T, int D>

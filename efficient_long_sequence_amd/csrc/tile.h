@@ -1,12 +1,17 @@
 // A 32-row step of keys (and values) staged in LDS for the matrix cores.
 //
 // Keys are stored row-major, Ks[j][c] with a padded row stride KS, which is
-// the A-operand order of the score product (key rows, d along K).  Values are
-// stored transposed, Vs[c][j] with row stride VS, which is the A-operand
-// order of O^T = V^T P^T (d rows, keys along K).  Each thread first pulls its
-// 16-byte chunks of the step into registers (so the global loads of step
-// i+1 overlap the matrix work of step i) and then writes them to LDS; the
-// transposing write packs two key rows per 32-bit word for bf16.
+// the A-operand order of the score product (key rows, d along K).  The
+// product O^T = V^T P^T needs the values transposed (d rows, keys along K):
+// bf16 values are stored row-major too, with row stride VSR, and read
+// transposed by the LDS transpose read (tr_frag), so key and value rows are
+// staged alike, one 16-byte chunk per thread and step; fp32 values are
+// stored transposed, Vs[c][j] with row stride VS.  Each thread first pulls
+// its chunks of the step into registers (so the global loads of step i+1
+// overlap the matrix work of step i) and then writes them to LDS.  (A key
+// row stride of 72 elements keeps the row-wise key reads free of LDS bank
+// conflicts and a value row stride of 80 the transposed value reads, in a
+// 64-bank model.)
 #pragma once
 #include "mita_dev.h"
 
@@ -17,8 +22,12 @@ struct TileLayout {
   static constexpr int EPC = 16 / (int)sizeof(T);     // elements per 16 bytes
   static constexpr int KS = D + EPC;   // padded key row (elements); 16-byte aligned rows
   static constexpr int VS = 36;        // padded V^T row (elements); 8-byte (bf16) / 16-byte (f32) aligned
+  // bf16: value rows are staged as they come, padded to VSR elements, and
+  // read transposed (ds_read_b64_tr_b16)
+  static constexpr bool ROWV = sizeof(T) == 2;
+  static constexpr int VSR = D + 16;
   static constexpr int K_ELEMS = 32 * KS;
-  static constexpr int V_ELEMS = D * VS;
+  static constexpr int V_ELEMS = ROWV ? 32 * VSR : D * VS;
   static constexpr int ELEMS = K_ELEMS + V_ELEMS;
 };
 
@@ -26,24 +35,19 @@ template <typename T, int D, int NT, bool WITH_V>
 struct TileLoader {
   using L = TileLayout<T, D>;
   static constexpr int EPC = L::EPC;
-  static constexpr int CPR = D / EPC;                  // 16-byte chunks per row
+  static constexpr int CPR = D / EPC;  // 16-byte chunks per row
   static constexpr int KCH = 32 * CPR;
-  static constexpr int KPT = (KCH + NT - 1) / NT;
-  static constexpr int VROWS = sizeof(T) == 2 ? 2 : 1;  // rows per transposing task
-  static constexpr int VCH = WITH_V ? (32 / VROWS) * CPR : 0;
-  static constexpr int VPT = WITH_V ? (VCH + NT - 1) / NT : 0;
-  static constexpr int VS = L::VS;
-  // Split placement (bf16, when the block has room): key chunks go to the
-  // first threads and the value transpose, in tasks of two rows by four
-  // elements, to the last ones.  A SIMD runs waves w and w + NT/256 of the
-  // block, so each SIMD then carries one key-loading and one value-loading
-  // wave and the per-step barrier waits less for the slowest.
-  static constexpr int VFINE = WITH_V ? 16 * (D / 4) : 0;
-  static constexpr bool SPLIT = WITH_V && sizeof(T) == 2 && KCH + VFINE <= NT;
+  // bf16 with values: key and value rows alike, 2 KCH chunks over the block
+  // (with 512 threads, one each: the first half keys, the second values)
+  static constexpr bool ROWV = WITH_V && sizeof(T) == 2;
+  static constexpr int TCH = ROWV ? 2 * KCH : KCH;
+  static constexpr int RPT = (TCH + NT - 1) / NT;
+  // fp32 with values: the value transpose, one row chunk per task
+  static constexpr bool TRV = WITH_V && !ROWV;
+  static constexpr int VPT = TRV ? (KCH + NT - 1) / NT : 0;
 
-  uint4 kreg[KPT];
-  uint4 vreg[SPLIT ? 1 : (VPT > 0 ? VPT : 1)][SPLIT ? 1 : VROWS];
-  uint2 vfine[SPLIT ? 2 : 1];
+  uint4 rreg[RPT];
+  uint4 vreg[VPT > 0 ? VPT : 1];
 
   // rk(j) / rv(j): pointer to key / value row j of the step, or nullptr for a
   // row past the end (it is staged as zeros).
@@ -51,35 +55,23 @@ struct TileLoader {
   __device__ __forceinline__ void load(RK rk, RV rv) {
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int c = 0; c < KPT; ++c) {
+    for (int c = 0; c < RPT; ++c) {
       const int i = tid + c * NT;
-      kreg[c] = make_uint4(0, 0, 0, 0);
-      if (i < KCH) {
-        const T* p = rk(i / CPR);
-        if (p) kreg[c] = *(const uint4*)(p + (i % CPR) * EPC);
+      rreg[c] = make_uint4(0, 0, 0, 0);
+      if (i < TCH) {
+        const int ii = i < KCH ? i : i - KCH;
+        const T* p = i < KCH ? rk(ii / CPR) : rv(ii / CPR);
+        if (p) rreg[c] = *(const uint4*)(p + (ii % CPR) * EPC);
       }
     }
-    if constexpr (SPLIT) {
-      const int i = tid - (NT - VFINE);
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        vfine[r] = make_uint2(0, 0);
-        if (i >= 0) {
-          const T* p = rv(2 * (i / (D / 4)) + r);
-          if (p) vfine[r] = *(const uint2*)(p + (i % (D / 4)) * 4);
-        }
-      }
-    } else if constexpr (WITH_V) {
+    if constexpr (TRV) {
 #pragma unroll
       for (int c = 0; c < VPT; ++c) {
         const int i = tid + c * NT;
-#pragma unroll
-        for (int r = 0; r < VROWS; ++r) {
-          vreg[c][r] = make_uint4(0, 0, 0, 0);
-          if (i < VCH) {
-            const T* p = rv((i / CPR) * VROWS + r);
-            if (p) vreg[c][r] = *(const uint4*)(p + (i % CPR) * EPC);
-          }
+        vreg[c] = make_uint4(0, 0, 0, 0);
+        if (i < KCH) {
+          const T* p = rv(i / CPR);
+          if (p) vreg[c] = *(const uint4*)(p + (i % CPR) * EPC);
         }
       }
     }
@@ -88,50 +80,49 @@ struct TileLoader {
   __device__ __forceinline__ void store(T* Ks, T* Vs) const {
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int c = 0; c < KPT; ++c) {
+    for (int c = 0; c < RPT; ++c) {
       const int i = tid + c * NT;
-      if (i < KCH) *(uint4*)(Ks + (i / CPR) * L::KS + (i % CPR) * EPC) = kreg[c];
-    }
-    if constexpr (SPLIT) {
-      const int i = tid - (NT - VFINE);
-      if (i >= 0) {
-        const int jp = i / (D / 4), c0 = (i % (D / 4)) * 4;
-        const uint32_t* a = (const uint32_t*)&vfine[0];
-        const uint32_t* b = (const uint32_t*)&vfine[1];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          // elements 2u, 2u+1 of rows 2jp (a) and 2jp+1 (b)
-          *(uint32_t*)(Vs + (c0 + 2 * u) * VS + 2 * jp) = (a[u] & 0xFFFFu) | (b[u] << 16);
-          *(uint32_t*)(Vs + (c0 + 2 * u + 1) * VS + 2 * jp) = (a[u] >> 16) | (b[u] & 0xFFFF0000u);
-        }
+      if (i < TCH) {
+        const int ii = i < KCH ? i : i - KCH;
+        T* dst = i < KCH ? Ks + (ii / CPR) * L::KS : Vs + (ii / CPR) * L::VSR;
+        *(uint4*)(dst + (ii % CPR) * EPC) = rreg[c];
       }
-    } else if constexpr (WITH_V) {
+    }
+    if constexpr (TRV) {
 #pragma unroll
       for (int c = 0; c < VPT; ++c) {
         const int i = tid + c * NT;
-        if (i < VCH) {
-          const int jp = i / CPR, c0 = (i % CPR) * EPC;
-          if constexpr (sizeof(T) == 2) {
-            const uint32_t* a = (const uint32_t*)&vreg[c][0];
-            const uint32_t* b = (const uint32_t*)&vreg[c][1];
+        if (i < KCH) {
+          const int j = i / CPR, c0 = (i % CPR) * EPC;
+          const float* a = (const float*)&vreg[c];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              // elements 2u, 2u+1 of rows 2jp (a) and 2jp+1 (b)
-              const uint32_t lo = (a[u] & 0xFFFFu) | (b[u] << 16);
-              const uint32_t hi = (a[u] >> 16) | (b[u] & 0xFFFF0000u);
-              *(uint32_t*)(Vs + (c0 + 2 * u) * VS + 2 * jp) = lo;
-              *(uint32_t*)(Vs + (c0 + 2 * u + 1) * VS + 2 * jp) = hi;
-            }
-          } else {
-            const float* a = (const float*)&vreg[c][0];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) Vs[(c0 + u) * VS + jp] = a[u];
-          }
+          for (int u = 0; u < 4; ++u) Vs[(c0 + u) * L::VS + j] = a[u];
         }
       }
     }
   }
 };
+
+// The V^T-order operand of one 16-column block `cb` for the 32 rows x0 ..
+// x0+31 of a row-major bf16 tile (row stride KS), in the slot permutation of
+// the score layout (slot t < 4: row x0 + 4g + t; t >= 4: row x0 + 16 + 4g +
+// t - 4), read with the LDS transpose read ds_read_b64_tr_b16: in each
+// 16-lane group, lane i receives element i mod 4 of the 8-byte words supplied
+// by lanes i/4 + 4t (t = 0..3); lane j supplies row x0 + 4g + j/4, columns
+// 16 cb + 4 (j mod 4) .. + 3, so lane (li, g) receives column 16 cb + li of
+// the four rows of its slots.  The two results are joined as whole vectors.
+typedef short tr_v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void tr_frag(Frag<__bf16>& f, const __bf16* rows, int KS, int x0, int cb, int lane16,
+                                        int g) {
+  const int r = lane16 / 4, c = cb * 16 + 4 * (lane16 % 4);
+  const tr_v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) tr_v4s*)(rows + (size_t)(x0 + 4 * g + r) * KS + c));
+  const tr_v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) tr_v4s*)(rows + (size_t)(x0 + 16 + 4 * g + r) * KS + c));
+  const bf16x4 a4 = __builtin_bit_cast(bf16x4, a), b4 = __builtin_bit_cast(bf16x4, b);
+  f.v = __builtin_shufflevector(a4, b4, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ void tr_frag(Frag<float>&, const float*, int, int, int, int, int) {}
 
 // Per-lane key slot -> key offset inside a 32-key step.
 __device__ __forceinline__ int slot_key(int t, int g) { return t < 4 ? 4 * g + t : 16 + 4 * g + (t - 4); }
@@ -149,10 +140,15 @@ struct StepFrags {
       for (int dc = 0; dc < D / 32; ++dc) load8(ka[jt][dc], Ks + (jt * 16 + li) * L::KS + dc * 32 + 8 * g);
   }
   __device__ __forceinline__ void load_vals(const T* Vs, int li, int g) {
+    if constexpr (TileLayout<T, D>::ROWV) {
 #pragma unroll
-    for (int cb = 0; cb < D / 16; ++cb) {
-      const T* row = Vs + (cb * 16 + li) * TileLayout<T, D>::VS;
-      load4x2(va[cb], row + 4 * g, row + 16 + 4 * g);
+      for (int cb = 0; cb < D / 16; ++cb) tr_frag(va[cb], Vs, TileLayout<T, D>::VSR, 0, cb, li, g);
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb) {
+        const T* row = Vs + (cb * 16 + li) * TileLayout<T, D>::VS;
+        load4x2(va[cb], row + 4 * g, row + 16 + 4 * g);
+      }
     }
   }
 };
