@@ -188,21 +188,25 @@ __global__ __launch_bounds__(NW * 64, (score_waves_per_eu<T, NW, IB>())) void k_
     return [=](int r) -> const T* { const int j = j0 + r; return j < j_end ? Vh + (size_t)j * D : nullptr; };
   };
 
-  TileLoader<T, D, NT, SHARED> ld;
+  // two register stages: the loads of step st + 2 are issued at the start of
+  // step st, the tile of step st + 1 (loaded a step earlier) is stored at its
+  // end; the two loaders swap roles every step (the loop is unrolled by two)
+  TileLoader<T, D, NT, SHARED> la, lb;
   const int nsteps = (j_end - j_begin + 31) / 32;
-  ld.load(rowK(j_begin), rowV(j_begin));
-  ld.store(buf0, buf0 + TL::K_ELEMS);
+  la.load(rowK(j_begin), rowV(j_begin));
+  la.store(buf0, buf0 + TL::K_ELEMS);
+  if (nsteps > 1) la.load(rowK(j_begin + 32), rowV(j_begin + 32));
   __syncthreads();
   // one 32-key step; MASKED: the chunk's last, partial step (its absent keys
   // get score -inf).  The partial step is peeled off the loop: with both
   // forms of the step in the loop body the kernel runs out of registers.
-  auto body = [&](int st, auto masked) {
+  auto body = [&](int st, auto masked, auto& lnext, auto& lfar) {
     constexpr bool MASKED = decltype(masked)::value;
     const int j0 = j_begin + st * 32;
     T* cur = (st & 1) ? buf1 : buf0;
     T* nxt = (st & 1) ? buf0 : buf1;
     const bool more = st + 1 < nsteps;
-    if (more) ld.load(rowK(j0 + 32), rowV(j0 + 32));
+    if (st + 2 < nsteps) lfar.load(rowK(j0 + 64), rowV(j0 + 64));
     StepFrags<T, D> f;
     f.load_keys(cur, li, lg);
     if constexpr (SHARED) f.load_vals(cur + TL::K_ELEMS, li, lg);
@@ -238,12 +242,22 @@ __global__ __launch_bounds__(NW * 64, (score_waves_per_eu<T, NW, IB>())) void k_
     };
     if constexpr (SHARED) attn_step<IB, MASKED>(f, one, qf, nv, lg, cscale, M, Z, acc, cands);
     else score_step<IB, MASKED>(f, qf, nv, lg, cands);
-    if (more) ld.store(nxt, nxt + TL::K_ELEMS);
+    if (more) lnext.store(nxt, nxt + TL::K_ELEMS);
     __syncthreads();
   };
   const int nfull = (j_end - j_begin) / 32;
-  for (int st = 0; st < nfull; ++st) body(st, BoolTag<false>{});
-  if (nfull < nsteps) body(nfull, BoolTag<true>{});
+  int st = 0;
+  for (; st + 1 < nfull; st += 2) {
+    body(st, BoolTag<false>{}, la, lb);
+    body(st + 1, BoolTag<false>{}, lb, la);
+  }
+  if (st < nfull) {
+    body(st, BoolTag<false>{}, la, lb);
+    ++st;
+    if (st < nsteps) body(st, BoolTag<true>{}, lb, la);
+  } else if (st < nsteps) {
+    body(st, BoolTag<true>{}, la, lb);
+  }
 
   // partial shared values of this chunk: (max, normaliser, 2 pad, unnormalised sums)
   if constexpr (SHARED) {
