@@ -10,8 +10,8 @@
 // its chunks of the step into registers (so the global loads of step i+1
 // overlap the matrix work of step i) and then writes them to LDS.  (A key
 // row stride of 72 elements keeps the row-wise key reads free of LDS bank
-// conflicts and a value row stride of 80 the transposed value reads, in a
-// 64-bank model.)
+// conflicts and a value row stride of 80 the transposed value reads, with
+// 32 or 64 banks of 4 bytes alike.)
 #pragma once
 #include "mita_dev.h"
 
