@@ -81,6 +81,13 @@ EDGE = {
     # compacting search) and with 64 keys selected (the largest on-chip k)
     "small_n400": (1, 2, 20, 20, 64, 4, 4, 30, 1, "clustered", 8, "bf16"),
     "small_n512_k64": (1, 1, 1, 512, 64, 1, 8, 64, 2, "runs", 8, "bf16"),
+    # many heads, so each head's keys split into few chunks of several
+    # 32-key steps: chunks of 4 full steps and a last one of 3 full steps
+    # plus a partial one (N = 485), and of 3 full steps and a last one of 2
+    # plus a partial one (N = 359; the 8-wave scoring shape, m = 80): every
+    # order of the scoring loop's two alternating staging registers
+    "chunks_4steps_tail3": (4, 32, 1, 485, 64, 1, 4, 16, 1, "runs", 8, "bf16"),
+    "chunks_3steps_tail2_m80": (4, 32, 1, 359, 64, 1, 80, 16, 1, "clustered", 8, "bf16"),
 }
 
 
