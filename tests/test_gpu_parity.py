@@ -88,6 +88,9 @@ EDGE = {
     # order of the scoring loop's two alternating staging registers
     "chunks_4steps_tail3": (4, 32, 1, 485, 64, 1, 4, 16, 1, "runs", 8, "bf16"),
     "chunks_3steps_tail2_m80": (4, 32, 1, 359, 64, 1, 80, 16, 1, "clustered", 8, "bf16"),
+    # the same above the dense limit (sampled threshold, score records):
+    # chunks of 72 steps and a last one of 69 full steps plus a partial one
+    "sparse_chunks_odd_tail": (4, 32, 1, 9125, 64, 1, 4, 16, 1, "runs", 8, "bf16"),
 }
 
 
