@@ -20,7 +20,7 @@
 namespace mita {
 
 template <typename T, int D, int NW, int IB>
-__global__ __launch_bounds__(NW * 64) void k_dense(const T* __restrict__ Q, const T* __restrict__ K,
+__global__ __launch_bounds__(NW * 64, 2) void k_dense(const T* __restrict__ Q, const T* __restrict__ K,
                                                    const T* __restrict__ V, T* __restrict__ O, int N,
                                                    float cscale) {
   constexpr int NT = NW * 64;
@@ -56,27 +56,44 @@ __global__ __launch_bounds__(NW * 64) void k_dense(const T* __restrict__ Q, cons
   auto rowV = [&](int j0) {
     return [=](int r) -> const T* { const int j = j0 + r; return j < N ? V + hb + (size_t)j * D : nullptr; };
   };
-  TileLoader<T, D, NT, true> ld;
+  // two register stages: the loads of step st + 2 are issued at the start of
+  // step st, the tile of step st + 1 (loaded a step earlier) is stored at its
+  // end; the two loaders swap roles every step (the loop is unrolled by two).
+  // The partial last step is peeled off the loop: with both forms of the step
+  // in the loop body the kernel runs out of registers.
+  TileLoader<T, D, NT, true> la, lb;
   T* buf0 = smem;
   T* buf1 = smem + TL::ELEMS;
   const int nsteps = (N + 31) / 32;
-  ld.load(rowK(0), rowV(0));
-  ld.store(buf0, buf0 + TL::K_ELEMS);
+  la.load(rowK(0), rowV(0));
+  la.store(buf0, buf0 + TL::K_ELEMS);
+  if (nsteps > 1) la.load(rowK(32), rowV(32));
   __syncthreads();
-  for (int st = 0; st < nsteps; ++st) {
+  auto body = [&](int st, auto masked, auto& lnext, auto& lfar) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int j0 = st * 32;
     T* cur = (st & 1) ? buf1 : buf0;
     T* nxt = (st & 1) ? buf0 : buf1;
-    const bool more = st + 1 < nsteps;
-    if (more) ld.load(rowK(j0 + 32), rowV(j0 + 32));
+    if (st + 2 < nsteps) lfar.load(rowK(j0 + 64), rowV(j0 + 64));
     StepFrags<T, D> f;
     f.load_keys(cur, li, lg);
     f.load_vals(cur + TL::K_ELEMS, li, lg);
-    const int nv = min(32, N - j0);
-    if (nv == 32) attn_step<IB, false>(f, one, qf, nv, lg, cscale, M, Z, acc, NoHook{});
-    else attn_step<IB, true>(f, one, qf, nv, lg, cscale, M, Z, acc, NoHook{});
-    if (more) ld.store(nxt, nxt + TL::K_ELEMS);
+    attn_step<IB, MASKED>(f, one, qf, min(32, N - j0), lg, cscale, M, Z, acc, NoHook{});
+    if (st + 1 < nsteps) lnext.store(nxt, nxt + TL::K_ELEMS);
     __syncthreads();
+  };
+  const int nfull = N / 32;
+  int st = 0;
+  for (; st + 1 < nfull; st += 2) {
+    body(st, BoolTag<false>{}, la, lb);
+    body(st + 1, BoolTag<false>{}, lb, la);
+  }
+  if (st < nfull) {
+    body(st, BoolTag<false>{}, la, lb);
+    ++st;
+    if (st < nsteps) body(st, BoolTag<true>{}, lb, la);
+  } else if (st < nsteps) {
+    body(st, BoolTag<true>{}, la, lb);
   }
 
 #pragma unroll
