@@ -107,7 +107,11 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
     const double e = 0.35 * (double)k * p.L / N;
     int s4 = (int)std::ceil(20.0 * e);
     s4 = s4 < REC_MIN ? REC_MIN : s4;
-    p.s4 = steps < s4 ? steps : s4;
+    s4 = steps < s4 ? steps : s4;
+    // the scoring kernel indexes records with 32 bits
+    const long long segs = (long long)p.BH * m * p.C * 4;
+    const long long most = (long long)UINT32_MAX / segs;
+    p.s4 = s4 < most ? s4 : (int)most;
     // Test hook (host-forced): MITA_TEST_FORCE_FALLBACK=1 sets every candidate
     // threshold to +inf, so no row collects candidates and every row is
     // selected by the exact fallback kernel instead.

@@ -157,8 +157,12 @@ __global__ __launch_bounds__(NW * 64, (score_waves_per_eu<T, NW, IB>())) void k_
   // sparse mode: every lane appends its own records (no cross-lane work on
   // the inner loop); rcnt[b] counts those of block b
   int rcnt[IB];
+  uint32_t rbase32[IB];  // each block's first record of this lane (the plan keeps record indices in 32 bits)
 #pragma unroll
-  for (int b = 0; b < IB; ++b) rcnt[b] = 0;
+  for (int b = 0; b < IB; ++b) {
+    rcnt[b] = 0;
+    rbase32[b] = (uint32_t)(((((size_t)bh * m + rbase + b * 16 + li) * C + ch) * 4 + lg) * s4);
+  }
 
   Frag<T> qf[IB][D / 32];
   float tau[IB];
@@ -225,13 +229,13 @@ __global__ __launch_bounds__(NW * 64, (score_waves_per_eu<T, NW, IB>())) void k_
             if (kl < nv) dst[kl] = ckey(sc[t], (uint32_t)(j0 + kl));
           }
         }
-      } else if (SEL == SEL_SPARSE && wave_any(mx >= tau[b])) {
+      } else if (SEL == SEL_SPARSE) {
         // (rows past m have tau = +inf and never get here)
         if (mx >= tau[b]) {
           const int c = rcnt[b];
           if (c < s4) {
-            const size_t e = ((((size_t)bh * m + row) * C + ch) * 4 + lg) * s4 + c;
-            float4* dst = (float4*)(rec_sc + e * 8);
+            const uint32_t e = rbase32[b] + (uint32_t)c;
+            float4* dst = (float4*)(rec_sc + (size_t)e * 8);
             dst[0] = make_float4(sc[0], sc[1], sc[2], sc[3]);
             dst[1] = make_float4(sc[4], sc[5], sc[6], sc[7]);
             rec_st[e] = st;
