@@ -108,7 +108,8 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
     int s4 = (int)std::ceil(20.0 * e);
     s4 = s4 < REC_MIN ? REC_MIN : s4;
     s4 = steps < s4 ? steps : s4;
-    // the scoring kernel indexes records with 32 bits
+    // the scoring kernel indexes records with 32 bits (segs < 2^32 under the
+    // argument limits above, B*H <= 65535 and m <= 4096, so s4 stays >= 1)
     const long long segs = (long long)p.BH * m * p.C * 4;
     const long long most = (long long)UINT32_MAX / segs;
     p.s4 = s4 < most ? s4 : (int)most;

@@ -232,14 +232,14 @@ __global__ __launch_bounds__(NW * 64, (score_waves_per_eu<T, NW, IB>())) void k_
       } else if (SEL == SEL_SPARSE) {
         // (rows past m have tau = +inf and never get here)
         if (mx >= tau[b]) {
+          // past the lane's s4 records the last one is overwritten: the
+          // count then exceeds s4 and the row takes the exact fallback
           const int c = rcnt[b];
-          if (c < s4) {
-            const uint32_t e = rbase32[b] + (uint32_t)c;
-            float4* dst = (float4*)(rec_sc + (size_t)e * 8);
-            dst[0] = make_float4(sc[0], sc[1], sc[2], sc[3]);
-            dst[1] = make_float4(sc[4], sc[5], sc[6], sc[7]);
-            rec_st[e] = st;
-          }
+          const uint32_t e = rbase32[b] + (uint32_t)min(c, s4 - 1);
+          float4* dst = (float4*)(rec_sc + (size_t)e * 8);
+          dst[0] = make_float4(sc[0], sc[1], sc[2], sc[3]);
+          dst[1] = make_float4(sc[4], sc[5], sc[6], sc[7]);
+          rec_st[e] = st;
           rcnt[b] = c + 1;
         }
       }
