@@ -144,20 +144,25 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
     else if (avg <= 256) { p.ex_nw = 4; p.ex_ib = 4; }
     // experts of up to ~1K queries: sixteen waves of one 16-query block
     // (four waves per SIMD; 64K: 0.079 -> 0.067 ms, 256K: 0.082 -> 0.075 ms);
-    // larger ones sixteen waves of two blocks (N = 1M: 0.424 -> 0.404 ms
-    // against eight waves of four)
+    // larger ones two blocks (N = 1M: 0.424 -> 0.404 ms with sixteen waves
+    // against eight waves of four), in twelve waves, which leaves the
+    // registers to fetch the stored shared part before the key loop
+    // (0.44 -> 0.415 ms)
     else if (avg <= 1024) { p.ex_nw = 16; p.ex_ib = 1; }
-    else { p.ex_nw = 16; p.ex_ib = 2; }
+    else { p.ex_nw = 12; p.ex_ib = 2; }
     // queries per work item: about twice the average expert (at least 64),
-    // in whole groups of the launch shape, at most four: an expert that fits
-    // one item stages its keys once, while smaller items spread a large
-    // expert over more workgroups (measured: DeiT-S 19.5 -> 17.6 us,
-    // ADE 32x32 18 -> 15, 40x40 21 -> 17, N = 64K 69 -> 60 us, against
-    // items of about the average)
+    // in whole groups of the launch shape, at most 2048 queries (the
+    // work-list scan's size classes): an expert that fits one item stages
+    // its keys once, while smaller items spread a large expert over more
+    // workgroups (measured: DeiT-S 19.5 -> 17.6 us, ADE 32x32 18 -> 15,
+    // 40x40 21 -> 17, N = 64K 69 -> 60 us, against items of about the
+    // average; N = 256K 68-72 -> 64-66 us with items of 2048 queries
+    // instead of 1024)
     const int per = p.ex_nw * 16 * p.ex_ib;
     const double want = 2.0 * avg > 64.0 ? 2.0 * avg : 64.0;
+    const int gmax = 2048 / per;
     int gpw = (int)(want / per + 0.5);
-    gpw = gpw < 1 ? 1 : gpw > 4 ? 4 : gpw;
+    gpw = gpw < 1 ? 1 : gpw > gmax ? gmax : gpw;
     p.T = per * gpw;
   } else {
     if (p.dtype == 0 || avg <= 16) { p.at_nw = 1; p.at_ib = 1; }

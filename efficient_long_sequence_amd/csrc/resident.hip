@@ -336,13 +336,16 @@ __global__ __launch_bounds__(NW * 64, NW >= 16 ? 4 : 1) void k_route_shared(
 // ---------------------------------------------------------------------------
 // One group of IB blocks of 16 queries (query rows qn[b], -1 for an empty
 // slot) against the expert's k resident entries, merged with the stored
-// finished part.
-template <int IB, typename T, int D>
+// finished part.  EARLY: the stored part is fetched before the key loop (it
+// arrives while the loop computes; for the launch shapes with registers to
+// hold it), else after it.  issue() starts the caller's own loads for later
+// (the next group's query rows) once the group's own are in.
+template <int IB, typename T, int D, bool EARLY, class IS>
 __device__ __forceinline__ void expert_group(const Frag<T> (&qf)[IB][D / 32], const int (&qn)[IB], const T* Ks,
                                              const T* Vs, int Kp, int k, const Frag<T>& one, size_t row0,
                                              float2* __restrict__ plse, typename PartT<T>::type* __restrict__ po,
                                              T* __restrict__ O, TrainOut tr, int merge_in, int last, float cscale, int li,
-                                             int lg) {
+                                             int lg, IS issue) {
   using RL = Resident<T, D>;
   using P = typename PartT<T>::type;
   using PV = typename Vec4<P>::type;
@@ -356,6 +359,29 @@ __device__ __forceinline__ void expert_group(const Frag<T> (&qf)[IB][D / 32], co
 #pragma unroll
     for (int cb = 0; cb < D / 16; ++cb) acc[b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  // the stored part (none before the first routed slot of the routing-only
+  // variant): (log2-sum-exp, scale) and the scaled row
+  float2 plv[IB];
+  PV hv[IB][D / 16];
+  auto fetch = [&](int b) {
+    plv[b] = make_float2(M0, 0.f);
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb) hv[b][cb] = PV{};
+    if (merge_in && qn[b] >= 0) {
+      const size_t qrow = row0 + qn[b];
+      plv[b] = plse[qrow];
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb) hv[b][cb] = *(const PV*)(po + qrow * D + part_pos<D>(lg, cb));
+    }
+  };
+  if constexpr (EARLY) {
+    // the query rows first: the loop needs them at once, and with their loads
+    // still counted the compiler would wait for these ones inside the loop too
+    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int b = 0; b < IB; ++b) fetch(b);
+  }
+  issue();
   int x0 = 0;
   for (; x0 + 32 <= k; x0 += 32) {
     StepFrags<T, D> f;
@@ -372,10 +398,11 @@ __device__ __forceinline__ void expert_group(const Frag<T> (&qf)[IB][D / 32], co
     const float Zt = finish_z(Z[b], li);
     if (qn[b] < 0) continue;
     const size_t qrow = row0 + qn[b];
-    // merge with the stored partial (none before the first routed slot of
-    // the routing-only variant): weights 2^lse of the two parts; the stored
+    // merge with the stored part: weights 2^lse of the two parts; the stored
     // row comes back multiplied by its scale
-    const float2 pl = merge_in ? plse[qrow] : make_float2(M0, 0.f);
+    float2 pl;
+    if constexpr (EARLY) pl = plv[b];
+    else pl = merge_in ? plse[qrow] : make_float2(M0, 0.f);
     const float la = pl.x;
     const float lb = M[b].M + __builtin_amdgcn_logf(Zt);
     const float mx = fmaxf(la, lb);
@@ -387,9 +414,16 @@ __device__ __forceinline__ void expert_group(const Frag<T> (&qf)[IB][D / 32], co
 #pragma unroll
     for (int cb = 0; cb < D / 16; ++cb) {
       PV h = PV{};
-      if (merge_in) h = *(const PV*)(o + part_pos<D>(lg, cb));
+      if constexpr (EARLY) h = hv[b][cb];
+      else if (merge_in) h = *(const PV*)(o + part_pos<D>(lg, cb));
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[cb][r] = ca * (float)h[r] + cb_ * acc[b][cb][r];
+      for (int r = 0; r < 4; ++r) {
+        float hf = (float)h[r];
+        // (converted on its own: folded into a mixed-precision multiply-add
+        // the merge was not reproducible from run to run)
+        if constexpr (EARLY) asm volatile("" : "+v"(hf));
+        v[cb][r] = ca * hf + cb_ * acc[b][cb][r];
+      }
     }
     // the log2-sum-exp of everything merged so far: the next slot's input,
     // or after the last slot the query's whole normaliser (kept for the
@@ -419,7 +453,7 @@ __device__ __forceinline__ void expert_group(const Frag<T> (&qf)[IB][D / 32], co
   }
 }
 
-template <int IBX, typename T, int D, class QR>
+template <int IBX, typename T, int D, bool EARLY, class QR>
 __device__ __forceinline__ void expert_blocks(const T* Qh, QR qrow, const T* Ks, const T* Vs, int Kp, int k,
                                               const Frag<T>& one, size_t row0, float2* plse,
                                               typename PartT<T>::type* po, T* O, TrainOut tr, int merge_in, int last,
@@ -429,13 +463,15 @@ __device__ __forceinline__ void expert_blocks(const T* Qh, QR qrow, const T* Ks,
   load_queries<T, D, IBX>(qf, Qh, lg, qrow);
 #pragma unroll
   for (int b = 0; b < IBX; ++b) qn[b] = (int)qrow(b);
-  expert_group<IBX, T, D>(qf, qn, Ks, Vs, Kp, k, one, row0, plse, po, O, tr, merge_in, last, cscale, li, lg);
+  expert_group<IBX, T, D, EARLY>(qf, qn, Ks, Vs, Kp, k, one, row0, plse, po, O, tr, merge_in, last, cscale, li, lg,
+                                 [] {});
 }
 
 template <typename T, int D, int NW, int IB>
-// (sixteen waves of one or two 16-query blocks each for bf16: four waves per
-// SIMD, so one wave's dependency stalls are covered by the others)
-__global__ __launch_bounds__(NW * 64, NW >= 16 ? 4 : 2) void k_expert(
+// (for bf16 sixteen waves of one 16-query block, four per SIMD, or twelve of
+// two, three per SIMD with the registers to fetch the stored part early: one
+// wave's dependency stalls are covered by the others)
+__global__ __launch_bounds__(NW * 64, NW >= 16 ? 4 : NW >= 12 ? 3 : 2) void k_expert(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const int32_t* __restrict__ topk,
     const int32_t* __restrict__ perm, const WorkItem* __restrict__ wl, const int* __restrict__ wl_count,
     float2* __restrict__ plse, typename PartT<T>::type* __restrict__ po, T* __restrict__ O, TrainOut tr, int N, int m, int k,
@@ -473,10 +509,13 @@ __global__ __launch_bounds__(NW * 64, NW >= 16 ? 4 : 2) void k_expert(
   auto group_rows = [&](int gi) {
     return [=](int b) -> long long { return s_q[gi * GQ + b * 16 + li]; };
   };
-  // the next group's query rows are fetched while the current one computes
-  // (not with sixteen waves of two blocks: no registers for it, and the
-  // other three waves of the SIMD cover the load)
-  constexpr bool PREFETCH = !(NW == 16 && IB == 2);
+  // the stored part is fetched before each group's key loop where the
+  // registers allow (sixteen waves of one block, twelve of two: 0.44 -> 0.415
+  // ms at N = 1M, 62 -> 60 us at 64K); the next group's query rows while the
+  // current one computes (not with twelve waves of two blocks: no registers
+  // for both, and the other waves of the SIMD cover the load)
+  constexpr bool EARLY = NW >= 12;
+  constexpr bool PREFETCH = !(NW == 12 && IB == 2);
   Frag<T> qnx[PREFETCH ? IB : 1][D / 32];
   if constexpr (PREFETCH)
     if (wave < nfull) load_queries<T, D, IB>(qnx, Qh, lg, group_rows(wave));
@@ -488,13 +527,16 @@ __global__ __launch_bounds__(NW * 64, NW >= 16 ? 4 : 2) void k_expert(
       for (int b = 0; b < IB; ++b)
 #pragma unroll
         for (int dc = 0; dc < D / 32; ++dc) qf[b][dc] = qnx[b][dc];
-      if (gi + NW < nfull) load_queries<T, D, IB>(qnx, Qh, lg, group_rows(gi + NW));
     } else {
       load_queries<T, D, IB>(qf, Qh, lg, group_rows(gi));
     }
 #pragma unroll
     for (int b = 0; b < IB; ++b) qn[b] = s_q[gi * GQ + b * 16 + li];
-    expert_group<IB, T, D>(qf, qn, Ks, Vs, Kp, k, one, row0, plse, po, O, tr, merge_in, last, cscale, li, lg);
+    expert_group<IB, T, D, EARLY>(qf, qn, Ks, Vs, Kp, k, one, row0, plse, po, O, tr, merge_in, last, cscale, li, lg,
+                                  [&] {
+                                    if constexpr (PREFETCH)
+                                      if (gi + NW < nfull) load_queries<T, D, IB>(qnx, Qh, lg, group_rows(gi + NW));
+                                  });
   }
   // ... then the rest in blocks of 16 queries dealt to the waves in turn, so
   // a short remainder keeps every wave busy on narrower groups
@@ -506,13 +548,13 @@ __global__ __launch_bounds__(NW * 64, NW >= 16 ? 4 : 2) void k_expert(
     return l < it.count ? s_q[l] : -1;
   };
   if constexpr (IB >= 4) {
-    if (mine == 4) expert_blocks<4, T, D>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, tr, merge_in, last, cscale, li, lg);
-    if (mine == 3) expert_blocks<3, T, D>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, tr, merge_in, last, cscale, li, lg);
+    if (mine == 4) expert_blocks<4, T, D, EARLY>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, tr, merge_in, last, cscale, li, lg);
+    if (mine == 3) expert_blocks<3, T, D, EARLY>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, tr, merge_in, last, cscale, li, lg);
   }
   if constexpr (IB >= 2) {
-    if (mine == 2) expert_blocks<2, T, D>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, tr, merge_in, last, cscale, li, lg);
+    if (mine == 2) expert_blocks<2, T, D, EARLY>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, tr, merge_in, last, cscale, li, lg);
   }
-  if (mine == 1) expert_blocks<1, T, D>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, tr, merge_in, last, cscale, li, lg);
+  if (mine == 1) expert_blocks<1, T, D, EARLY>(Qh, rem_rows, Ks, Vs, Kp, k, one, row0, plse, po, O, tr, merge_in, last, cscale, li, lg);
 }
 
 // ---------------------------------------------------------------------------
@@ -583,7 +625,7 @@ static void launch_expert_d(const Plan& p) {
   else if (p.ex_nw == 1) launch_expert_t<T, D, 1, 2>(p);
   else if (p.ex_nw == 4) launch_expert_t<T, D, 4, 4>(p);
   else if (p.ex_ib == 1) launch_expert_t<T, D, 16, 1>(p);
-  else launch_expert_t<T, D, 16, 2>(p);
+  else launch_expert_t<T, D, 12, 2>(p);
 }
 
 void launch_expert(const Plan& p) {
