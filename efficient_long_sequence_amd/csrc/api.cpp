@@ -137,8 +137,11 @@ Plan make_plan(mita_dtype dtype, int B, int H, int N, int d, mita_pool pool, int
     p.rs_qpw = (int)(qpw < 512 ? 512 : qpw);
     // bf16: sixteen waves of one 16-query block each (four per SIMD, which
     // cover each other's dependency stalls; N = 1M: 0.373 -> 0.357 ms,
-    // DeiT-S: 18 -> 13.5 us); fp32: eight waves of four blocks
-    p.rs_nw = p.dtype == 1 ? 16 : 8;
+    // DeiT-S: 18 -> 13.5 us), or for top-1 routing over 512 or more
+    // landmarks twelve waves of two blocks (three per SIMD, the two blocks'
+    // chains interleaved: N = 1M 0.413-0.416 -> 0.398-0.399 ms; level at
+    // m = 256, 128; 1 us slower at DeiT-S); fp32: eight waves of four blocks
+    p.rs_nw = p.dtype == 1 ? (m >= 512 && s == 1 ? 12 : 16) : 8;
     if (p.dtype == 0 || avg <= 16) { p.ex_nw = 1; p.ex_ib = 1; }
     else if (avg <= 64) { p.ex_nw = 1; p.ex_ib = 2; }
     else if (avg <= 256) { p.ex_nw = 4; p.ex_ib = 4; }

@@ -72,7 +72,7 @@ struct Plan {
   int UB;         // upper bound on work items per slot
   int fast;       // LDS-resident routing + shared part and per-expert attention
   int rs_qpw;     // queries per routing workgroup (resident path)
-  int rs_nw;      // its waves: 8 (four 16-query blocks each) or 16 (one block each)
+  int rs_nw;      // its waves: 8 (four 16-query blocks each), 12 (two) or 16 (one)
   int ex_nw, ex_ib;  // expert kernel waves and 16-query blocks per query group
   float cscale;   // log2(e) / sqrt(d)
   float cscale_sh;  // log2(e) times the scale of the shared logits (1/sqrt(d) or 1/d)

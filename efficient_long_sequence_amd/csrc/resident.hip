@@ -198,7 +198,7 @@ __device__ __forceinline__ void list_insert(float* lv, int* lx, float v, int i) 
 // IB: 16-query blocks per wave group (four with eight waves; one with sixteen
 // waves, four per SIMD, for mid-size heads)
 template <typename T, int D, int NW, int SMAX, int IB>
-__global__ __launch_bounds__(NW * 64, NW >= 16 ? 4 : 1) void k_route_shared(
+__global__ __launch_bounds__(NW * 64, NW >= 16 ? 4 : NW >= 12 ? 3 : 1) void k_route_shared(
     const T* __restrict__ Q, const T* __restrict__ Qt, const T* __restrict__ VtT, int32_t* __restrict__ route,
     int* __restrict__ counts, float2* __restrict__ plse, typename PartT<T>::type* __restrict__ po, int N, int m, int s,
     int BH, int qpw, int hist_lds, float cscale) {  // cscale: log2(e) x the shared-logit scale
@@ -578,6 +578,10 @@ static void launch_route_shared_t(const Plan& p) {
 
 template <typename T, int D>
 static void launch_route_shared_d(const Plan& p) {
+  if (p.rs_nw == 12) {  // (top-1 routing only)
+    launch_route_shared_t<T, D, 1, 12, 2>(p);
+    return;
+  }
   if (p.rs_nw == 16) {
     switch (p.smax) {
       case 1: launch_route_shared_t<T, D, 1, 16, 1>(p); break;

@@ -91,6 +91,10 @@ EDGE = {
     # the same above the dense limit (sampled threshold, score records):
     # chunks of 72 steps and a last one of 69 full steps plus a partial one
     "sparse_chunks_odd_tail": (4, 32, 1, 9125, 64, 1, 4, 16, 1, "runs", 8, "bf16"),
+    # top-1 routing over 512 landmarks (the twelve-wave, two-block routing
+    # shape): rounds of 12 query groups per workgroup that do not come out
+    # even, and a last workgroup of 43 queries (a partial 16-query block)
+    "route_m512_ragged": (1, 2, 1, 20011, 64, 1, 512, 24, 1, "runs", 32, "bf16"),
 }
 
 
